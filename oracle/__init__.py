@@ -1,0 +1,18 @@
+"""CPU oracle for causal linear attention with a carried state.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import anything from this package.  It shares
+no code with the GPU library and never imports it.
+
+* :mod:`oracle.core`   -- ctypes front end of ``la_oracle.c``: the per-token fp64
+  recurrence (forward) and reverse scan (backward), OpenMP over groups.
+* :mod:`oracle.forms`  -- independent numpy fp64 forms used to cross-check it: the
+  masked-einsum form, the blocked form at any block size, and the whole-chunk
+  matrix backward.
+* :mod:`oracle.exact`  -- exact rational brute force (fractions + dual numbers)
+  for tiny shapes; writes the stored golden values.
+
+Every function cites the passage of "Fractus-1B training optimization" it
+follows.  Which pins cover which function is listed in the test suite.
+"""
+from .core import build, fwd, bwd, lib_path, max_threads  # noqa: F401
