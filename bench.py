@@ -1,0 +1,180 @@
+"""Throughput of chunked causal linear attention, forward + backward, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one forward and one backward launch (the whole path) over one
+batch of seeded synthetic inputs already resident in device memory.  Steps
+rotate over enough buffer sets (>= 640 MB) that the 256 MB last-level cache
+cannot serve the traffic.  The timed region is bracketed by device
+synchronisation; per-kernel durations come from HIP events recorded around
+each launch on the stream the kernels run on.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens·groups/s for linear-attn fwd+bwd at G=160,C=128,D=64; % roofline"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_la_bwd_g160_c128_d64_bf16.json")
+
+
+def algorithmic_bytes(G, C, D, esz, carry, upstream):
+    """Bytes each kernel must move at minimum (inputs read once, outputs written once)."""
+    tok = G * C * D * esz
+    st = G * D * D * 4
+    z = G * D * 4
+    carry_b = st + z
+    fwd = 3 * tok + tok + (carry_b if carry else 0) + carry_b            # q,k,v,[S_in,z_in] -> o,S_out,z_out
+    bwd = 4 * tok + 3 * tok + (carry_b if carry else 0) + (carry_b if upstream else 0) + carry_b
+    return fwd, bwd
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("la_bwd.hip", "la_fwd.hip", "la_common.h"):
+        with open(os.path.join(ROOT, "causal_linear_attention_chunked_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """Counter-measured HBM bytes per backward launch, if taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(I, w, min_seconds=10.0):
+    """The fp64 oracle as it stands, on this host's cores, over the same workload, repeated."""
+    import oracle
+    threads = os.cpu_count() or 1
+    args = [I[n] for n in ("q", "k", "v", "S_in", "z_in")]
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.fwd(*args, nthreads=threads)
+        oracle.bwd(*args, I["dO"], nthreads=threads)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= min_seconds and len(times) >= 3:
+            break
+    times.sort()
+    med = times[len(times) // 2]
+    return {"value": w.G * w.T / med, "unit": "tokens·groups/s", "cores": threads, "kind": "oracle",
+            "sample": f"full {w.name} workload (G={w.G}, {w.T} tokens, D={w.D}), forward+backward in fp64, "
+                      f"median of {len(times)} repeats ({sum(times):.1f} s of CPU work)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="g160_c128_d64_bf16_fwdbwd")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--footprint-mb", type=float, default=640.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(groups shard across GPUs with no communication, so one GPU's share is the measurement)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import causal_linear_attention_chunked_amd as lac
+    from causal_linear_attention_chunked_amd import inputs as inp
+
+    lac.load_library()
+    w = inp.workload(args.workload)
+    if len(w.chunks) != 1 or not w.backward:
+        raise SystemExit("bench.py times single-chunk forward+backward workloads")
+    G, C, D = w.G, w.T, w.D
+    I = inp.workload_inputs(w)
+    dev = torch.device("cuda:0")
+    esz = 2 if w.dtype == "bf16" else 4
+    carry = I["S_in"] is not None
+    fwd_bytes, bwd_bytes = algorithmic_bytes(G, C, D, esz, carry, False)
+    set_bytes = fwd_bytes + bwd_bytes
+    nsets = max(2, math.ceil(args.footprint_mb * 1e6 / set_bytes))
+
+    def dev_copy(x):
+        return None if x is None else x.to(dev).contiguous()
+
+    sets = []
+    for _ in range(nsets):
+        s = {n: dev_copy(I[n]) for n in ("q", "k", "v", "S_in", "z_in", "dO")}
+        s["fout"] = (torch.empty_like(s["q"]), torch.empty((G, D, D), device=dev),
+                     torch.empty((G, D), device=dev))
+        s["bout"] = (torch.empty_like(s["q"]), torch.empty_like(s["q"]), torch.empty_like(s["q"]),
+                     torch.empty((G, D, D), device=dev), torch.empty((G, D), device=dev))
+        sets.append(s)
+
+    def step(s):
+        lac.fwd(s["q"], s["k"], s["v"], s["S_in"], s["z_in"], out=s["fout"])
+        lac.bwd(s["q"], s["k"], s["v"], s["S_in"], s["z_in"], s["dO"], out=s["bout"])
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        s = sets[i % nsets]
+        ev[3 * i].record()
+        lac.fwd(s["q"], s["k"], s["v"], s["S_in"], s["z_in"], out=s["fout"])
+        ev[3 * i + 1].record()
+        lac.bwd(s["q"], s["k"], s["v"], s["S_in"], s["z_in"], s["dO"], out=s["bout"])
+        ev[3 * i + 2].record()
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    fwd_ms = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(K)) / K
+    bwd_ms = sum(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(K)) / K
+    ms_per_step = total_ms / K
+    value = G * C / (ms_per_step / 1e3)
+
+    bwd_gbs = bwd_bytes / (bwd_ms / 1e3) / 1e9
+    fwd_gbs = fwd_bytes / (fwd_ms / 1e3) / 1e9
+    traffic = measured_traffic()
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens·groups/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "G": G, "C": C, "D": D, "block": w.block, "carry": w.carry,
+                   "buffer_sets": nsets, "footprint_mb": round(nsets * set_bytes / 1e6, 1),
+                   "graph_captured": False},
+        "roofline": {"bound": "hbm", "kernel": "la_bwd_kernel", "achieved": bwd_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": bwd_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": bwd_bytes, "avg_us": bwd_ms * 1e3},
+        "kernels": {"la_fwd_kernel": {"avg_us": fwd_ms * 1e3, "algorithmic_bytes": fwd_bytes,
+                                      "GB/s": fwd_gbs, "frac": fwd_gbs / HBM_PEAK_GBS},
+                    "la_bwd_kernel": {"avg_us": bwd_ms * 1e3, "algorithmic_bytes": bwd_bytes,
+                                      "GB/s": bwd_gbs, "frac": bwd_gbs / HBM_PEAK_GBS}},
+        "step_roofline_frac": (fwd_bytes + bwd_bytes) / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+    }
+    if not args.no_cpu_baseline:
+        Ic = {n: I[n] for n in ("q", "k", "v", "S_in", "z_in", "dO")}
+        out["cpu_baseline"] = cpu_baseline(Ic, w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+"""Chunked causal linear attention with a carried state on AMD MI355X (gfx950).
+
+Python binding of the C ABI in ``include/la_chunk.h`` (library ``liblachunk.so``
+in this directory, built by ``python -m causal_linear_attention_chunked_amd.build``).
+The binding only marshals arguments: every step of the computation runs in the
+library's HIP kernels, and importing or calling it without the built library
+raises.  PyTorch supplies device memory and the current stream.
+
+    o, S_out, z_out = fwd(q, k, v, S_in=None, z_in=None)
+    dq, dk, dv, dS_in, dz_in = bwd(q, k, v, S_in, z_in, dO, dS_out=None, dz_out=None)
+
+q, k, v, dO: contiguous (G, C, D) CUDA tensors, float32 or bfloat16 (one dtype
+for all); S: (G, D, D) float32 with S[p][c] (p key feature, c value feature);
+z: (G, D) float32.  See the header for the operation and its rules.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = ["fwd", "bwd", "chain_fwd", "chain_bwd", "LachunkError", "lib_path", "load_library",
+           "abi_version", "status_str", "BWD_MAX_C"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liblachunk.so")
+_lock = threading.Lock()
+_lib = None
+
+LA_F32, LA_BF16 = 0, 1
+BWD_MAX_C = 2048
+_STATUS = {0: "LA_OK", 1: "LA_ERR_INVALID", 2: "LA_ERR_UNSUPPORTED", 3: "LA_ERR_ALIGN",
+           4: "LA_ERR_ALIAS", 5: "LA_ERR_LAUNCH"}
+
+
+class LachunkError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load liblachunk.so; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m causal_linear_attention_chunked_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i = ctypes.c_void_p, ctypes.c_int
+        lib.la_chunk_fwd.restype = i
+        lib.la_chunk_fwd.argtypes = [vp] * 8 + [i] * 5 + [vp]
+        lib.la_chunk_bwd.restype = i
+        lib.la_chunk_bwd.argtypes = [vp] * 13 + [i] * 5 + [vp]
+        lib.la_status_str.restype = ctypes.c_char_p
+        lib.la_status_str.argtypes = [i]
+        lib.la_abi_version.restype = i
+        lib.la_abi_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def abi_version() -> int:
+    return int(load_library().la_abi_version())
+
+
+def status_str(s: int) -> str:
+    return load_library().la_status_str(int(s)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(fn, status):
+    if status != 0:
+        raise LachunkError(fn, status, status_str(status))
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return LA_F32
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    raise TypeError(f"unsupported element type {t.dtype}; use float32 or bfloat16")
+
+
+def _validate_tokens(names, tensors):
+    ref = tensors[0]
+    if ref.dim() != 3:
+        raise ValueError(f"{names[0]} must be (G, C, D), got {tuple(ref.shape)}")
+    for n, t in zip(names, tensors):
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a CUDA tensor")
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError(f"{n}: shape/dtype/device {tuple(t.shape)}/{t.dtype}/{t.device} differs from "
+                             f"{names[0]} {tuple(ref.shape)}/{ref.dtype}/{ref.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+
+
+def _validate_state(name, t, shape, device):
+    import torch
+    if t is None:
+        return
+    if t.dtype != torch.float32 or tuple(t.shape) != shape or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shape} on {device}")
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def fwd(q, k, v, S_in=None, z_in=None, block: int = 64, out=None):
+    """Forward over one chunk: returns (o, S_out, z_out).  ``out`` may supply them."""
+    import torch
+    lib = load_library()
+    _validate_tokens(("q", "k", "v"), (q, k, v))
+    G, C, D = q.shape
+    if (S_in is None) != (z_in is None):
+        raise ValueError("S_in and z_in must be given together")
+    _validate_state("S_in", S_in, (G, D, D), q.device)
+    _validate_state("z_in", z_in, (G, D), q.device)
+    if out is None:
+        o = torch.empty_like(q)
+        S_out = torch.empty((G, D, D), dtype=torch.float32, device=q.device)
+        z_out = torch.empty((G, D), dtype=torch.float32, device=q.device)
+    else:
+        o, S_out, z_out = out
+    _check("la_chunk_fwd", lib.la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(S_in), _ptr(z_in),
+                                            _ptr(o), _ptr(S_out), _ptr(z_out), G, C, D, int(block),
+                                            _dtype_code(q), _stream(q.device)))
+    return o, S_out, z_out
+
+
+def bwd(q, k, v, S_in, z_in, dO, dS_out=None, dz_out=None, block: int = 64, out=None):
+    """Backward over one chunk: returns (dq, dk, dv, dS_in, dz_in)."""
+    import torch
+    lib = load_library()
+    _validate_tokens(("q", "k", "v", "dO"), (q, k, v, dO))
+    G, C, D = q.shape
+    if (S_in is None) != (z_in is None) or (dS_out is None) != (dz_out is None):
+        raise ValueError("S_in/z_in and dS_out/dz_out must each be given together")
+    for n, t, shp in (("S_in", S_in, (G, D, D)), ("z_in", z_in, (G, D)),
+                      ("dS_out", dS_out, (G, D, D)), ("dz_out", dz_out, (G, D))):
+        _validate_state(n, t, shp, q.device)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        dS_in = torch.empty((G, D, D), dtype=torch.float32, device=q.device)
+        dz_in = torch.empty((G, D), dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv, dS_in, dz_in = out
+    _check("la_chunk_bwd", lib.la_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(S_in), _ptr(z_in), _ptr(dO),
+                                            _ptr(dS_out), _ptr(dz_out), _ptr(dq), _ptr(dk), _ptr(dv),
+                                            _ptr(dS_in), _ptr(dz_in), G, C, D, int(block),
+                                            _dtype_code(q), _stream(q.device)))
+    return dq, dk, dv, dS_in, dz_in
+
+
+def chain_fwd(q_chunks, k_chunks, v_chunks, S_in=None, z_in=None, block: int = 64):
+    """Forward over consecutive chunks (lists of (G, C_i, D) tensors), carrying (S, z).
+
+    Returns (list of o chunks, list of (S_in_i, z_in_i) that fed each chunk, (S_out, z_out)).
+    The per-chunk carries are what ``chain_bwd`` needs; they stay on the device."""
+    outs, carries = [], []
+    S, z = S_in, z_in
+    for qc, kc, vc in zip(q_chunks, k_chunks, v_chunks):
+        carries.append((S, z))
+        o, S, z = fwd(qc, kc, vc, S, z, block)
+        outs.append(o)
+    return outs, carries, (S, z)
+
+
+def chain_bwd(q_chunks, k_chunks, v_chunks, carries, dO_chunks, dS_out=None, dz_out=None, block: int = 64):
+    """Backward over consecutive chunks, last chunk first, passing (dS, dz) down the chain.
+
+    Returns (dq chunks, dk chunks, dv chunks, dS_in, dz_in) for the whole sequence."""
+    n = len(q_chunks)
+    dqs, dks, dvs = [None] * n, [None] * n, [None] * n
+    gS, gz = dS_out, dz_out
+    for i in range(n - 1, -1, -1):
+        S, z = carries[i]
+        dqs[i], dks[i], dvs[i], gS, gz = bwd(q_chunks[i], k_chunks[i], v_chunks[i], S, z, dO_chunks[i],
+                                             gS, gz, block)
+    return dqs, dks, dvs, gS, gz

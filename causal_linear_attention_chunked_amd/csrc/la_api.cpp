@@ -1,0 +1,142 @@
+// Host side of the C ABI declared in include/la_chunk.h: argument validation,
+// dispatch to the typed launchers, status strings.  Validation happens before
+// any HIP call, so an invalid call touches neither the device nor the runtime.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/la_chunk.h"
+#include "la_launch.h"
+
+namespace {
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool mul_ok(size_t a, size_t b, size_t *out) {
+    if (a != 0 && b > SIZE_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+bool overlap(const Span &a, const Span &b) {
+    return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi;
+}
+
+Span span(const void *p, size_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{lo, p ? lo + bytes : lo};
+}
+
+bool aligned16(const void *p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Sizes {
+    size_t tok, st, z;  // bytes of one token tensor, one state tensor, one normaliser
+};
+
+la_status common_checks(int G, int C, int D, int block, la_dtype dt, Sizes *sz) {
+    if (G < 1 || C < 1) return LA_ERR_INVALID;
+    if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return LA_ERR_UNSUPPORTED;
+    if (block != 64) return LA_ERR_UNSUPPORTED;
+    const size_t esz = dt == LA_F32 ? 4 : 2;
+    size_t a, b;
+    if (!mul_ok((size_t)G, (size_t)C, &a) || !mul_ok(a, (size_t)D, &b) || !mul_ok(b, esz, &sz->tok))
+        return LA_ERR_INVALID;
+    if (!mul_ok((size_t)G, (size_t)D * D, &a) || !mul_ok(a, 4, &sz->st)) return LA_ERR_INVALID;
+    sz->z = (size_t)G * D * 4;
+    return LA_OK;
+}
+
+// every output span against every input span and every other output span
+la_status alias_checks(const Span *in, int nin, const Span *out, int nout) {
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j)
+            if (overlap(out[i], in[j])) return LA_ERR_ALIAS;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(out[i], out[j])) return LA_ERR_ALIAS;
+    }
+    return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status la_chunk_fwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
+                       void *o, float *S_out, float *z_out, int G, int C, int D, int block, la_dtype dt,
+                       void *stream) {
+    Sizes sz;
+    la_status st = common_checks(G, C, D, block, dt, &sz);
+    if (st != LA_OK) return st;
+    if (!q || !k || !v || !o || !S_out || !z_out) return LA_ERR_INVALID;
+    if ((S_in == nullptr) != (z_in == nullptr)) return LA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, S_in, z_in, o, S_out, z_out};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return LA_ERR_ALIGN;
+    const Span in[] = {span(q, sz.tok), span(k, sz.tok), span(v, sz.tok), span(S_in, sz.st), span(z_in, sz.z)};
+    const Span out[] = {span(o, sz.tok), span(S_out, sz.st), span(z_out, sz.z)};
+    st = alias_checks(in, 5, out, 3);
+    if (st != LA_OK) return st;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dt == LA_BF16)
+        e = D == 64 ? lachunk::launch_fwd<__bf16, 64>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s)
+                    : lachunk::launch_fwd<__bf16, 128>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s);
+    else
+        e = D == 64 ? lachunk::launch_fwd<float, 64>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s)
+                    : lachunk::launch_fwd<float, 128>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s);
+    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
+
+la_status la_chunk_bwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
+                       const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
+                       float *dS_in, float *dz_in, int G, int C, int D, int block, la_dtype dt, void *stream) {
+    Sizes sz;
+    la_status st = common_checks(G, C, D, block, dt, &sz);
+    if (st != LA_OK) return st;
+    if (C > LA_BWD_MAX_C) return LA_ERR_UNSUPPORTED;
+    if (dt == LA_F32 && D == 128) return LA_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !dO || !dq || !dk || !dv || !dS_in || !dz_in) return LA_ERR_INVALID;
+    if ((S_in == nullptr) != (z_in == nullptr)) return LA_ERR_INVALID;
+    if ((dS_out == nullptr) != (dz_out == nullptr)) return LA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return LA_ERR_ALIGN;
+    const Span in[] = {span(q, sz.tok),   span(k, sz.tok),      span(v, sz.tok),     span(S_in, sz.st),
+                       span(z_in, sz.z), span(dO, sz.tok),     span(dS_out, sz.st), span(dz_out, sz.z)};
+    const Span out[] = {span(dq, sz.tok), span(dk, sz.tok), span(dv, sz.tok), span(dS_in, sz.st),
+                        span(dz_in, sz.z)};
+    st = alias_checks(in, 8, out, 5);
+    if (st != LA_OK) return st;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dt == LA_BF16)
+        e = D == 64 ? lachunk::launch_bwd<__bf16, 64>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in,
+                                                     dz_in, G, C, s)
+                    : lachunk::launch_bwd<__bf16, 128>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in,
+                                                      dz_in, G, C, s);
+    else
+        e = lachunk::launch_bwd<float, 64>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, G, C,
+                                           s);
+    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
+
+const char *la_status_str(la_status s) {
+    switch (s) {
+        case LA_OK: return "ok";
+        case LA_ERR_INVALID: return "invalid argument (null pointer, non-positive size, half-given carry or overflow)";
+        case LA_ERR_UNSUPPORTED: return "unsupported configuration (D, block, dtype or chunk length)";
+        case LA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case LA_ERR_ALIAS: return "an output buffer overlaps an input or another output";
+        case LA_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int la_abi_version(void) { return LA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,17 @@
+// Typed launchers, one per supported (element type, head dim) pair.  Each
+// enqueues its kernel on `stream` and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace lachunk {
+
+template <typename T, int D>
+hipError_t launch_fwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
+                      void *o, float *S_out, float *z_out, int G, int C, hipStream_t stream);
+
+template <typename T, int D>
+hipError_t launch_bwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
+                      const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
+                      float *dS_in, float *dz_in, int G, int C, hipStream_t stream);
+
+}  // namespace lachunk

@@ -1,0 +1,114 @@
+/*
+ * la_chunk.h -- C ABI of the MI355X (gfx950) chunked causal linear attention library.
+ *
+ * The operation ("Fractus-1B training optimization", section 1, Bottleneck #1,
+ * and section 2, Opt 2): for each of G independent groups (batch x levels x
+ * heads flattened, section 1 "Diagnosis") and a chunk of C tokens with head
+ * dimension D, given positive features q_t, k_t (the caller has already applied
+ * its feature map), values v_t and a carried state (S_in, z_in),
+ *
+ *     S_t = S_in + sum_{j<=t} k_j v_j^T      z_t = z_in + sum_{j<=t} k_j      (inclusive of token t)
+ *     o_t = (S_t^T q_t) / (q_t . z_t)
+ *     S_out = S_C,  z_out = z_C.
+ *
+ * The forward is computed in the blocked ("chunked") form of section 2, Opt 2:
+ * blocks of `block` tokens, a masked block x block score matrix for the block's
+ * own tokens plus a term against the running state (S_run, z_run) read before
+ * the block updates it; the C mod block tokens left at the end (the ragged
+ * tail) take the exact per-token cumsum form.  The backward is the reverse
+ * scan the same page names (the gradient of a prefix sum is a suffix sum); it
+ * recomputes the forward from its inputs and takes no saved activations.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer (hipMalloc'd or equivalent),
+ *     row-major, contiguous, 16-byte aligned.  The caller allocates and owns all
+ *     buffers; the library allocates nothing, keeps no state between calls and
+ *     is reentrant.
+ *   - Token tensors q, k, v, o, dO, dq, dk, dv are [G][C][D] in the element type
+ *     `dt` (fp32 or bf16).  The state S (and dS) is [G][D][D] fp32 with S[p][c]:
+ *     p indexes the key feature, c the value feature; z (and dz) is [G][D] fp32.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued on
+ *     it and the call returns at once; the library never synchronises the
+ *     device.  Calls on one stream run in stream order.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is launched and a status other than LA_OK is returned.
+ *     Nothing is printed, thrown or exited across this boundary.
+ *   - Preconditions NOT checked on the device: q_t . z_t > 0 for every token
+ *     (true for positive features: q, k > 0 elementwise and z_in >= 0), and
+ *     finite inputs.  No epsilon is added to the denominator.
+ *   - Supported: D in {64, 128}, block == 64, G >= 1, 1 <= C.  The backward
+ *     additionally needs C <= LA_BWD_MAX_C and, for D == 128, bf16 elements.
+ *     Anything else returns LA_ERR_UNSUPPORTED.
+ */
+#ifndef LA_CHUNK_H
+#define LA_CHUNK_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_ABI_VERSION 1
+#define LA_BWD_MAX_C 2048
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_INVALID = 1,     /* NULL required pointer, G < 1, C < 1, half-given carry, size overflow */
+    LA_ERR_UNSUPPORTED = 2, /* D, block, dtype or C outside the supported set */
+    LA_ERR_ALIGN = 3,       /* a tensor pointer is not 16-byte aligned */
+    LA_ERR_ALIAS = 4,       /* an output overlaps an input or another output */
+    LA_ERR_LAUNCH = 5       /* the HIP runtime rejected the kernel launch */
+} la_status;
+
+/*
+ * Forward over one chunk.
+ *   q, k, v  : [G][C][D] dt, inputs.  q and k are positive features.
+ *   S_in     : [G][D][D] fp32 carried state, or NULL (zero state).
+ *   z_in     : [G][D]    fp32 carried normaliser, or NULL.  S_in and z_in are
+ *              both NULL or both non-NULL.
+ *   o        : [G][C][D] dt, output o_t.
+ *   S_out    : [G][D][D] fp32, output state after the chunk (S_C).
+ *   z_out    : [G][D]    fp32, output normaliser after the chunk (z_C).
+ *   block    : tokens per block of the blocked form (must be 64).
+ * S_out may not alias S_in: the call is pure (the carry goes in, a new carry
+ * comes out), so chaining chunks ping-pongs two state buffers.
+ */
+la_status la_chunk_fwd(const void *q, const void *k, const void *v,
+                       const float *S_in, const float *z_in,
+                       void *o, float *S_out, float *z_out,
+                       int G, int C, int D, int block, la_dtype dt, void *stream);
+
+/*
+ * Backward over one chunk, for the loss
+ *     L = sum_t <dO_t, o_t> + <dS_out, S_out> + dz_out . z_out.
+ *   q, k, v, S_in, z_in : exactly the inputs of the forward call (S_in/z_in may
+ *                         be NULL together, meaning a zero carry).
+ *   dO       : [G][C][D] dt, gradient of o.
+ *   dS_out   : [G][D][D] fp32 gradient of S_out (from the next chunk), or NULL.
+ *   dz_out   : [G][D]    fp32 gradient of z_out, or NULL; NULL together with dS_out
+ *              (both NULL = zero).
+ *   dq,dk,dv : [G][C][D] dt, outputs.
+ *   dS_in    : [G][D][D] fp32 output, gradient of S_in (pass it as the previous
+ *              chunk's dS_out when chaining).
+ *   dz_in    : [G][D]    fp32 output, gradient of z_in.
+ * With a NULL carry, dS_in/dz_in still receive the gradient with respect to a
+ * zero carry.
+ */
+la_status la_chunk_bwd(const void *q, const void *k, const void *v,
+                       const float *S_in, const float *z_in,
+                       const void *dO, const float *dS_out, const float *dz_out,
+                       void *dq, void *dk, void *dv, float *dS_in, float *dz_in,
+                       int G, int C, int D, int block, la_dtype dt, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *la_status_str(la_status s);
+
+/* LA_ABI_VERSION of the built library. */
+int la_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_CHUNK_H */

@@ -1,0 +1,115 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the device.
+
+Only error paths are exercised: validation runs on the host before any HIP
+call, so the fake device addresses below are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_linear_attention_chunked_amd as lac
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la_chunk.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, ALIAS = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lac.lib_path()):
+        from causal_linear_attention_chunked_amd import build
+        build.build()
+    return lac.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(la_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["la_abi_version", "la_chunk_bwd", "la_chunk_fwd", "la_status_str"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {lac.lib_path()}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_version_and_status_strings(lib):
+    assert lac.abi_version() == 1
+    for s in range(6):
+        assert len(lac.status_str(s)) > 0
+    assert lac.status_str(99) == "unknown status"
+
+
+# fake, 16-byte aligned, non-overlapping device addresses (never dereferenced)
+BASE = 1 << 40
+STEP = 1 << 32
+
+
+def addr(i):
+    return ctypes.c_void_p(BASE + i * STEP)
+
+
+def fwd_call(lib, G=4, C=128, D=64, block=64, dt=1, **over):
+    args = {n: addr(i) for i, n in enumerate(["q", "k", "v", "S_in", "z_in", "o", "S_out", "z_out"])}
+    args.update(over)
+    return lib.la_chunk_fwd(args["q"], args["k"], args["v"], args["S_in"], args["z_in"], args["o"],
+                            args["S_out"], args["z_out"], G, C, D, block, dt, None)
+
+
+def bwd_call(lib, G=4, C=128, D=64, block=64, dt=1, **over):
+    names = ["q", "k", "v", "S_in", "z_in", "dO", "dS_out", "dz_out", "dq", "dk", "dv", "dS_in", "dz_in"]
+    args = {n: addr(i) for i, n in enumerate(names)}
+    args.update(over)
+    return lib.la_chunk_bwd(*[args[n] for n in names], G, C, D, block, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(G=0), INVALID), (dict(C=0), INVALID), (dict(G=-3), INVALID),
+    (dict(D=32), UNSUPPORTED), (dict(D=96), UNSUPPORTED), (dict(block=32), UNSUPPORTED),
+    (dict(dt=7), UNSUPPORTED),
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(S_out=None), INVALID),
+    (dict(S_in=None), INVALID),                          # z_in given without S_in
+    (dict(q=ctypes.c_void_p(BASE + 8)), ALIGN),
+    (dict(o=addr(0)), ALIAS),                            # o == q
+    (dict(S_out=addr(3)), ALIAS),                        # S_out == S_in (the call is pure)
+    (dict(z_out=ctypes.c_void_p(BASE + 5 * STEP + 64)), ALIAS),  # z_out inside o
+])
+def test_fwd_rejects(lib, kw, status):
+    assert fwd_call(lib, **kw) == status
+
+
+def test_fwd_size_overflow(lib):
+    assert fwd_call(lib, G=2**31 - 1, C=2**31 - 1, D=128) in (INVALID,)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(G=0), INVALID), (dict(D=48), UNSUPPORTED), (dict(block=16), UNSUPPORTED),
+    (dict(C=lac.BWD_MAX_C + 1), UNSUPPORTED),
+    (dict(dt=0, D=128), UNSUPPORTED),                    # fp32 backward at D=128
+    (dict(dO=None), INVALID), (dict(dS_in=None), INVALID),
+    (dict(dS_out=None), INVALID),                        # dz_out without dS_out
+    (dict(z_in=None), INVALID),
+    (dict(dk=ctypes.c_void_p(BASE + 9 * STEP + 4)), ALIGN),
+    (dict(dq=addr(5)), ALIAS),                           # dq == dO
+    (dict(dS_in=addr(6)), ALIAS),                        # dS_in == dS_out
+    (dict(dv=addr(9)), ALIAS),                           # dv == dk
+])
+def test_bwd_rejects(lib, kw, status):
+    assert bwd_call(lib, **kw) == status
+
+
+def test_python_binding_rejects_cpu_tensors(lib):
+    import torch
+    q = torch.ones(2, 8, 64)
+    with pytest.raises(ValueError):
+        lac.fwd(q, q, q)
