@@ -24,8 +24,8 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
 
 constexpr int BK = 64;      // tokens per block of the blocked form
-constexpr int NWAVE = 4;    // waves per workgroup
-constexpr int NTHR = 256;   // threads per workgroup
+constexpr int NWAVE = 8;    // waves per workgroup: two per SIMD
+constexpr int NTHR = 512;   // threads per workgroup
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -108,6 +108,36 @@ __device__ __forceinline__ float wsum_g(float x) {
     x += __shfl_xor(x, 16);
     x += __shfl_xor(x, 32);
     return x;
+}
+
+// Transposed operand fragment: 16 rows x one k-chunk of X where X is stored
+// "k, row contiguous" (X^T row-major, pitch ld).  `base` points at (k0, row0).
+// bf16 uses the gfx950 LDS transpose read: in each 16-lane group the lanes
+// supply 16 addresses of 4 consecutive elements, and lane i gets element i%4 of
+// the rows supplied by lanes i/4, 4+i/4, 8+i/4, 12+i/4.  Addressing lane
+// (m = (l%16)/4, a = l%4) of group g at stored row k0 + 4g + m, column row0 + 4a
+// therefore hands lane (r = l%16, g) the four k values 4g..4g+3 of row r, which
+// is slots 0..3 of the fragment; rows k0 + 16 + ... give slots 4..7.  fp32 reads
+// the same elements one by one.
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+template <typename T>
+__device__ __forceinline__ Frag<T> ldfrag_tr(const T *base, int ld, int lane) {
+    Frag<T> f;
+    if constexpr (sizeof(T) == 2) {
+        const int g = lane >> 4, m = (lane & 15) >> 2, a = lane & 3;
+        const T *p = base + (4 * g + m) * ld + 4 * a;
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(p));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(p + 16 * ld));
+        f = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi),
+                                    0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+        const T *p = base + (lane & 15);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) f[s] = p[kslot(lane, s) * ld];
+    }
+    return f;
 }
 
 // ---------------------------------------------------------------------------
@@ -197,6 +227,45 @@ __device__ __forceinline__ floatx8 ld8_scaled(const T *base, int ld, int lane, f
     for (int s = 0; s < 8; ++s) x[s] = tof(f[s]) * sc;
     return x;
 }
+// Split fragment read from stored hi / lo copies (lo is not read for fp32 elements).
+template <typename T>
+__device__ __forceinline__ SFrag<T> ldsplit(const T *hi, const T *lo, int ld, int lane) {
+    SFrag<T> f;
+    f.hi = ldfrag<T>(hi, ld, lane);
+    if constexpr (is_bf16<T>()) f.lo = ldfrag<T>(lo, ld, lane);
+    return f;
+}
+template <typename T>
+__device__ __forceinline__ SFrag<T> ldsplit_tr(const T *hi, const T *lo, int ld, int lane) {
+    SFrag<T> f;
+    f.hi = ldfrag_tr<T>(hi, ld, lane);
+    if constexpr (is_bf16<T>()) f.lo = ldfrag_tr<T>(lo, ld, lane);
+    return f;
+}
+// fp32 values of an element fragment
+template <typename T> __device__ __forceinline__ floatx8 tof8(const Frag<T> &f) {
+    floatx8 x;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) x[s] = tof(f[s]);
+    return x;
+}
+// Writes four consecutive fp32 values as hi (and lo for bf16) element copies.
+template <typename T>
+__device__ __forceinline__ void store_split4(T *hi, T *lo, const floatx4 &x) {
+    if constexpr (is_bf16<T>()) {
+        bf16x4 h, l;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            h[i] = (bf16)x[i];
+            l[i] = (bf16)(x[i] - (float)h[i]);
+        }
+        *reinterpret_cast<bf16x4 *>(hi) = h;
+        *reinterpret_cast<bf16x4 *>(lo) = l;
+    } else {
+        *reinterpret_cast<floatx4 *>(hi) = x;
+    }
+}
+
 template <typename T> __device__ __forceinline__ Frag<T> ones_frag() {
     Frag<T> f;
 #pragma unroll
@@ -205,11 +274,50 @@ template <typename T> __device__ __forceinline__ Frag<T> ones_frag() {
 }
 
 // ---------------------------------------------------------------------------
-// LDS staging of a [rows][NCOL] tile (rows <= 64) read from global memory with
-// row pitch `gld` elements.  16-byte vectors; each thread handles whole vectors.
+// Global reads go through buffer resources: a base address and a byte range.
+// A read past the range returns zero without touching memory, so ragged rows,
+// blocks past the end of a chunk and an absent (NULL) carry need no branches,
+// and every load of a prefetch can be issued unconditionally.  Offsets are byte
+// offsets from the base (32-bit: the host keeps each per-group range below 2 GiB).
+// Keeps every load issued above this point above it: neither the IR optimiser
+// (a memory clobber) nor the machine scheduler may move memory operations across.
+// Used right after a prefetch is issued, so the loads go out early.
+__device__ __forceinline__ void issue_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+struct GRes {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ GRes(const void *base, uint32_t bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000)) {}
+};
+template <typename V> __device__ __forceinline__ V gload(const GRes &g, uint32_t off) {
+    static_assert(sizeof(V) == 4 || sizeof(V) == 8 || sizeof(V) == 16, "buffer load width");
+    if constexpr (sizeof(V) == 16) {
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(g.r, off, 0, 0));
+    } else if constexpr (sizeof(V) == 8) {
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(g.r, off, 0, 0));
+    } else {
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(g.r, off, 0, 0));
+    }
+}
+// Operand fragment straight from global memory ("row, k contiguous", pitch ld elements);
+// `base` is the element offset of (row0, k0).
+template <typename T>
+__device__ __forceinline__ Frag<T> ldfrag_g(const GRes &g, uint32_t base, int ld, int lane) {
+    const uint32_t e = base + (lane & 15) * ld + 4 * (lane >> 4);
+    const Vec4<T> a = gload<Vec4<T>>(g, e * sizeof(T));
+    const Vec4<T> b = gload<Vec4<T>>(g, (e + 16) * sizeof(T));
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ---------------------------------------------------------------------------
+// LDS staging of a [64][NCOL] tile read from global memory (row pitch `gld`
+// elements) through registers: load() issues the 16-byte reads, store() writes
+// LDS later, so a block's loads are in flight while the previous block computes.
 //   nat : if non-null, [rows][ldn] natural copy
 //   tr  : if non-null, [NCOL][ldt] transposed copy (tr[c][row])
-// Rows at or beyond `nrows` are written as zero (only the ragged tail uses it).
 template <typename T, int NCOL>
 struct Stager {
     static constexpr int VE = 16 / sizeof(T);         // elements per 16-byte vector
@@ -220,29 +328,33 @@ struct Stager {
 
     vec_t r[PER];
 
-    __device__ __forceinline__ void load(const T *g, int gld, int nrows, int tid) {
+    static_assert(NV % NTHR == 0, "every thread stages whole vectors");
+    // rows past the resource's range (past the chunk) read as zero
+    __device__ __forceinline__ void load(const GRes &g, uint32_t base, int gld, int tid) {
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const int vi = tid + it * NTHR;
+            const int row = vi / VPR, cv = vi % VPR;
+            r[it] = gload<vec_t>(g, (base + (uint32_t)(row * gld + cv * VE)) * sizeof(T));
+        }
+    }
+    // row `row` times 1/den[row], written as hi (and lo for bf16) element copies
+    __device__ __forceinline__ void store_scaled_split(T *hi, T *lo, int ldn, const float *den, int tid) const {
 #pragma unroll
         for (int it = 0; it < PER; ++it) {
             int vi = tid + it * NTHR;
             int row = vi / VPR, cv = vi % VPR;
-            if (vi < NV && row < nrows) {
-                r[it] = *reinterpret_cast<const vec_t *>(g + (size_t)row * gld + cv * VE);
-            } else {
-#pragma unroll
-                for (int e = 0; e < VE; ++e) r[it][e] = fromf<T>(0.f);
-            }
-        }
-    }
-    // every element of row `row` is divided by den[row] (forms dO / den)
-    __device__ __forceinline__ void scale_rows_inv(const float *den, int tid) {
-#pragma unroll
-        for (int it = 0; it < PER; ++it) {
-            int vi = tid + it * NTHR;
-            int row = vi / VPR;
             if (vi < NV) {
-                float s = 1.f / den[row];
+                const float s = 1.f / den[row];
+                vec_t h, l;
 #pragma unroll
-                for (int e = 0; e < VE; ++e) r[it][e] = fromf<T>(tof(r[it][e]) * s);
+                for (int e = 0; e < VE; ++e) {
+                    const float x = tof(r[it][e]) * s;
+                    h[e] = fromf<T>(x);
+                    l[e] = fromf<T>(x - tof(h[e]));
+                }
+                *reinterpret_cast<vec_t *>(hi + row * ldn + cv * VE) = h;
+                if (sizeof(T) == 2) *reinterpret_cast<vec_t *>(lo + row * ldn + cv * VE) = l;
             }
         }
     }
@@ -257,33 +369,6 @@ struct Stager {
 #pragma unroll
                     for (int e = 0; e < VE; ++e) tr[(cv * VE + e) * ldt + row] = r[it][e];
                 }
-            }
-        }
-    }
-};
-
-// A [NR][NC] fp32 matrix (global row pitch gld) moved to LDS (row pitch lds) through
-// registers: load() issues the 16-byte global reads, store() writes LDS, so the
-// loads can be in flight while other work is issued.  src == nullptr gives zeros.
-template <int NR, int NC>
-struct F32Tile {
-    static constexpr int VPR = NC / 4, NV = NR * VPR, PER = (NV + NTHR - 1) / NTHR;
-    floatx4 r[PER];
-    __device__ __forceinline__ void load(const float *src, int gld, int tid) {
-#pragma unroll
-        for (int it = 0; it < PER; ++it) {
-            const int vi = tid + it * NTHR;
-            const int row = vi / VPR, cv = vi % VPR;
-            r[it] = (src && vi < NV) ? *reinterpret_cast<const floatx4 *>(src + (size_t)row * gld + 4 * cv) : zero4();
-        }
-    }
-    __device__ __forceinline__ void store(float *dst, int lds, int tid) const {
-#pragma unroll
-        for (int it = 0; it < PER; ++it) {
-            const int vi = tid + it * NTHR;
-            if (vi < NV) {
-                const int row = vi / VPR, cv = vi % VPR;
-                *reinterpret_cast<floatx4 *>(dst + row * lds + 4 * cv) = r[it];
             }
         }
     }
