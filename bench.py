@@ -5,9 +5,16 @@
 One step is one forward and one backward launch (the whole path) over one
 batch of seeded synthetic inputs already resident in device memory.  Steps
 rotate over enough buffer sets (>= 640 MB) that the 256 MB last-level cache
-cannot serve the traffic.  The timed region is bracketed by device
-synchronisation; per-kernel durations come from HIP events recorded around
-each launch on the stream the kernels run on.  Prints one JSON line.
+cannot serve the traffic.  Two timed regions, each bracketed by device
+synchronisation:
+  1. K plain steps: the throughput `value` and `ms_per_step`;
+  2. K more steps in which every launch carries a pair of HIP events recorded
+     on its kernel dispatch (la_time_next_launch): the per-kernel durations
+     behind the roofline.  Those events cost host time per launch, which is why
+     they stay out of region 1.
+Prints one JSON line.
+
+    python bench.py --copy-calibration   # one plain device copy of known size, for counter scaling
 """
 from __future__ import annotations
 
@@ -79,6 +86,19 @@ def cpu_baseline(I, w, min_seconds=10.0):
                       f"median of {len(times)} repeats ({sum(times):.1f} s of CPU work)"}
 
 
+def copy_calibration(torch, mib=256, reps=5):
+    """Plain copies of a known byte count: what FETCH_SIZE / WRITE_SIZE read for them scales the
+    counters taken on the kernels to bytes."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n * 4, "bytes_written": n * 4, "launches": reps}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,6 +107,8 @@ def main():
     ap.add_argument("--workload", default="g160_c128_d64_bf16_fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--footprint-mb", type=float, default=640.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only plain 256 MiB device-to-device copies (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -95,6 +117,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     import causal_linear_attention_chunked_amd as lac
     from causal_linear_attention_chunked_amd import inputs as inp
 
@@ -132,24 +157,29 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * K)]
+    # region 1: plain steps
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(K):
-        s = sets[i % nsets]
-        ev[3 * i].record()
-        lac.fwd(s["q"], s["k"], s["v"], s["S_in"], s["z_in"], out=s["fout"])
-        ev[3 * i + 1].record()
-        lac.bwd(s["q"], s["k"], s["v"], s["S_in"], s["z_in"], s["dO"], out=s["bout"])
-        ev[3 * i + 2].record()
+        step(sets[i % nsets])
     end.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    fwd_ms = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(K)) / K
-    bwd_ms = sum(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(K)) / K
-    ms_per_step = total_ms / K
+    ms_per_step = start.elapsed_time(end) / K
     value = G * C / (ms_per_step / 1e3)
+
+    # region 2: the same steps with dispatch-bound events on every launch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        s = sets[i % nsets]
+        lac.time_next_launch(ev[i][0], ev[i][1])
+        lac.fwd(s["q"], s["k"], s["v"], s["S_in"], s["z_in"], out=s["fout"])
+        lac.time_next_launch(ev[i][2], ev[i][3])
+        lac.bwd(s["q"], s["k"], s["v"], s["S_in"], s["z_in"], s["dO"], out=s["bout"])
+    torch.cuda.synchronize()
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    bwd_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
 
     bwd_gbs = bwd_bytes / (bwd_ms / 1e3) / 1e9
     fwd_gbs = fwd_bytes / (fwd_ms / 1e3) / 1e9
@@ -160,7 +190,8 @@ def main():
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "G": G, "C": C, "D": D, "block": w.block, "carry": w.carry,
                    "buffer_sets": nsets, "footprint_mb": round(nsets * set_bytes / 1e6, 1),
-                   "graph_captured": False},
+                   "graph_captured": False,
+                   "kernel_timing": "HIP events recorded on each kernel dispatch, separate timed loop"},
         "roofline": {"bound": "hbm", "kernel": "la_bwd_kernel", "achieved": bwd_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": bwd_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": bwd_bytes, "avg_us": bwd_ms * 1e3},

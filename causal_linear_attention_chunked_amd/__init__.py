@@ -8,6 +8,7 @@ raises.  PyTorch supplies device memory and the current stream.
 
     o, S_out, z_out = fwd(q, k, v, S_in=None, z_in=None)
     dq, dk, dv, dS_in, dz_in = bwd(q, k, v, S_in, z_in, dO, dS_out=None, dz_out=None)
+    time_next_launch(start_event, stop_event)   # kernel-only timing of the next call
 
 q, k, v, dO: contiguous (G, C, D) CUDA tensors, float32 or bfloat16 (one dtype
 for all); S: (G, D, D) float32 with S[p][c] (p key feature, c value feature);
@@ -20,7 +21,7 @@ import os
 import threading
 
 __all__ = ["fwd", "bwd", "chain_fwd", "chain_bwd", "LachunkError", "lib_path", "load_library",
-           "abi_version", "status_str", "BWD_MAX_C"]
+           "abi_version", "status_str", "time_next_launch", "BWD_MAX_C"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liblachunk.so")
@@ -62,6 +63,8 @@ def load_library():
         lib.la_status_str.argtypes = [i]
         lib.la_abi_version.restype = i
         lib.la_abi_version.argtypes = []
+        lib.la_time_next_launch.restype = i
+        lib.la_time_next_launch.argtypes = [vp, vp]
         _lib = lib
         return lib
 
@@ -72,6 +75,18 @@ def abi_version() -> int:
 
 def status_str(s: int) -> str:
     return load_library().la_status_str(int(s)).decode()
+
+
+def time_next_launch(start_event, stop_event):
+    """Have the next fwd/bwd call on this thread record two ``torch.cuda.Event``
+    (created with ``enable_timing=True``) on its kernel dispatch itself, so that
+    ``start_event.elapsed_time(stop_event)`` is the kernel's own duration."""
+    evs = []
+    for e in (start_event, stop_event):
+        if e.cuda_event == 0:  # torch creates the underlying event on first record
+            e.record()
+        evs.append(ctypes.c_void_p(e.cuda_event))
+    _check("la_time_next_launch", load_library().la_time_next_launch(*evs))
 
 
 def _ptr(t):

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/la_chunk.h: argument validation,
-// dispatch to the typed launchers, status strings.  Validation happens before
-// any HIP call, so an invalid call touches neither the device nor the runtime.
+// dispatch to the typed launchers, status strings, the launch-timing hook.
+// Validation happens before any HIP call, so an invalid call touches neither
+// the device nor the runtime.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -35,6 +36,14 @@ struct Sizes {
     size_t tok, st, z;  // bytes of one token tensor, one state tensor, one normaliser
 };
 
+// Timing events for the next launch on this thread (la_time_next_launch); taken by that launch.
+thread_local hipEvent_t pending_ev[2] = {nullptr, nullptr};
+
+struct TakenEvents {
+    hipEvent_t ev[2];
+    TakenEvents() : ev{pending_ev[0], pending_ev[1]} { pending_ev[0] = pending_ev[1] = nullptr; }
+};
+
 la_status common_checks(int G, int C, int D, int block, la_dtype dt, Sizes *sz) {
     if (G < 1 || C < 1) return LA_ERR_INVALID;
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_UNSUPPORTED;
@@ -44,6 +53,9 @@ la_status common_checks(int G, int C, int D, int block, la_dtype dt, Sizes *sz) 
     size_t a, b;
     if (!mul_ok((size_t)G, (size_t)C, &a) || !mul_ok(a, (size_t)D, &b) || !mul_ok(b, esz, &sz->tok))
         return LA_ERR_INVALID;
+    // the kernels address one group's chunk with 32-bit byte offsets (buffer resources),
+    // with up to two windows of 128 tokens read past its end
+    if ((size_t)C * D * esz + (size_t)256 * D * esz >= ((size_t)1 << 31)) return LA_ERR_UNSUPPORTED;
     if (!mul_ok((size_t)G, (size_t)D * D, &a) || !mul_ok(a, 4, &sz->st)) return LA_ERR_INVALID;
     sz->z = (size_t)G * D * 4;
     return LA_OK;
@@ -67,6 +79,7 @@ extern "C" {
 la_status la_chunk_fwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
                        void *o, float *S_out, float *z_out, int G, int C, int D, int block, la_dtype dt,
                        void *stream) {
+    const TakenEvents te;
     Sizes sz;
     la_status st = common_checks(G, C, D, block, dt, &sz);
     if (st != LA_OK) return st;
@@ -83,17 +96,18 @@ la_status la_chunk_fwd(const void *q, const void *k, const void *v, const float 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (dt == LA_BF16)
-        e = D == 64 ? lachunk::launch_fwd<__bf16, 64>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s)
-                    : lachunk::launch_fwd<__bf16, 128>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s);
+        e = D == 64 ? lachunk::launch_fwd<__bf16, 64>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s, te.ev)
+                    : lachunk::launch_fwd<__bf16, 128>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s, te.ev);
     else
-        e = D == 64 ? lachunk::launch_fwd<float, 64>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s)
-                    : lachunk::launch_fwd<float, 128>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s);
+        e = D == 64 ? lachunk::launch_fwd<float, 64>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s, te.ev)
+                    : lachunk::launch_fwd<float, 128>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s, te.ev);
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
 la_status la_chunk_bwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
                        const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
                        float *dS_in, float *dz_in, int G, int C, int D, int block, la_dtype dt, void *stream) {
+    const TakenEvents te;
     Sizes sz;
     la_status st = common_checks(G, C, D, block, dt, &sz);
     if (st != LA_OK) return st;
@@ -116,12 +130,12 @@ la_status la_chunk_bwd(const void *q, const void *k, const void *v, const float 
     hipError_t e;
     if (dt == LA_BF16)
         e = D == 64 ? lachunk::launch_bwd<__bf16, 64>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in,
-                                                     dz_in, G, C, s)
+                                                     dz_in, G, C, s, te.ev)
                     : lachunk::launch_bwd<__bf16, 128>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in,
-                                                      dz_in, G, C, s);
+                                                      dz_in, G, C, s, te.ev);
     else
         e = lachunk::launch_bwd<float, 64>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, G, C,
-                                           s);
+                                           s, te.ev);
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
@@ -138,5 +152,12 @@ const char *la_status_str(la_status s) {
 }
 
 int la_abi_version(void) { return LA_ABI_VERSION; }
+
+la_status la_time_next_launch(void *start_event, void *stop_event) {
+    if ((start_event == nullptr) != (stop_event == nullptr)) return LA_ERR_INVALID;
+    pending_ev[0] = reinterpret_cast<hipEvent_t>(start_event);
+    pending_ev[1] = reinterpret_cast<hipEvent_t>(stop_event);
+    return LA_OK;
+}
 
 }  // extern "C"

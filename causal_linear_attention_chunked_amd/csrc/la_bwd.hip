@@ -22,6 +22,7 @@
 // holds natural row-major tiles only, double-buffered and loaded two blocks ahead.
 #include "la_common.h"
 #include "la_launch.h"
+#include <hip/hip_ext.h>
 #include "../../include/la_chunk.h"
 
 namespace lachunk {
@@ -665,21 +666,22 @@ __global__ __launch_bounds__(NTHR, 1) void la_bwd_kernel(
 template <typename T, int D>
 hipError_t launch_bwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
                       const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
-                      float *dS_in, float *dz_in, int G, int C, hipStream_t stream) {
-    hipLaunchKernelGGL((la_bwd_kernel<T, D>), dim3((unsigned)G), dim3(NTHR), 0, stream,
-                       (const T *)q, (const T *)k, (const T *)v, S_in, z_in, (const T *)dO, dS_out, dz_out,
-                       (T *)dq, (T *)dk, (T *)dv, dS_in, dz_in, C);
+                      float *dS_in, float *dz_in, int G, int C, hipStream_t stream,
+                      const hipEvent_t ev[2]) {
+    hipExtLaunchKernelGGL((la_bwd_kernel<T, D>), dim3((unsigned)G), dim3(NTHR), 0, stream, ev[0], ev[1], 0,
+                          (const T *)q, (const T *)k, (const T *)v, S_in, z_in, (const T *)dO, dS_out, dz_out,
+                          (T *)dq, (T *)dk, (T *)dv, dS_in, dz_in, C);
     return hipGetLastError();
 }
 
 template hipError_t launch_bwd<float, 64>(const void *, const void *, const void *, const float *, const float *,
                                           const void *, const float *, const float *, void *, void *, void *,
-                                          float *, float *, int, int, hipStream_t);
+                                          float *, float *, int, int, hipStream_t, const hipEvent_t *);
 template hipError_t launch_bwd<bf16, 64>(const void *, const void *, const void *, const float *, const float *,
                                          const void *, const float *, const float *, void *, void *, void *,
-                                         float *, float *, int, int, hipStream_t);
+                                         float *, float *, int, int, hipStream_t, const hipEvent_t *);
 template hipError_t launch_bwd<bf16, 128>(const void *, const void *, const void *, const float *, const float *,
                                           const void *, const float *, const float *, void *, void *, void *,
-                                          float *, float *, int, int, hipStream_t);
+                                          float *, float *, int, int, hipStream_t, const hipEvent_t *);
 
 }  // namespace lachunk

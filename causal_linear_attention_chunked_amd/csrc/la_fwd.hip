@@ -3,42 +3,59 @@
 // exact per-token cumsum for the ragged tail.
 //
 // Grid: one workgroup per (group, 64-wide slice of value columns); 8 waves, two per SIMD.
-// Per 64-token block b, with the running state S_run (fp32 MFMA accumulators
-// spread over the waves, mirrored in LDS as split S^T copies) and z_run (LDS):
-//   scores  P^T = K_b Q_b^T, masked to j <= t (inclusive)   [wave w: queries 16w..16w+15]
-//   den_t   = sum_j P[t][j] + q_t . z_run                     [row sums by lane shuffles]
-//   num^T   = V_b^T P^T + S_run^T Q_b^T                       [state read BEFORE the update]
+// The 64-token blocks are taken WIN at a time (a window; WIN = 2 except fp32 at D = 128).
+// Only the running state carries a dependency from one block to the next, and it
+// is cheap, so inside a window the state is advanced first and the blocks'
+// outputs are then computed side by side, waves 0-3 on the first block, 4-7 on
+// the second.  Per block b of a window, with S_b / z_b the state before it:
+//   S_b+1   = S_b + K_b^T V_b,   z_b+1 = z_b + K_b^T 1                [update]
+//   P^T     = K_b Q_b^T, masked to j <= t (inclusive)                 [wave: 16 queries]
+//   num^T   = V_b^T P^T + S_b^T Q_b^T                                  [all 64 value columns]
+//   den     = 1^T P^T + z_b^T Q_b^T                                    [a ones row: no shuffles]
 //   o_t     = num_t / den_t
-//   S_run  += K_b^T V_b,  z_run += K_b^T 1                    [update after reading]
 // then the ragged tail token by token: S += k v^T, z += k, o = S^T q / (q . z).
-// Staging is natural row-major only: transposed operands (K^T, V^T) come from
-// LDS transpose reads.  Blocks are double-buffered in LDS and loaded two ahead.
+// The state lives in the waves' MFMA accumulators (fp32) and, for operand reads,
+// as a bf16 S^T copy per block start in LDS.  The intra-block scores P enter the
+// MFMAs as split hi + lo operands; the state copy does not need to (its term
+// has no cancellation against the others).  Staging is natural row-major only:
+// transposed operands come from LDS transpose reads.  The next window's loads
+// are issued as soon as the current window is staged.
 #include "la_common.h"
 #include "la_launch.h"
+#include <hip/hip_ext.h>
 
 namespace lachunk {
 
+template <typename T, int D> constexpr int fwd_window() { return (is_bf16<T>() || D == 64) ? 2 : 1; }
+
 template <typename T, int D>
 struct FwdLds {
+    static constexpr int WIN = fwd_window<T, D>();
     static constexpr int PAD = Elem<T>::PAD;
-    static constexpr int LDN = D + PAD;    // K rows [BK][LDN]
-    static constexpr int LDV = 64 + PAD;   // V slice rows [BK][LDV]
+    static constexpr int LDN = D + PAD;    // K rows [WIN*BK][LDN]
+    static constexpr int LDV = 64 + PAD;   // V slice rows [WIN*BK][LDV]
     static constexpr int LDST = D + PAD;   // S^T copies [64 value columns][LDST]
-    static constexpr int NCOPY = is_bf16<T>() ? 2 : 1;
-    static constexpr int ZS = 0;                                         // [NTHR] z_run (first D used)
-    static constexpr int STH = NTHR * 4;                                 // S^T hi
-    static constexpr int STL = STH + 64 * LDST * (int)sizeof(T);         // S^T lo (bf16 only)
-    static constexpr int STAGE = STH + NCOPY * 64 * LDST * (int)sizeof(T);
-    static constexpr int KBUF = BK * LDN * (int)sizeof(T);
-    static constexpr int VBUF = BK * LDV * (int)sizeof(T);
-    static constexpr int BLOCK_END = STAGE + 2 * (KBUF + VBUF);          // two staging buffers
-    // ragged-tail phase (reuses the staging space)
-    static constexpr int LDSF = 64 + 4;
-    static constexpr int TQ = STAGE, TK = TQ + KBUF, TV = TK + KBUF, SF = TV + VBUF;
-    static constexpr int TAIL_END = SF + D * LDSF * 4;
-    static constexpr int BYTES = BLOCK_END > TAIL_END ? BLOCK_END : TAIL_END;
+    static constexpr int LDSF = 64 + 4;    // fp32 state, tail phase
+    static constexpr int ESZ = (int)sizeof(T);
+    static constexpr int ZS = 0;                                   // [WIN][D] z at the block starts
+    static constexpr int ST = ZS + WIN * D * 4;                    // [WIN][64][LDST]
+    static constexpr int ST_ELEMS = 64 * LDST;
+    static constexpr int KB = ST + WIN * ST_ELEMS * ESZ;            // [WIN*BK][LDN]
+    static constexpr int VB = KB + WIN * BK * LDN * ESZ;            // [WIN*BK][LDV]
+    static constexpr int TQ = VB + WIN * BK * LDV * ESZ;            // tail queries [BK][LDN]
+    static constexpr int SF = TQ + BK * LDN * ESZ;                  // tail state [D][LDSF] fp32
+    static constexpr int BYTES = SF + D * LDSF * 4;
+    static_assert(ST % 16 == 0 && KB % 16 == 0 && VB % 16 == 0 && TQ % 16 == 0 && SF % 16 == 0, "LDS alignment");
     static_assert(BYTES <= 160 * 1024, "forward LDS budget exceeded");
 };
+
+// fp32 values z[kslot(lane, s)] of one k-chunk, the same for every row of the fragment
+__device__ __forceinline__ floatx8 zrow8(const float *z, int lane) {
+    const float *p = z + 4 * (lane >> 4);
+    const floatx4 a = *reinterpret_cast<const floatx4 *>(p);
+    const floatx4 b = *reinterpret_cast<const floatx4 *>(p + 16);
+    return floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(NTHR, 1) void la_fwd_kernel(
@@ -46,21 +63,24 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_kernel(
     const float *__restrict__ S_in, const float *__restrict__ z_in,
     T *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out, int C) {
     using L = FwdLds<T, D>;
+    constexpr int WIN = L::WIN;
     constexpr int NVS = D / 64;          // value slices per group
-    constexpr int NPT = D / 64;          // key-feature tiles of the state per wave
     constexpr int NKC = D / 32;          // k-chunks over the feature dimension
+    constexpr int NOWN = D / 32;         // state tiles per wave (16 x 16 each)
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
     float *zs = reinterpret_cast<float *>(smem + L::ZS);
-    T *STh = reinterpret_cast<T *>(smem + L::STH);
-    T *STl = reinterpret_cast<T *>(smem + L::STL);
-    auto Kbuf = [&](int i) { return reinterpret_cast<T *>(smem + L::STAGE + i * (L::KBUF + L::VBUF)); };
-    auto Vbuf = [&](int i) { return reinterpret_cast<T *>(smem + L::STAGE + i * (L::KBUF + L::VBUF) + L::KBUF); };
+    T *ST = reinterpret_cast<T *>(smem + L::ST);
+    T *Ks = reinterpret_cast<T *>(smem + L::KB);
+    T *Vs = reinterpret_cast<T *>(smem + L::VB);
 
-    // wave w: query tile tq = w % 4 (16 tokens of each block) and value-column half hh = w / 4
-    // (column tiles 2hh, 2hh+1 of the 64-wide slice); the same pair indexes its share of the state
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
-    const int tq = w & 3, hh = w >> 2;
+    // outputs: block `blk` of the window, query tile tq (reversed on the second block, so
+    // waves that share a SIMD carry one long and one short causal row range)
+    const int blk = w >> 2;
+    const int tq = blk ? 3 - (w & 3) : (w & 3);
+    // state: value tile ct, key-feature tiles pt0 + 2i
+    const int ct = w & 3, pt0 = w >> 2;
     const int grp = blockIdx.x / NVS, vs = blockIdx.x % NVS;
     const size_t tok0 = (size_t)grp * C;
     const uint32_t chunk_bytes = (uint32_t)C * D * sizeof(T);
@@ -68,194 +88,202 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_kernel(
     // an absent carry is an empty range (reads give zero); the base only has to be a valid address
     const GRes sres(S_in ? (const void *)(S_in + (size_t)grp * D * D) : (const void *)S_out, S_in ? D * D * 4 : 0);
     const GRes zres(z_in ? (const void *)(z_in + (size_t)grp * D) : (const void *)z_out, z_in ? D * 4 : 0);
+    // waves without a block of their own (one-block windows) read nothing
+    const GRes qw(q + tok0 * D, blk < WIN ? chunk_bytes : 0);
     T *og = o + tok0 * D + vs * 64;
     const int nb = C / BK, tail = C % BK;
+    const int nwin = (nb + WIN - 1) / WIN;
 
-    struct Block {
-        Stager<T, D> k;
-        Stager<T, 64> v;
+    struct Window {
+        Stager<T, D> k[WIN];
+        Stager<T, 64> v[WIN];
         Frag<T> qf[NKC];
     };
-    auto load_block = [&](Block &x, int b) {  // blocks past the chunk read as zero
-        const uint32_t t0 = (uint32_t)b * BK;
-        x.k.load(kr, t0 * D, D, tid);
-        x.v.load(vr, t0 * D + vs * 64, D, tid);
+    auto load_window = [&](Window &x, int wi) {  // rows past the chunk read as zero
+        const uint32_t t0 = (uint32_t)wi * WIN * BK;
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) x.qf[kc] = ldfrag_g<T>(qr, (t0 + 16 * tq) * D + 32 * kc, D, lane);
+        for (int bi = 0; bi < WIN; ++bi) {
+            x.k[bi].load(kr, (t0 + bi * BK) * D, D, tid);
+            x.v[bi].load(vr, (t0 + bi * BK) * D + vs * 64, D, tid);
+        }
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+            x.qf[kc] = ldfrag_g<T>(qw, (t0 + blk * BK + 16 * tq) * D + 32 * kc, D, lane);
     };
-    auto store_block = [&](const Block &x, int buf) {
-        x.k.store(Kbuf(buf), L::LDN, nullptr, 0, tid);
-        x.v.store(Vbuf(buf), L::LDV, nullptr, 0, tid);
+    auto store_window = [&](const Window &x) {
+#pragma unroll
+        for (int bi = 0; bi < WIN; ++bi) {
+            x.k[bi].store(Ks + bi * BK * L::LDN, L::LDN, nullptr, 0, tid);
+            x.v[bi].store(Vs + bi * BK * L::LDV, L::LDV, nullptr, 0, tid);
+        }
     };
 
-    // ---- prologue: block 0 and the carry.  Each loop iteration first moves the block
-    // prefetched into registers to its LDS buffer and at once issues the next block's loads,
-    // which then run under this block's compute.
-    Block nxt;
-    load_block(nxt, 0);
-    floatx4 Sacc[NPT][2];  // acc(p, c): p-tiles tq + 4*pi, c-tiles 2hh + cc
+    // ---- prologue: window 0, the tail's queries and the carry, all issued before any wait
+    Window nxt;
+    load_window(nxt, 0);
+    Stager<T, D> qtail;
+    qtail.load(tail ? qr : GRes(q, 0), (uint32_t)nb * BK * D, D, tid);
+    floatx4 Sacc[NOWN];  // S[p][c], p-tile pt0 + 2i, c-tile ct: lane (c = r), element e: p = 4g + e
+    floatx4 zr[NOWN];    // z[p] for the same p-tiles (every lane; kept current by the waves of c-tile 0)
 #pragma unroll
-    for (int pi = 0; pi < NPT; ++pi)
+    for (int i = 0; i < NOWN; ++i)
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                Sacc[pi][cc][i] = gload<float>(sres, ((16 * (tq + 4 * pi) + 4 * g + i) * D + vs * 64 + 16 * (2 * hh + cc) + r) * 4);
-    const float zin = gload<float>(zres, tid * 4);  // threads past D read zero
+        for (int e = 0; e < 4; ++e) {
+            const int p = 16 * (pt0 + 2 * i) + 4 * g + e;
+            Sacc[i][e] = gload<float>(sres, (p * D + vs * 64 + 16 * ct + r) * 4);
+            zr[i][e] = gload<float>(zres, p * 4);
+        }
     __syncthreads();  // keeps every prologue load issued here, ahead of the first wait
-    auto write_copies = [&]() {
-#pragma unroll
-        for (int pi = 0; pi < NPT; ++pi)
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                const int off = (16 * (2 * hh + cc) + r) * L::LDST + 16 * (tq + 4 * pi) + 4 * g;
-                store_split4<T>(STh + off, STl + off, Sacc[pi][cc]);
-            }
-    };
-    write_copies();
-    zs[tid] = zin;
 
+    // state copy s <- (Sacc, zr); z is written by the waves of value tile 0
+    auto write_state = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < NOWN; ++i) {
+            const int p0 = 16 * (pt0 + 2 * i) + 4 * g;
+            *reinterpret_cast<Vec4<T> *>(ST + s * L::ST_ELEMS + (16 * ct + r) * L::LDST + p0) = to_vec4<T>(Sacc[i]);
+            if (ct == 0 && r == 0) *reinterpret_cast<floatx4 *>(zs + s * D + p0) = zr[i];
+        }
+    };
     const Frag<T> ones = ones_frag<T>();
-    for (int b = 0; b < nb; ++b) {
-        const int t0 = b * BK, buf = b & 1;
-        const T *Kn = Kbuf(buf), *Vn = Vbuf(buf);
-        store_block(nxt, buf);
+    // S += K_bi^T V_bi and z += K_bi^T 1 over one staged block
+    auto update = [&](int bi) {
+#pragma unroll
+        for (int kc2 = 0; kc2 < 2; ++kc2) {
+            const int t0 = bi * BK + 32 * kc2;
+            const Frag<T> vt = ldfrag_tr<T>(Vs + t0 * L::LDV + 16 * ct, L::LDV, lane);
+#pragma unroll
+            for (int i = 0; i < NOWN; ++i) {
+                const Frag<T> kt = ldfrag_tr<T>(Ks + t0 * L::LDN + 16 * (pt0 + 2 * i), L::LDN, lane);
+                mma(Sacc[i], kt, vt);
+                if (ct == 0) mma(zr[i], kt, ones);
+            }
+        }
+    };
+    write_state(0);
+
+    for (int wi = 0; wi < nwin; ++wi) {
+        const int nblk = (nb - wi * WIN) < WIN ? (nb - wi * WIN) : WIN;
+        const int t0 = wi * WIN * BK;
+        store_window(nxt);
         Frag<T> qc[NKC];
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) qc[kc] = nxt.qf[kc];
-        load_block(nxt, b + 1);  // past the end of the chunk: zeros, no memory traffic
-        __syncthreads();  // block b staged; the previous update of the state copies and z_run visible
-        // scores P^T[j][t] for every key tile (tiles after the diagonal are masked to zero)
-        floatx4 sc[4];
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) sc[jt] = zero4();
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-            Frag<T> kf[4];
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt) kf[jt] = ldfrag<T>(Kn + 16 * jt * L::LDN + 32 * kc, L::LDN, lane);
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt) mma(sc[jt], kf[jt], qc[kc]);
-        }
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool keep = jt < tq || (jt == tq && 4 * g + i <= r);
-                sc[jt][i] = keep ? sc[jt][i] : 0.f;
-            }
-        // den_t = sum_j P[t][j] + q_t . z_run
-        float dsum = 0.f;
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dsum += sc[jt][i];
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-            for (int s = 0; s < 8; ++s) dsum += tof(qc[kc][s]) * zs[32 * kc + kslot(lane, s)];
-        dsum = wsum_g(dsum);
-        const float inv = 1.f / dsum;
+        load_window(nxt, wi + 1);  // past the end of the chunk: zeros, no memory traffic
+        __syncthreads();           // window staged; state copy 0 visible
 
-        // num^T[c][t] = V^T P^T (intra) + S_run^T Q^T (inter, state before this block), own columns
-        Frag<T> vt[2][2];  // V^T rows c (k = key), reused by the state update
+        if constexpr (WIN == 2) {  // state after the window's first block: copy 1
+            update(0);
+            write_state(1);
+        }
+        // intra-block part of this wave's outputs: needs only the staged K, V and its queries
+        const bool active = blk < nblk;
+        const T *Kb = Ks + blk * BK * L::LDN;
+        const T *Vb = Vs + blk * BK * L::LDV;
+        floatx4 nm[4], dn = zero4();
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
+        for (int c = 0; c < 4; ++c) nm[c] = zero4();
+        if (active) {
+            floatx4 sc[4];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) vt[cc][h] = ldfrag_tr<T>(Vn + 32 * h * L::LDV + 16 * (2 * hh + cc), L::LDV, lane);
-        {
+            for (int jt = 0; jt < 4; ++jt) {
+                sc[jt] = zero4();
+                if (jt <= tq) {
+#pragma unroll
+                    for (int kc = 0; kc < NKC; ++kc)
+                        mma(sc[jt], ldfrag<T>(Kb + 16 * jt * L::LDN + 32 * kc, L::LDN, lane), qc[kc]);
+                }
+                if (jt == tq) {  // diagonal tile: keep key j <= query t
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sc[jt][e] = 4 * g + e <= r ? sc[jt][e] : 0.f;
+                }
+            }
             const SFrag<T> pf0 = split8<T>(acc8(sc[0], sc[1]));
-            const SFrag<T> pf1 = split8<T>(acc8(sc[2], sc[3]));
-            floatx4 nm[2];
+            mma_xs<T>(dn, ones, pf0);
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                nm[cc] = zero4();
-                mma_xs<T>(nm[cc], vt[cc][0], pf0);
-                mma_xs<T>(nm[cc], vt[cc][1], pf1);
+            for (int c = 0; c < 4; ++c) mma_xs<T>(nm[c], ldfrag_tr<T>(Vb + 16 * c, L::LDV, lane), pf0);
+            if (tq >= 2) {
+                const SFrag<T> pf1 = split8<T>(acc8(sc[2], sc[3]));
+                mma_xs<T>(dn, ones, pf1);
 #pragma unroll
-                for (int kc = 0; kc < NKC; ++kc) {
-                    const int off = 16 * (2 * hh + cc) * L::LDST + 32 * kc;
-                    mma_sx<T>(nm[cc], ldsplit<T>(STh + off, STl + off, L::LDST, lane), qc[kc]);
-                }
-            }
-            T *orow = og + (size_t)(t0 + 16 * tq + r) * D + 32 * hh + 4 * g;
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) *reinterpret_cast<Vec4<T> *>(orow + 16 * cc) = to_vec4<T>(nm[cc] * inv);
-        }
-        __syncthreads();  // every wave is done reading the state copies and z_run of this block
-
-        // update after reading: S_run += K^T V, z_run += K^T 1
-#pragma unroll
-        for (int pi = 0; pi < NPT; ++pi) {
-            const int p0 = 16 * (tq + 4 * pi);
-            const Frag<T> kt0 = ldfrag_tr<T>(Kn + p0, L::LDN, lane);
-            const Frag<T> kt1 = ldfrag_tr<T>(Kn + 32 * L::LDN + p0, L::LDN, lane);
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                mma(Sacc[pi][cc], kt0, vt[cc][0]);
-                mma(Sacc[pi][cc], kt1, vt[cc][1]);
-            }
-            if (hh == 0) {
-                floatx4 zacc = zero4();
-                mma(zacc, kt0, ones);
-                mma(zacc, kt1, ones);
-                if (r == 0) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) zs[p0 + 4 * g + i] += zacc[i];
-                }
+                for (int c = 0; c < 4; ++c)
+                    mma_xs<T>(nm[c], ldfrag_tr<T>(Vb + 32 * L::LDV + 16 * c, L::LDV, lane), pf1);
             }
         }
-        write_copies();
+        if constexpr (WIN == 2) __syncthreads();  // state copy 1 visible
+        if (active) {
+            // inter-block part: the state before this block, read before it is updated
+            const T *STb = ST + blk * L::ST_ELEMS;
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+                mma_sx<T>(dn, split8<T>(zrow8(zs + blk * D + 32 * kc, lane)), qc[kc]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    mma(nm[c], ldfrag<T>(STb + 16 * c * L::LDST + 32 * kc, L::LDST, lane), qc[kc]);
+            }
+            const float inv = __builtin_amdgcn_rcpf(dn[0]);
+            T *orow = og + (size_t)(t0 + blk * BK + 16 * tq + r) * D + 4 * g;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) *reinterpret_cast<Vec4<T> *>(orow + 16 * c) = to_vec4<T>(nm[c] * inv);
+        }
+        // state after the window
+        if constexpr (WIN == 2) {
+            if (nblk == 2) update(1);
+        } else {
+            update(0);
+        }
+        if (wi + 1 < nwin) {
+            __syncthreads();  // every wave is done reading this window's staging and state copies
+            write_state(0);
+        }
     }
 
     if (tail == 0) {
-        float *Sg = S_out + (size_t)grp * D * D + vs * 64;
+        float *Sg = S_out + (size_t)grp * D * D + vs * 64 + 16 * ct + r;
 #pragma unroll
-        for (int pi = 0; pi < NPT; ++pi)
+        for (int i = 0; i < NOWN; ++i)
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc)
+            for (int e = 0; e < 4; ++e) Sg[(size_t)(16 * (pt0 + 2 * i) + 4 * g + e) * D] = Sacc[i][e];
+        if (vs == 0 && ct == 0 && r == 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Sg[(size_t)(16 * (tq + 4 * pi) + 4 * g + i) * D + 16 * (2 * hh + cc) + r] = Sacc[pi][cc][i];
-        __syncthreads();
-        if (vs == 0 && tid < D) z_out[(size_t)grp * D + tid] = zs[tid];
+            for (int i = 0; i < NOWN; ++i)
+                *reinterpret_cast<floatx4 *>(z_out + (size_t)grp * D + 16 * (pt0 + 2 * i) + 4 * g) = zr[i];
+        }
         return;
     }
 
-    // ---- ragged tail: exact per-token cumsum from (S_run, z_run); waves 0..3 own the columns
+    // ---- ragged tail: exact per-token cumsum from (S_run, z_run).  Its keys and values are
+    // either the empty block slot of the last window (already staged) or the prefetch of the
+    // window after it (still in registers).
     T *Tq = reinterpret_cast<T *>(smem + L::TQ);
-    T *Tk = reinterpret_cast<T *>(smem + L::TK);
-    T *Tv = reinterpret_cast<T *>(smem + L::TV);
     float *Sf = reinterpret_cast<float *>(smem + L::SF);
+    const int slot = nb % WIN;
     const int tt0 = nb * BK;
-    {
-        Stager<T, D> qs, ks;
-        Stager<T, 64> vs_;
-        qs.load(qr, tt0 * D, D, tid);  // rows past the chunk read as zero
-        ks.load(kr, tt0 * D, D, tid);
-        vs_.load(vr, tt0 * D + vs * 64, D, tid);
-        __syncthreads();  // the block phase is finished with the staging space
-#pragma unroll
-        for (int pi = 0; pi < NPT; ++pi)
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Sf[(16 * (tq + 4 * pi) + 4 * g + i) * L::LDSF + 16 * (2 * hh + cc) + r] = Sacc[pi][cc][i];
-        qs.store(Tq, L::LDN, nullptr, 0, tid);
-        ks.store(Tk, L::LDN, nullptr, 0, tid);
-        vs_.store(Tv, L::LDV, nullptr, 0, tid);
-        __syncthreads();
+    if (nwin > 0) __syncthreads();  // the window phase is finished with the staging space
+    if (slot == 0) {
+        nxt.k[0].store(Ks, L::LDN, nullptr, 0, tid);
+        nxt.v[0].store(Vs, L::LDV, nullptr, 0, tid);
     }
+    qtail.store(Tq, L::LDN, nullptr, 0, tid);
+#pragma unroll
+    for (int i = 0; i < NOWN; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int p = 16 * (pt0 + 2 * i) + 4 * g + e;
+            Sf[p * L::LDSF + 16 * ct + r] = Sacc[i][e];
+            if (ct == 0 && r == 0) zs[p] = zr[i][e];
+        }
+    __syncthreads();
     if (w >= 4) return;  // no barrier follows
+    const T *Tk = Ks + slot * BK * L::LDN;
+    const T *Tv = Vs + slot * BK * L::LDV;
     // lane owns value column c = 16w + r of the slice and key features p in [g*NP, (g+1)*NP)
     constexpr int NP = D / 4;
     const int c = 16 * w + r;
-    float Sr[NP], zr[NP];
+    float Sr[NP], zl[NP];
 #pragma unroll
     for (int s = 0; s < NP; ++s) {
         Sr[s] = Sf[(g * NP + s) * L::LDSF + c];
-        zr[s] = zs[g * NP + s];
+        zl[s] = zs[g * NP + s];
     }
     for (int t = 0; t < tail; ++t) {
         const float vc = tof(Tv[t * L::LDV + c]);
@@ -270,9 +298,9 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_kernel(
             for (int e = 0; e < 4; ++e) {
                 const float kp = tof(k4[e]), qp = tof(q4[e]);
                 Sr[s4 + e] += kp * vc;  // update first: token t reads a state that includes it
-                zr[s4 + e] += kp;
+                zl[s4 + e] += kp;
                 n += qp * Sr[s4 + e];
-                d += qp * zr[s4 + e];
+                d += qp * zl[s4 + e];
             }
         }
         n = wsum_g(n);
@@ -284,26 +312,27 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_kernel(
     for (int s = 0; s < NP; ++s) Sg[(size_t)(g * NP + s) * D + c] = Sr[s];
     if (vs == 0 && w == 0 && r == 0) {
 #pragma unroll
-        for (int s = 0; s < NP; ++s) z_out[(size_t)grp * D + g * NP + s] = zr[s];
+        for (int s = 0; s < NP; ++s) z_out[(size_t)grp * D + g * NP + s] = zl[s];
     }
 }
 
 template <typename T, int D>
 hipError_t launch_fwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
-                      void *o, float *S_out, float *z_out, int G, int C, hipStream_t stream) {
+                      void *o, float *S_out, float *z_out, int G, int C, hipStream_t stream,
+                      const hipEvent_t ev[2]) {
     dim3 grid((unsigned)G * (D / 64)), block(NTHR);
-    hipLaunchKernelGGL((la_fwd_kernel<T, D>), grid, block, 0, stream,
-                       (const T *)q, (const T *)k, (const T *)v, S_in, z_in, (T *)o, S_out, z_out, C);
+    hipExtLaunchKernelGGL((la_fwd_kernel<T, D>), grid, block, 0, stream, ev[0], ev[1], 0,
+                          (const T *)q, (const T *)k, (const T *)v, S_in, z_in, (T *)o, S_out, z_out, C);
     return hipGetLastError();
 }
 
 template hipError_t launch_fwd<float, 64>(const void *, const void *, const void *, const float *, const float *,
-                                          void *, float *, float *, int, int, hipStream_t);
+                                          void *, float *, float *, int, int, hipStream_t, const hipEvent_t *);
 template hipError_t launch_fwd<float, 128>(const void *, const void *, const void *, const float *, const float *,
-                                           void *, float *, float *, int, int, hipStream_t);
+                                           void *, float *, float *, int, int, hipStream_t, const hipEvent_t *);
 template hipError_t launch_fwd<bf16, 64>(const void *, const void *, const void *, const float *, const float *,
-                                         void *, float *, float *, int, int, hipStream_t);
+                                         void *, float *, float *, int, int, hipStream_t, const hipEvent_t *);
 template hipError_t launch_fwd<bf16, 128>(const void *, const void *, const void *, const float *, const float *,
-                                          void *, float *, float *, int, int, hipStream_t);
+                                          void *, float *, float *, int, int, hipStream_t, const hipEvent_t *);
 
 }  // namespace lachunk

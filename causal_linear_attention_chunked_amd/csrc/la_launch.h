@@ -1,5 +1,6 @@
 // Typed launchers, one per supported (element type, head dim) pair.  Each
-// enqueues its kernel on `stream` and returns hipGetLastError().
+// enqueues its kernel on `stream` and returns the launch status.  `ev` holds
+// two hipEvent_t (start, stop) recorded on the dispatch itself, or nulls.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -7,11 +8,13 @@ namespace lachunk {
 
 template <typename T, int D>
 hipError_t launch_fwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
-                      void *o, float *S_out, float *z_out, int G, int C, hipStream_t stream);
+                      void *o, float *S_out, float *z_out, int G, int C, hipStream_t stream,
+                      const hipEvent_t ev[2]);
 
 template <typename T, int D>
 hipError_t launch_bwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
                       const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
-                      float *dS_in, float *dz_in, int G, int C, hipStream_t stream);
+                      float *dS_in, float *dz_in, int G, int C, hipStream_t stream,
+                      const hipEvent_t ev[2]);
 
 }  // namespace lachunk

@@ -22,8 +22,9 @@
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer (hipMalloc'd or equivalent),
  *     row-major, contiguous, 16-byte aligned.  The caller allocates and owns all
- *     buffers; the library allocates nothing, keeps no state between calls and
- *     is reentrant.
+ *     buffers; the library allocates nothing and is reentrant.  The only state
+ *     it keeps between calls is a pending timing request (la_time_next_launch),
+ *     per calling thread.
  *   - Token tensors q, k, v, o, dO, dq, dk, dv are [G][C][D] in the element type
  *     `dt` (fp32 or bf16).  The state S (and dS) is [G][D][D] fp32 with S[p][c]:
  *     p indexes the key feature, c the value feature; z (and dz) is [G][D] fp32.
@@ -36,7 +37,9 @@
  *   - Preconditions NOT checked on the device: q_t . z_t > 0 for every token
  *     (true for positive features: q, k > 0 elementwise and z_in >= 0), and
  *     finite inputs.  No epsilon is added to the denominator.
- *   - Supported: D in {64, 128}, block == 64, G >= 1, 1 <= C.  The backward
+ *   - Supported: D in {64, 128}, block == 64, G >= 1, 1 <= C, and one group's
+ *     chunk plus 256 tokens below 2 GiB ((C + 256) * D * element size < 2^31:
+ *     the kernels address a chunk with 32-bit byte offsets).  The backward
  *     additionally needs C <= LA_BWD_MAX_C and, for D == 128, bf16 elements.
  *     Anything else returns LA_ERR_UNSUPPORTED.
  */
@@ -47,7 +50,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 1
+#define LA_ABI_VERSION 2
 #define LA_BWD_MAX_C 2048
 
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
@@ -106,6 +109,19 @@ const char *la_status_str(la_status s);
 
 /* LA_ABI_VERSION of the built library. */
 int la_abi_version(void);
+
+/*
+ * Measurement hook for benchmarks and profilers: the next la_chunk_fwd or
+ * la_chunk_bwd call made by the calling thread records start_event and
+ * stop_event (hipEvent_t, created by the caller with timing enabled) on its
+ * kernel dispatch itself, so hipEventElapsedTime(start, stop) is that kernel's
+ * execution time with no marker packets in between.  Each of the two entry
+ * points launches exactly one kernel.  The request is taken by that next call
+ * whatever its status; (NULL, NULL) clears it.  Returns LA_ERR_INVALID if only
+ * one event is given.  The events are not validated: they must be live events
+ * of the device the next call runs on.
+ */
+la_status la_time_next_launch(void *start_event, void *stop_event);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["la_abi_version", "la_chunk_bwd", "la_chunk_fwd", "la_status_str"]
+    assert declared_functions() == ["la_abi_version", "la_chunk_bwd", "la_chunk_fwd", "la_status_str",
+                                    "la_time_next_launch"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lac.abi_version() == 1
+    assert lac.abi_version() == 2
     for s in range(6):
         assert len(lac.status_str(s)) > 0
     assert lac.status_str(99) == "unknown status"
@@ -106,6 +107,23 @@ def test_fwd_size_overflow(lib):
 ])
 def test_bwd_rejects(lib, kw, status):
     assert bwd_call(lib, **kw) == status
+
+
+def test_fwd_chunk_beyond_32bit_offsets(lib):
+    # (C + 256) * D * 2 bytes must stay below 2^31
+    assert fwd_call(lib, G=1, C=(1 << 31) // (128 * 2), D=128) == UNSUPPORTED
+    assert fwd_call(lib, G=1, C=(1 << 31) // (128 * 4) - 200, D=128, dt=0) == UNSUPPORTED
+    assert bwd_call(lib, G=1, C=(1 << 31) // (64 * 2), D=64) == UNSUPPORTED
+
+
+def test_time_next_launch_pairs(lib):
+    assert lib.la_time_next_launch(addr(0), None) == INVALID
+    assert lib.la_time_next_launch(None, addr(1)) == INVALID
+    assert lib.la_time_next_launch(None, None) == OK
+    # a pending request is taken by the next call even when that call is rejected
+    assert lib.la_time_next_launch(addr(0), addr(1)) == OK
+    assert fwd_call(lib, G=0) == INVALID
+    assert lib.la_time_next_launch(None, None) == OK
 
 
 def test_python_binding_rejects_cpu_tensors(lib):
