@@ -128,7 +128,9 @@ la_status la_chunk_bwd(const void *q, const void *k, const void *v, const float 
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
-    if (dt == LA_BF16)
+    if (dt == LA_BF16 && D == 64 && C == 128)
+        e = lachunk::launch_bwd_c128(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, G, s, te.ev);
+    else if (dt == LA_BF16)
         e = D == 64 ? lachunk::launch_bwd<__bf16, 64>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in,
                                                      dz_in, G, C, s, te.ev)
                     : lachunk::launch_bwd<__bf16, 128>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in,
