@@ -95,7 +95,9 @@ la_status la_chunk_fwd(const void *q, const void *k, const void *v, const float 
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
-    if (dt == LA_BF16)
+    if (dt == LA_BF16 && D == 64 && C == 128)
+        e = lachunk::launch_fwd_c128(q, k, v, S_in, z_in, o, S_out, z_out, G, s, te.ev);
+    else if (dt == LA_BF16)
         e = D == 64 ? lachunk::launch_fwd<__bf16, 64>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s, te.ev)
                     : lachunk::launch_fwd<__bf16, 128>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s, te.ev);
     else

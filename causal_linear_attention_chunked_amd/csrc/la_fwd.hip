@@ -33,7 +33,9 @@ struct FwdLds {
     static constexpr int WIN = fwd_window<T, D>();
     static constexpr int PAD = Elem<T>::PAD;
     static constexpr int LDN = D + PAD;    // K rows [WIN*BK][LDN]
-    static constexpr int LDV = 64 + PAD;   // V slice rows [WIN*BK][LDV]
+    // V slice rows [WIN*BK][LDV]: read only through transposed fragment reads, which are free of
+    // bank conflicts at a 40-dword row pitch for bf16
+    static constexpr int LDV = is_bf16<T>() ? 64 + 16 : 64 + PAD;
     static constexpr int LDST = D + PAD;   // S^T copies [64 value columns][LDST]
     static constexpr int LDSF = 64 + 4;    // fp32 state, tail phase
     static constexpr int ESZ = (int)sizeof(T);
@@ -168,7 +170,10 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_kernel(
         Frag<T> qc[NKC];
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) qc[kc] = nxt.qf[kc];
-        load_window(nxt, wi + 1);  // past the end of the chunk: zeros, no memory traffic
+        // the next window, or the blocks after the last one when the ragged tail needs its keys and
+        // values from them (reads past the chunk give zeros); nothing when neither is wanted, so the
+        // barrier below does not wait on useless loads
+        if (wi + 1 < nwin || (tail && nb % WIN == 0)) load_window(nxt, wi + 1);
         __syncthreads();           // window staged; state copy 0 visible
 
         if constexpr (WIN == 2) {  // state after the window's first block: copy 1

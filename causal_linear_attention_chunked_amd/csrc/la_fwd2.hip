@@ -1,0 +1,211 @@
+// Forward kernel for 128-token bf16 chunks at D = 64: the blocked form of
+// "Fractus-1B training optimization" (section 2, Opt 2) over the chunk's two
+// 64-token blocks, computed side by side in one workgroup per group.
+//
+// Per block b with S_b, z_b the state before it (S_0 = S_in, S_1 = S_0 + K_0^T V_0):
+//   P^T   = K_b Q_b^T, masked to j <= t (inclusive)          scores, fp32
+//   den_t = sum_j P[t][j] + q_t . z_b                         (the read-after-update rule:
+//   num_t = sum_j P[t][j] v_j + S_b^T q_t                      the block's own tokens are in P)
+//   o_t   = num_t / den_t
+//   S_out = S_1 + K_1^T V_1,  z_out = z_1 + K_1^T 1
+//
+// Work split (8 waves, two per SIMD): wave w owns query tile tq of block w / 4 (the
+// second block's tiles in reverse, so the two waves of a SIMD carry one long and one
+// short causal row range) and state tiles (key-feature tiles pt0, pt0 + 2; value tile
+// ct).  Three phases separated by two barriers:
+//   A  stage K, V into LDS; write the bf16 copy of S_0^T and the split row of z_0
+//   B  S_1 (copy + split z_1), then S_out stored; scores, the fp32 row sums of P,
+//      and the intra-block numerator
+//   C  the inter-block terms against S_b, z_b; o = num / den stored.
+// The row sums of P come straight from the fp32 accumulators (lanes hold one query
+// each); P enters the numerator MFMA as a split hi + lo operand; the state copy is
+// a plain bf16 operand (its term has no cancellation against the others); z_b is a
+// split row so the denominator's inter-block term is exact to about 16 bits.
+#include "la_tile.h"
+#include "la_launch.h"
+#include <hip/hip_ext.h>
+
+namespace lachunk {
+
+namespace {
+struct Fwd2Lds {
+    static constexpr int KT = 0;                  // K tiles, blocks 0 and 1
+    static constexpr int VT = KT + 2 * TBYTES;    // V tiles
+    static constexpr int ST = VT + 2 * TBYTES;    // S_b^T copies (bf16), b = 0, 1
+    static constexpr int ZR = ST + 2 * TBYTES;    // [b][hi, lo][64] bf16 rows of z_b
+    static constexpr int BYTES = ZR + 4 * 128;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+}  // namespace
+
+__global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_in, const float *__restrict__ z_in,
+    bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out) {
+    using L = Fwd2Lds;
+    constexpr int D = 64, C = 128;
+    constexpr uint32_t CHUNK = C * D * 2;
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    char *const Kt = smem + L::KT, *const Vt = smem + L::VT, *const STt = smem + L::ST, *const zrow = smem + L::ZR;
+
+    const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int blk = w >> 2;
+    const int tq = blk ? 3 - (w & 3) : (w & 3);
+    const int ct = w & 3, pt0 = w >> 2;
+    const int grp = blockIdx.x;
+    const size_t tok0 = (size_t)grp * C;
+    const GRes qr(q + tok0 * D, CHUNK), kr(k + tok0 * D, CHUNK), vr(v + tok0 * D, CHUNK);
+    // an absent carry is an empty range (reads give zero); the base only has to be a valid address
+    const GRes sres(S_in ? (const void *)(S_in + (size_t)grp * D * D) : (const void *)S_out, S_in ? D * D * 4 : 0);
+    const GRes zres(z_in ? (const void *)(z_in + (size_t)grp * D) : (const void *)z_out, z_in ? D * 4 : 0);
+    const TileLanes TL(lane);
+    // this wave's state tiles: value tile ct, key-feature tiles pt[i] = pt0 + 2i, held as
+    // accumulators C[c][p] (lane: p = 16 pt[i] + r, c = 16 ct + 4g + e)
+    const int pt[2] = {pt0, pt0 + 2};
+    const uint32_t tr_c = TL.tr_at(ct), tr_p[2] = {TL.tr_at(pt0), TL.tr_at(pt0 + 2)}, nat_c = TL.nat_at(ct);
+
+    // ---- prologue: every load of the chunk issued before anything waits
+    bf16x8 kst[2], vst[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        kst[b] = gload<bf16x8>(kr, b * TBYTES + tid * 16);
+        vst[b] = gload<bf16x8>(vr, b * TBYTES + tid * 16);
+    }
+    bf16x8 qf[2];  // this wave's 16 queries: row t = r, k = key feature
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) qf[kc] = ldfrag_g<bf16>(qr, (64 * blk + 16 * tq) * D + 32 * kc, D, lane);
+    floatx4 Sacc[2], zr[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        Sacc[i] = gload<floatx4>(sres, ((16 * pt[i] + r) * D + 16 * ct + 4 * g) * 4);
+        const float zv = ct == 0 ? gload<float>(zres, (16 * pt[i] + r) * 4) : 0.f;
+        zr[i] = floatx4{zv, zv, zv, zv};
+    }
+    issue_fence();
+
+    // ---- phase A
+    const uint32_t so = stage_off(tid);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        *reinterpret_cast<bf16x8 *>(Kt + b * TBYTES + so) = kst[b];
+        *reinterpret_cast<bf16x8 *>(Vt + b * TBYTES + so) = vst[b];
+    }
+    // bf16 copy of S_b (row p, column c) and the split row of z_b, from the state accumulators
+    auto write_state = [&](int b) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            tstore_acc(STt + b * TBYTES, nat_c, pt[i], pack4(Sacc[i]));
+            if (ct == 0 && g == 0) {
+                bf16x2 hi, lo;
+                split_pair(zr[i][0], 0.f, hi, lo);
+                const int off = 2 * (16 * pt[i] + r);
+                *reinterpret_cast<bf16 *>(zrow + (2 * b) * 128 + off) = hi[0];
+                *reinterpret_cast<bf16 *>(zrow + (2 * b + 1) * 128 + off) = lo[0];
+            }
+        }
+    };
+    write_state(0);
+    __syncthreads();
+
+    // ---- phase B.  State: S += K_b^T V_b as C[c][p] = sum_j V[j][c] K[j][p]; z += K_b^T 1
+    const bf16x8 ones = ones_frag<bf16>();
+    auto advance = [&](int b) {
+        bf16x8 vt[2], kt[2][2];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            vt[kc] = tfrag_tr(Vt + b * TBYTES, tr_c, kc);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) kt[kc][i] = tfrag_tr(Kt + b * TBYTES, tr_p[i], kc);
+        }
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                mma(Sacc[i], vt[kc], kt[kc][i]);
+                if (ct == 0) mma(zr[i], ones, kt[kc][i]);
+            }
+    };
+    // intra-block part of this wave's outputs: operands first
+    const char *Kb = Kt + blk * TBYTES, *Vb = Vt + blk * TBYTES;
+    bf16x8 kf[4][2];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) kf[jt][kc] = jt <= tq ? tfrag(Kb, TL, jt, kc) : qf[kc];
+    advance(0);
+    write_state(1);
+    // scores P^T[j][t] (lane: query t = r, key j = 16 jt + 4g + i), masked to j <= t
+    floatx4 sc[4];
+    float dsum = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+        sc[jt] = zero4();
+        if (jt <= tq) {
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) mma(sc[jt], kf[jt][kc], qf[kc]);
+            if (jt == tq) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sc[jt][e] = 4 * g + e <= r ? sc[jt][e] : 0.f;
+            }
+            dsum += (sc[jt][0] + sc[jt][1]) + (sc[jt][2] + sc[jt][3]);
+        }
+    }
+    // num^T[c][t] = sum_j V^T[c][j] P[t][j]: P (accumulators as operand, split) against V^T
+    floatx4 nm[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) nm[c] = zero4();
+#pragma unroll
+    for (int jc = 0; jc < 2; ++jc) {
+        if (2 * jc <= tq) {
+            bf16x8 vf[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) vf[c] = tfrag_tr(Vb, TL.tr[c], jc);
+            const Split8 pf = split_acc(sc[2 * jc], sc[2 * jc + 1]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) mma_s(nm[c], vf[c], pf);
+        }
+    }
+    const float den_intra = gsum(dsum);
+    __syncthreads();  // the S_1 copy and z_1 row visible
+
+    // ---- phase C: inter-block terms against the state before this block, then o;
+    // S_out = S_1 + K_1^T V_1 alongside
+    const char *STb = STt + blk * TBYTES, *zb = zrow + 2 * blk * 128;
+    bf16x8 sf[2][4], zf[2][2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sf[kc][c] = tfrag_tr(STb, TL.tr[c], kc);
+        zf[kc][0] = rowfrag(zb, lane, kc);
+        zf[kc][1] = rowfrag(zb + 128, lane, kc);
+    }
+    floatx4 dn = zero4();
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mma(nm[c], sf[kc][c], qf[kc]);
+        mma(dn, zf[kc][0], qf[kc]);
+        mma(dn, zf[kc][1], qf[kc]);
+    }
+    const float inv = __builtin_amdgcn_rcpf(den_intra + dn[0]);
+    bf16 *orow = o + (tok0 + 64 * blk + 16 * tq + r) * D + 4 * g;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) __builtin_nontemporal_store(pack4(nm[c] * inv), reinterpret_cast<bf16x4 *>(orow + 16 * c));
+    advance(1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int p = 16 * pt[i] + r;
+        __builtin_nontemporal_store(Sacc[i], reinterpret_cast<floatx4 *>(S_out + ((size_t)grp * D + p) * D + 16 * ct + 4 * g));
+        if (ct == 0 && g == 0) __builtin_nontemporal_store(zr[i][0], z_out + (size_t)grp * D + p);
+    }
+}
+
+hipError_t launch_fwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
+                           void *o, float *S_out, float *z_out, int G, hipStream_t stream, const hipEvent_t ev[2]) {
+    hipExtLaunchKernelGGL(la_fwd_c128_kernel, dim3((unsigned)G), dim3(NTHR), 0, stream, ev[0], ev[1], 0,
+                          (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_in, z_in, (bf16 *)o, S_out, z_out);
+    return hipGetLastError();
+}
+
+}  // namespace lachunk

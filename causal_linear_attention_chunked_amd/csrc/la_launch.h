@@ -18,6 +18,8 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const float *
                       const hipEvent_t ev[2]);
 
 // bf16, D = 64, exactly two blocks (C = 128): both blocks of the chunk worked on side by side.
+hipError_t launch_fwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
+                           void *o, float *S_out, float *z_out, int G, hipStream_t stream, const hipEvent_t ev[2]);
 hipError_t launch_bwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
                            const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
                            float *dS_in, float *dz_in, int G, hipStream_t stream, const hipEvent_t ev[2]);
