@@ -1,0 +1,460 @@
+// Backward kernel for 128-token bf16 chunks at D = 64: the reverse scan of
+// "Fractus-1B training optimization" (section 1: the gradient of a prefix sum is a
+// suffix sum) over the blocked form of section 2, Opt 2, one workgroup of 16 waves
+// (four per SIMD) per group.
+//
+// Loss L = sum_t <dO_t, o_t> + <dS_out, S_out> + dz_out . z_out.  Block b has the
+// forward state S_b, z_b before it (S_0 = S_in, S_1 = S_0 + K_0^T V_0) and the reverse
+// state Sh_b, zh_b after it (Sh_1 = dS_out, Sh_0 = Sh_1 + Q_1^T dN_1).  Per query t of
+// block b, with A = Q K^T and G = dO V^T masked to j <= t and H_t = S_b dO_t:
+//   den_t = sum_j A_tj + q_t . z_b          inv_t = 1 / den_t
+//   rho_t = inv_t (sum_j A_tj G_tj + q_t . H_t)      (= dO_t . o_t)
+//   dden_t = -rho_t inv_t,   dN_t = inv_t dO_t,   dP_tj = inv_t (G_tj - rho_t)
+//   dq_t  = sum_j dP_tj k_j + inv_t H_t + dden_t z_b
+//   dk_j  = sum_{t>=j} dP_tj q_t + Sh_b v_j + zh_b
+//   dv_j  = sum_{t>=j} A_tj inv_t dO_t + Sh_b^T k_j
+//   dS_in = Sh_0 + Q_0^T dN_0,   dz_in = zh_0 + Q_0^T dden_0   (zh likewise with dden)
+// den and rho come from fp32 accumulators (A, G are exact products of the bf16 inputs),
+// so the scores never enter a second product in pass 1.  fp32 intermediates that are
+// MFMA operands (S_b, dP, A inv, dN, Sh) are split hi + lo.
+//
+// The kernel is bound by latency at this size (one workgroup per CU, a few thousand
+// dependent instructions), so the work is cut into 16 waves, four per SIMD:
+//   pass 1: two waves per query tile (8 tiles: block w%8 / 4; the second block's tiles
+//           reversed so each SIMD holds a long and a short causal range); half h = w / 8
+//           takes key tiles 2h, 2h+1 (A, G, dP) and key-feature tiles 2h, 2h+1 (H, dq);
+//           the two halves' row sums meet in LDS
+//   state : one 16 x 16 tile per wave (value tile w%4, key-feature tile w/4) for S_1, Sh_0
+//           and dS_in
+//   pass 2: one (block, key tile, output) task per wave: dv on waves 0-7, dk on 8-15
+// Phases, separated by LDS-only barriers:
+//   0  stage Q, K, V, dO; split copies of S_0 and Sh_1; z_0, zh_1
+//   1  S_1 (split copy, z_1); A and G of the wave's key tiles
+//   2  H of the wave's key-feature tiles; partial row sums
+//   3  den, rho; dP of the wave's key tiles (split, stored for dq and pass 2); inv, rho, dden
+//   4  dq; Sh_0 = Sh_1 + Q_1^T dN_1 (split copy), zh_0; pass 2 of block 1 and the
+//      intra-block part of pass 2 of block 0
+//   5  the inter-block part of pass 2 of block 0; dS_in = Sh_0 + Q_0^T dN_0
+#include "la_tile.h"
+#include "la_launch.h"
+#include <hip/hip_ext.h>
+#include <type_traits>
+
+namespace lachunk {
+
+namespace {
+constexpr int W16_THREADS = 1024;
+
+struct Bwd4Lds {
+    static constexpr int QT = 0;                 // Q[2], K[2], V[2], dO[2] tiles
+    static constexpr int KT = QT + 2 * TBYTES;
+    static constexpr int VT = KT + 2 * TBYTES;
+    static constexpr int GT = VT + 2 * TBYTES;
+    static constexpr int SS = GT + 2 * TBYTES;   // [b][hi, lo] split S_b; from phase 4: Sh_0 [hi, lo]
+    static constexpr int SH1 = SS + 4 * TBYTES;  // Sh_1 [hi, lo]
+    static constexpr int DP = SH1 + 2 * TBYTES;  // [b][hi, lo] split dP, stored [t][j]
+    static constexpr int ZF = DP + 4 * TBYTES;   // [b][64] z_b fp32
+    static constexpr int ZH = ZF + 2 * 64 * 4;   // [b][64] zh_b fp32
+    static constexpr int INV = ZH + 2 * 64 * 4;  // [128] inv_t
+    static constexpr int RHO = INV + 128 * 4;    // [128] rho_t
+    static constexpr int DDR = RHO + 128 * 4;    // [hi, lo][128] dden_t bf16
+    static constexpr int PS = DDR + 2 * 128 * 2; // [8 query tiles][2 halves][16 rows] (den, rho den) partials
+    static constexpr int BYTES = PS + 8 * 2 * 16 * 8;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+}  // namespace
+
+__global__ __launch_bounds__(W16_THREADS, 1) void la_bwd_c128w16_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_in, const float *__restrict__ z_in, const bf16 *__restrict__ dO,
+    const float *__restrict__ dS_out, const float *__restrict__ dz_out,
+    bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
+    float *__restrict__ dS_in, float *__restrict__ dz_in) {
+    using L = Bwd4Lds;
+    constexpr int D = 64, C = 128;
+    constexpr uint32_t CHUNK = C * D * 2;
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    float *const zf = reinterpret_cast<float *>(smem + L::ZF);
+    float *const zh = reinterpret_cast<float *>(smem + L::ZH);
+    float *const invs = reinterpret_cast<float *>(smem + L::INV);
+    float *const rhos = reinterpret_cast<float *>(smem + L::RHO);
+    bf16 *const ddr = reinterpret_cast<bf16 *>(smem + L::DDR);
+    floatx2 *const psum = reinterpret_cast<floatx2 *>(smem + L::PS);
+    auto tile = [&](int base, int b) -> char * { return smem + base + b * TBYTES; };
+
+    const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // pass 1: query tile u (block blk, tile tq) and half h
+    const int u = w & 7, h = w >> 3;
+    const int blk = u >> 2;
+    const int tq = blk ? 3 - (u & 3) : (u & 3);
+    // state tile: value tile ct, key-feature tile pt
+    const int ct = w & 3, pt = w >> 2;
+    const int grp = blockIdx.x;
+    const size_t tok0 = (size_t)grp * C;
+    const bool has_up = dS_out != nullptr;
+    const GRes qr(q + tok0 * D, CHUNK), kr(k + tok0 * D, CHUNK), vr(v + tok0 * D, CHUNK), gr(dO + tok0 * D, CHUNK);
+    const float *const dummy = dS_in;  // a valid base for an empty range
+    const GRes sres(S_in ? (const void *)(S_in + (size_t)grp * D * D) : dummy, S_in ? D * D * 4 : 0);
+    const GRes zres(z_in ? (const void *)(z_in + (size_t)grp * D) : dummy, z_in ? D * 4 : 0);
+    const GRes shres(has_up ? (const void *)(dS_out + (size_t)grp * D * D) : dummy, has_up ? D * D * 4 : 0);
+    const GRes zhres(dz_out ? (const void *)(dz_out + (size_t)grp * D) : dummy, dz_out ? D * 4 : 0);
+    const TileLanes TL(lane);
+    const uint32_t tr_c = TL.tr_at(ct), tr_p = TL.tr_at(pt), nat_c = TL.nat_at(ct);
+
+    // ---- prologue: every load issued before anything waits.  Thread tid stages 16 bytes of
+    // Q, K, V and dO of block tid / 512.
+    const int sb = tid >> 9;
+    const uint32_t gso = sb * TBYTES + (tid & 511) * 16;
+    bf16x8 st[4];
+    st[0] = gload<bf16x8>(qr, gso);
+    st[1] = gload<bf16x8>(kr, gso);
+    st[2] = gload<bf16x8>(vr, gso);
+    st[3] = gload<bf16x8>(gr, gso);
+    // state accumulators C[c][p] (lane: p = 16 pt + r, c = 16 ct + 4g + e): S and Sh
+    floatx4 Sacc, Sh, zr, zhr;
+    {
+        const uint32_t so = ((16 * pt + r) * D + 16 * ct + 4 * g) * 4;
+        Sacc = gload<floatx4>(sres, so);
+        Sh = gload<floatx4>(shres, so);
+        const float a = ct == 0 ? gload<float>(zres, (16 * pt + r) * 4) : 0.f;
+        const float b = ct == 0 ? gload<float>(zhres, (16 * pt + r) * 4) : 0.f;
+        zr = floatx4{a, a, a, a};
+        zhr = floatx4{b, b, b, b};
+    }
+    issue_fence();
+
+    // ---- phase 0
+    {
+        const uint32_t so = sb * TBYTES + stage_off(tid & 511);
+        *reinterpret_cast<bf16x8 *>(smem + L::QT + so) = st[0];
+        *reinterpret_cast<bf16x8 *>(smem + L::KT + so) = st[1];
+        *reinterpret_cast<bf16x8 *>(smem + L::VT + so) = st[2];
+        *reinterpret_cast<bf16x8 *>(smem + L::GT + so) = st[3];
+    }
+    // split copy of the wave's state tile (C[c][p] accumulator), stored [p][c] (hi, lo tiles)
+    auto write_split = [&](char *hi, char *lo, const floatx4 &acc) {
+        bf16x4 hh, ll;
+        split4(acc, hh, ll);
+        tstore_acc(hi, nat_c, pt, hh);
+        tstore_acc(lo, nat_c, pt, ll);
+    };
+    auto write_z = [&](float *dst, const floatx4 &zz) {
+        if (ct == 0 && g == 0) dst[16 * pt + r] = zz[0];
+    };
+    write_split(tile(L::SS, 0), tile(L::SS, 1), Sacc);
+    write_z(zf, zr);
+    if (has_up) write_split(tile(L::SH1, 0), tile(L::SH1, 1), Sh);
+    write_z(zh + 64, zhr);
+    lds_barrier();
+
+    // ---- phase 1.  S_1 = S_0 + K_0^T V_0 as C[c][p] = sum_j V[j][c] K[j][p]; z_1 = z_0 + K_0^T 1
+    const bf16x8 ones = ones_frag<bf16>();
+    {
+        bf16x8 vt[2], kt[2];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            vt[kc] = tfrag_tr(tile(L::VT, 0), tr_c, kc);
+            kt[kc] = tfrag_tr(tile(L::KT, 0), tr_p, kc);
+        }
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) mma(Sacc, vt[kc], kt[kc]);
+        if (ct == 0) {
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) mma(zr, ones, kt[kc]);
+        }
+    }
+    // pass-1 operands: this wave's queries (row t = r, k = feature) and its two key tiles
+    bf16x8 qf[2], df[2], kfr[2][2], vfr[2][2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+        qf[kc] = tfrag(tile(L::QT, blk), TL, tq, kc);
+        df[kc] = tfrag(tile(L::GT, blk), TL, tq, kc);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            kfr[jj][kc] = tfrag(tile(L::KT, blk), TL, 2 * h + jj, kc);
+            vfr[jj][kc] = tfrag(tile(L::VT, blk), TL, 2 * h + jj, kc);
+        }
+    }
+    // A^T, G^T (lane: query t = r, key j = 16 (2h + jj) + 4g + i), masked to j <= t
+    floatx4 aT[2], gT[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        aT[jj] = zero4();
+        gT[jj] = zero4();
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            mma(aT[jj], kfr[jj][kc], qf[kc]);
+            mma(gT[jj], vfr[jj][kc], df[kc]);
+        }
+        const int j4 = 2 * h + jj;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool keep = j4 < tq || (j4 == tq && 4 * g + e <= r);
+            aT[jj][e] = keep ? aT[jj][e] : 0.f;
+            gT[jj][e] = keep ? gT[jj][e] : 0.f;
+        }
+    }
+    write_split(tile(L::SS, 2), tile(L::SS, 3), Sacc);
+    write_z(zf + 64, zr);
+    lds_barrier();
+
+    // ---- phase 2.  H^T[p][t] = sum_c S_b[p][c] dO[t][c] for key-feature tiles 2h, 2h+1
+    // (lane: t = r, p = 16 (2h + pp) + 4g + i); partial row sums of this half
+    floatx4 hT[2], zv[2];
+    {
+        bf16x8 sh[2][2], sl[2][2];
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                sh[pp][kc] = tfrag(tile(L::SS, 2 * blk), TL, 2 * h + pp, kc);
+                sl[pp][kc] = tfrag(tile(L::SS, 2 * blk + 1), TL, 2 * h + pp, kc);
+            }
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            hT[pp] = zero4();
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                mma(hT[pp], sh[pp][kc], df[kc]);
+                mma(hT[pp], sl[pp][kc], df[kc]);
+            }
+        }
+    }
+    {
+        float dpart = 0.f, rpart = 0.f;
+        const bf16x8 qh = h ? qf[1] : qf[0];  // key features 32h..32h+31 of q_t
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            zv[pp] = *reinterpret_cast<const floatx4 *>(zf + 64 * blk + 16 * (2 * h + pp) + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // q_t[p] for p = 16 (2h + pp) + 4g + e: k-chunk h, slot 4 pp + e
+                const float qv = (float)qh[4 * pp + e];
+                dpart += qv * zv[pp][e];
+                rpart += qv * hT[pp][e];
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dpart += aT[jj][e];
+                rpart += aT[jj][e] * gT[jj][e];
+            }
+        const float dsum = gsum(dpart), rsum = gsum(rpart);
+        if (g == 0) psum[(u * 2 + h) * 16 + r] = floatx2{dsum, rsum};
+    }
+    lds_barrier();
+
+    // ---- phase 3.  Row statistics from both halves; dP for this wave's key tiles
+    float inv, dden;
+    {
+        const floatx2 mine = psum[(u * 2 + h) * 16 + r], other = psum[(u * 2 + 1 - h) * 16 + r];
+        const float den = mine[0] + other[0];
+        inv = __builtin_amdgcn_rcpf(den);
+        const float rho = (mine[1] + other[1]) * inv;
+        dden = -rho * inv;
+        // dP^T[j][t] = inv (G - rho), masked; split; stored [t][j] for dq and pass 2
+        floatx4 d[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j4 = 2 * h + jj;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool keep = j4 < tq || (j4 == tq && 4 * g + e <= r);
+                d[jj][e] = keep ? (gT[jj][e] - rho) * inv : 0.f;
+            }
+        }
+        const Split8 dps = split_acc(d[0], d[1]);
+        tstore_frag_at(tile(L::DP, 2 * blk), TL, tq, h, dps.hi);
+        tstore_frag_at(tile(L::DP, 2 * blk + 1), TL, tq, h, dps.lo);
+        if (h == 0 && g == 0) {
+            const int t = 64 * blk + 16 * tq + r;
+            invs[t] = inv;
+            rhos[t] = rho;
+            bf16x2 hh, ll;
+            split_pair(dden, 0.f, hh, ll);
+            ddr[t] = hh[0];
+            ddr[128 + t] = ll[0];
+        }
+    }
+    lds_barrier();
+
+    // ---- phase 4.  dq^T[p][t] = sum_j K^T[p][j] dP[t][j] + inv H^T[p][t] + dden z_b[p]
+    {
+        bf16x8 dph[2], dpl[2], ktr[2][2];
+#pragma unroll
+        for (int jc = 0; jc < 2; ++jc) {
+            dph[jc] = tfrag(tile(L::DP, 2 * blk), TL, tq, jc);
+            dpl[jc] = tfrag(tile(L::DP, 2 * blk + 1), TL, tq, jc);
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) ktr[pp][jc] = tfrag_tr(tile(L::KT, blk), TL.tr_at(2 * h + pp), jc);
+        }
+        bf16 *dqrow = dq + (tok0 + 64 * blk + 16 * tq + r) * D + 4 * g;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            floatx4 acc = hT[pp] * inv + dden * zv[pp];
+#pragma unroll
+            for (int jc = 0; jc < 2; ++jc) {
+                mma(acc, ktr[pp][jc], dph[jc]);
+                mma(acc, ktr[pp][jc], dpl[jc]);
+            }
+            __builtin_nontemporal_store(pack4(acc), reinterpret_cast<bf16x4 *>(dqrow + 16 * (2 * h + pp)));
+        }
+    }
+    // reverse state: Sh += Q_b^T dN_b as C[c][p] = sum_t dN[t][c] Q[t][p], zh += Q_b^T dden_b;
+    // dN^T (operand rows c, k = t) is dO^T scaled by inv_t
+    auto reverse = [&](int b) {
+        bf16x8 xg[2], qt[2];
+        floatx4 iv[2][2];
+#pragma unroll
+        for (int tc = 0; tc < 2; ++tc) {
+            xg[tc] = tfrag_tr(tile(L::GT, b), tr_c, tc);
+            qt[tc] = tfrag_tr(tile(L::QT, b), tr_p, tc);
+            iv[tc][0] = *reinterpret_cast<const floatx4 *>(invs + 64 * b + 32 * tc + 4 * g);
+            iv[tc][1] = *reinterpret_cast<const floatx4 *>(invs + 64 * b + 32 * tc + 16 + 4 * g);
+        }
+#pragma unroll
+        for (int tc = 0; tc < 2; ++tc) {
+            const bf16x8 x = xg[tc];
+            const floatx4 a0{(float)x[0] * iv[tc][0][0], (float)x[1] * iv[tc][0][1], (float)x[2] * iv[tc][0][2],
+                             (float)x[3] * iv[tc][0][3]};
+            const floatx4 a1{(float)x[4] * iv[tc][1][0], (float)x[5] * iv[tc][1][1], (float)x[6] * iv[tc][1][2],
+                             (float)x[7] * iv[tc][1][3]};
+            mma_s(Sh, split_acc(a0, a1), qt[tc]);
+        }
+        if (ct == 0) {
+#pragma unroll
+            for (int tc = 0; tc < 2; ++tc) {
+                mma(zhr, rowfrag(reinterpret_cast<const char *>(ddr + 64 * b), lane, tc), qt[tc]);
+                mma(zhr, rowfrag(reinterpret_cast<const char *>(ddr + 128 + 64 * b), lane, tc), qt[tc]);
+            }
+        }
+    };
+    reverse(1);
+    write_split(tile(L::SS, 0), tile(L::SS, 1), Sh);  // Sh_0 (the S_0 copy is no longer read)
+    write_z(zh, zhr);
+
+    // pass 2: wave w takes block (w / 4) % 2 and dv (w < 8, key tile w % 4) or dk (key tile
+    // 3 - w % 4: each SIMD holds a long and a short causal range of either output);
+    // accumulators dv^T[c][j] or dk^T[p][j] (lane: key j = r, column 16 x + 4g + i)
+    auto pass2 = [&](auto dk_tag, auto b_tag, bool inter_phase, floatx4 (&acc)[4], bf16x8 (&kv)[2]) {
+        constexpr bool DK = decltype(dk_tag)::value;
+        constexpr int B = decltype(b_tag)::value;
+        const int jt = DK ? 3 - (w & 3) : (w & 3);
+        auto inter = [&](const char *shh, const char *shl) {
+            bf16x8 sh[4][2], sl[4][2];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    sh[x][kc] = DK ? tfrag(shh, TL, x, kc) : tfrag_tr(shh, TL.tr[x], kc);
+                    sl[x][kc] = DK ? tfrag(shl, TL, x, kc) : tfrag_tr(shl, TL.tr[x], kc);
+                }
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    mma(acc[x], sh[x][kc], kv[kc]);
+                    mma(acc[x], sl[x][kc], kv[kc]);
+                }
+        };
+        auto store = [&]() {
+            bf16 *row = (DK ? dk : dv) + (tok0 + 64 * B + 16 * jt + r) * D + 4 * g;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                floatx4 y = acc[x];
+                if constexpr (DK) y += *reinterpret_cast<const floatx4 *>(zh + 64 * B + 16 * x + 4 * g);
+                __builtin_nontemporal_store(pack4(y), reinterpret_cast<bf16x4 *>(row + 16 * x));
+            }
+        };
+        if (inter_phase) {  // phase 5, block 0: against Sh_0
+            inter(tile(L::SS, 0), tile(L::SS, 1));
+            store();
+            return;
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) acc[x] = zero4();
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) kv[kc] = tfrag(tile(DK ? L::VT : L::KT, B), TL, jt, kc);
+        const uint32_t tr_jt = TL.tr_at(jt);
+#pragma unroll
+        for (int tc = 0; tc < 2; ++tc) {
+            if (2 * tc + 1 < jt) continue;  // every query of the slab precedes the key tile
+            bf16x8 xo[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) xo[x] = tfrag_tr(tile(DK ? L::QT : L::GT, B), TL.tr[x], tc);
+            Split8 y;
+            if constexpr (DK) {
+                // dP rows j, k = t, from the pass-1 copy
+                y = Split8{tfrag_tr(tile(L::DP, 2 * B), tr_jt, tc), tfrag_tr(tile(L::DP, 2 * B + 1), tr_jt, tc)};
+            } else {
+                // A[t][j] inv_t recomputed (lane: j = r, t = 32 tc + 16 hh + 4g + i), masked to t >= j
+                bf16x8 qa[2][2];
+                floatx4 iv[2], at[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    iv[hh] = *reinterpret_cast<const floatx4 *>(invs + 64 * B + 32 * tc + 16 * hh + 4 * g);
+#pragma unroll
+                    for (int kc = 0; kc < 2; ++kc) qa[hh][kc] = tfrag(tile(L::QT, B), TL, 2 * tc + hh, kc);
+                }
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int t4 = 2 * tc + hh;
+                    at[hh] = zero4();
+#pragma unroll
+                    for (int kc = 0; kc < 2; ++kc) mma(at[hh], qa[hh][kc], kv[kc]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        at[hh][e] = (t4 > jt || (t4 == jt && 4 * g + e >= r)) ? at[hh][e] * iv[hh][e] : 0.f;
+                }
+                y = split_acc(at[0], at[1]);
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x) mma_s(acc[x], xo[x], y);
+        }
+        if (B == 1) {  // block 1 completes here, against Sh_1 = dS_out
+            if (has_up) inter(tile(L::SH1, 0), tile(L::SH1, 1));
+            store();
+        }
+    };
+    using T1 = std::integral_constant<bool, true>;
+    using F1 = std::integral_constant<bool, false>;
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    const int p2b = (w >> 2) & 1, p2dk = w >> 3;
+    floatx4 acc[4];
+    bf16x8 kv[2];
+    if (p2dk) {
+        if (p2b) pass2(T1{}, B1{}, false, acc, kv);
+        else pass2(T1{}, B0{}, false, acc, kv);
+    } else {
+        if (p2b) pass2(F1{}, B1{}, false, acc, kv);
+        else pass2(F1{}, B0{}, false, acc, kv);
+    }
+    lds_barrier();  // Sh_0, zh_0 visible
+
+    // ---- phase 5
+    if (p2b == 0) {
+        if (p2dk) pass2(T1{}, B0{}, true, acc, kv);
+        else pass2(F1{}, B0{}, true, acc, kv);
+    }
+    reverse(0);
+    {
+        const int p = 16 * pt + r;
+        __builtin_nontemporal_store(Sh, reinterpret_cast<floatx4 *>(dS_in + ((size_t)grp * D + p) * D + 16 * ct + 4 * g));
+        if (ct == 0 && g == 0) __builtin_nontemporal_store(zhr[0], dz_in + (size_t)grp * D + p);
+    }
+}
+
+hipError_t launch_bwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
+                           const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
+                           float *dS_in, float *dz_in, int G, hipStream_t stream, const hipEvent_t ev[2]) {
+    hipExtLaunchKernelGGL(la_bwd_c128w16_kernel, dim3((unsigned)G), dim3(W16_THREADS), 0, stream, ev[0], ev[1], 0,
+                          (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_in, z_in, (const bf16 *)dO, dS_out,
+                          dz_out, (bf16 *)dq, (bf16 *)dk, (bf16 *)dv, dS_in, dz_in);
+    return hipGetLastError();
+}
+
+}  // namespace lachunk

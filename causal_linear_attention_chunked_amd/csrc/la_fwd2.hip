@@ -106,7 +106,7 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_kernel(
         }
     };
     write_state(0);
-    __syncthreads();
+    lds_barrier();
 
     // ---- phase B.  State: S += K_b^T V_b as C[c][p] = sum_j V[j][c] K[j][p]; z += K_b^T 1
     const bf16x8 ones = ones_frag<bf16>();
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_kernel(
         }
     }
     const float den_intra = gsum(dsum);
-    __syncthreads();  // the S_1 copy and z_1 row visible
+    lds_barrier();  // the S_1 copy and z_1 row visible
 
     // ---- phase C: inter-block terms against the state before this block, then o;
     // S_out = S_1 + K_1^T V_1 alongside

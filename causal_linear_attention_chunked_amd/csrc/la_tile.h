@@ -19,6 +19,7 @@
 namespace lachunk {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 constexpr int TROW = 128;            // bytes per tile row
 constexpr int TBYTES = 64 * TROW;    // bytes per tile
@@ -55,7 +56,10 @@ struct TileLanes {
     __device__ __forceinline__ uint32_t tr_at(int u) const { return trow + 8 * ((4 * u) ^ lt); }
 };
 
-__device__ __forceinline__ bf16x4 lds_b64(const char *p) { return *reinterpret_cast<const bf16x4 *>(p); }
+// Volatile, so that the two 8-byte halves of different fragments are never merged into one
+// ds_read2 (which would land them in the wrong registers and cost a v_mov per dword).
+typedef __attribute__((address_space(3))) const volatile bf16x4 lds_vbf16x4;
+__device__ __forceinline__ bf16x4 lds_b64(const char *p) { return *(lds_vbf16x4 *)(p); }
 
 // Operand fragment of tile rows 16*rt..+15 (row, k contiguous), k-chunk kc.
 __device__ __forceinline__ bf16x8 tfrag(const char *tile, const TileLanes &L, int rt, int kc) {
@@ -89,10 +93,26 @@ __device__ __forceinline__ void tstore_frag(char *tile, const TileLanes &L, int 
     *reinterpret_cast<bf16x4 *>(b + L.nat[2 * kc]) = __builtin_shufflevector(f, f, 0, 1, 2, 3);
     *reinterpret_cast<bf16x4 *>(b + L.nat[2 * kc + 1]) = __builtin_shufflevector(f, f, 4, 5, 6, 7);
 }
+// The same for a k-chunk known only at run time.
+__device__ __forceinline__ void tstore_frag_at(char *tile, const TileLanes &L, int rt, int kc, const bf16x8 &f) {
+    char *b = tile + rt * 16 * TROW;
+    *reinterpret_cast<bf16x4 *>(b + L.nat_at(2 * kc)) = __builtin_shufflevector(f, f, 0, 1, 2, 3);
+    *reinterpret_cast<bf16x4 *>(b + L.nat_at(2 * kc + 1)) = __builtin_shufflevector(f, f, 4, 5, 6, 7);
+}
 // Byte offset of a thread's 16-byte staging slot (8 threads per 128-byte row).
 __device__ __forceinline__ uint32_t stage_off(int tid) {
     const int row = tid >> 3, c = tid & 7;
     return row * TROW + 8 * ((2 * c) ^ swz(row));
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() fences every address space, so
+// each wave would first wait for its own outstanding global loads and stores; here the
+// waves exchange data through LDS alone, and outputs stored to global memory before a
+// barrier keep draining across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // bf16x4 of four fp32 values (round to nearest even)
