@@ -15,6 +15,10 @@ synchronisation:
 Prints one JSON line.
 
     python bench.py --copy-calibration   # one plain device copy of known size, for counter scaling
+    python bench.py --counters-summary DIR
+        # HBM bytes per launch of each kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+        # (DIR/fetch_bench, DIR/write_bench over this benchmark; DIR/fetch_copy, DIR/write_copy
+        # over --copy-calibration), written to profiles/ for the `traffic` field
 """
 from __future__ import annotations
 
@@ -31,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "tokens·groups/s for linear-attn fwd+bwd at G=160,C=128,D=64; % roofline"
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_la_bwd_g160_c128_d64_bf16.json")
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
 def algorithmic_bytes(G, C, D, esz, carry, upstream):
@@ -46,23 +50,72 @@ def algorithmic_bytes(G, C, D, esz, carry, upstream):
 
 
 def kernel_source_hash():
+    """Hash of every kernel source: counter-measured traffic is only reported for the build it was taken on."""
+    import glob
     h = hashlib.sha256()
-    for f in ("la_bwd.hip", "la_fwd.hip", "la_common.h"):
-        with open(os.path.join(ROOT, "causal_linear_attention_chunked_amd", "csrc", f), "rb") as fh:
+    for f in sorted(glob.glob(os.path.join(ROOT, "causal_linear_attention_chunked_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """Counter-measured HBM bytes per backward launch, if taken on the current kernel source."""
+def traffic_file(workload):
+    return os.path.join(TRAFFIC_DIR, f"traffic_{workload}.json")
+
+
+def measured_traffic(workload, kernel):
+    """Counter-measured HBM bytes per launch of `kernel`, if taken on the current kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return t.get("bytes_per_launch")
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def counter_rows(d, counter):
+    """(kernel name, value) for every dispatch in a rocprofv3 counter-collection output directory."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {d}")
+    return rows
+
+
+def counters_summary(d, workload, kernels):
+    """Per-launch HBM bytes of each kernel: FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by
+    what the same counters read for plain 256 MiB device copies (bench.py --copy-calibration)."""
+    cal = 256 * 1024  # KiB moved each way by one calibration copy
+    fc = max(v for _, v in counter_rows(os.path.join(d, "fetch_copy"), "FETCH_SIZE"))
+    wc = max(v for _, v in counter_rows(os.path.join(d, "write_copy"), "WRITE_SIZE"))
+    scale_f, scale_w = cal / fc, cal / wc
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+           "calibration": {"copy_KiB": cal, "fetch_KiB_read": fc, "write_KiB_read": wc,
+                           "fetch_scale": scale_f, "write_scale": scale_w},
+           "kernels": {}}
+    fetch = counter_rows(os.path.join(d, "fetch_bench"), "FETCH_SIZE")
+    write = counter_rows(os.path.join(d, "write_bench"), "WRITE_SIZE")
+    for k in kernels:
+        fv = [v for n, v in fetch if k in n]
+        wv = [v for n, v in write if k in n]
+        if not fv or not wv:
+            continue
+        fb = sum(fv) / len(fv) * scale_f * 1024
+        wb = sum(wv) / len(wv) * scale_w * 1024
+        out["kernels"][k] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb,
+                             "dispatches": [len(fv), len(wv)]}
+    with open(traffic_file(workload), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(I, w, min_seconds=10.0):
@@ -109,6 +162,8 @@ def main():
     ap.add_argument("--footprint-mb", type=float, default=640.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only plain 256 MiB device-to-device copies (HBM counter calibration)")
+    ap.add_argument("--counters-summary", metavar="DIR",
+                    help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE passes under DIR into per-launch HBM bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -116,6 +171,14 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.counters_summary:
+        import causal_linear_attention_chunked_amd as lac
+        from causal_linear_attention_chunked_amd import inputs as inp
+        w = inp.workload(args.workload)
+        dt = "bf16" if w.dtype == "bf16" else "float32"
+        counters_summary(args.counters_summary, w.name,
+                         [lac.kernel_name(False, dt, w.T, w.D), lac.kernel_name(True, dt, w.T, w.D)])
+        return
     import torch
     if args.copy_calibration:
         copy_calibration(torch)
@@ -183,7 +246,9 @@ def main():
 
     bwd_gbs = bwd_bytes / (bwd_ms / 1e3) / 1e9
     fwd_gbs = fwd_bytes / (fwd_ms / 1e3) / 1e9
-    traffic = measured_traffic()
+    fwd_name = lac.kernel_name(False, w.dtype, C, D)
+    bwd_name = lac.kernel_name(True, w.dtype, C, D)
+    traffic = measured_traffic(w.name, bwd_name)
     out = {
         "metric": METRIC, "value": value, "unit": "tokens·groups/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
@@ -192,13 +257,14 @@ def main():
                    "buffer_sets": nsets, "footprint_mb": round(nsets * set_bytes / 1e6, 1),
                    "graph_captured": False,
                    "kernel_timing": "HIP events recorded on each kernel dispatch, separate timed loop"},
-        "roofline": {"bound": "hbm", "kernel": "la_bwd_kernel", "achieved": bwd_gbs, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": bwd_name, "achieved": bwd_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": bwd_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": bwd_bytes, "avg_us": bwd_ms * 1e3},
-        "kernels": {"la_fwd_kernel": {"avg_us": fwd_ms * 1e3, "algorithmic_bytes": fwd_bytes,
-                                      "GB/s": fwd_gbs, "frac": fwd_gbs / HBM_PEAK_GBS},
-                    "la_bwd_kernel": {"avg_us": bwd_ms * 1e3, "algorithmic_bytes": bwd_bytes,
-                                      "GB/s": bwd_gbs, "frac": bwd_gbs / HBM_PEAK_GBS}},
+        "kernels": {fwd_name: {"avg_us": fwd_ms * 1e3, "algorithmic_bytes": fwd_bytes,
+                               "GB/s": fwd_gbs, "frac": fwd_gbs / HBM_PEAK_GBS,
+                               "traffic": measured_traffic(w.name, fwd_name)},
+                    bwd_name: {"avg_us": bwd_ms * 1e3, "algorithmic_bytes": bwd_bytes,
+                               "GB/s": bwd_gbs, "frac": bwd_gbs / HBM_PEAK_GBS, "traffic": traffic}},
         "step_roofline_frac": (fwd_bytes + bwd_bytes) / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
     }
     if not args.no_cpu_baseline:

@@ -21,7 +21,7 @@ import os
 import threading
 
 __all__ = ["fwd", "bwd", "chain_fwd", "chain_bwd", "LachunkError", "lib_path", "load_library",
-           "abi_version", "status_str", "time_next_launch", "BWD_MAX_C"]
+           "abi_version", "status_str", "time_next_launch", "kernel_name", "BWD_MAX_C"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liblachunk.so")
@@ -65,6 +65,8 @@ def load_library():
         lib.la_abi_version.argtypes = []
         lib.la_time_next_launch.restype = i
         lib.la_time_next_launch.argtypes = [vp, vp]
+        lib.la_kernel_name.restype = ctypes.c_char_p
+        lib.la_kernel_name.argtypes = [i, i, i, i]
         _lib = lib
         return lib
 
@@ -75,6 +77,14 @@ def abi_version() -> int:
 
 def status_str(s: int) -> str:
     return load_library().la_status_str(int(s)).decode()
+
+
+def kernel_name(backward: bool, dtype, C: int, D: int):
+    """Name of the kernel a fwd (backward=False) or bwd call launches for this element type
+    ("bf16"/"float32" or a torch dtype), chunk length and head dimension; None if unsupported."""
+    dt = LA_BF16 if str(dtype).replace("torch.", "") in ("bf16", "bfloat16") else LA_F32
+    name = load_library().la_kernel_name(int(bool(backward)), dt, int(C), int(D))
+    return None if name is None else name.decode()
 
 
 def time_next_launch(start_event, stop_event):

@@ -157,6 +157,14 @@ const char *la_status_str(la_status s) {
 
 int la_abi_version(void) { return LA_ABI_VERSION; }
 
+const char *la_kernel_name(int backward, la_dtype dt, int C, int D) {
+    if ((dt != LA_F32 && dt != LA_BF16) || (D != 64 && D != 128) || C < 1) return nullptr;
+    const bool c128 = dt == LA_BF16 && D == 64 && C == 128;  // the dispatch rule of the entry points
+    if (!backward) return c128 ? "la_fwd_c128_kernel" : "la_fwd_kernel";
+    if (C > LA_BWD_MAX_C || (dt == LA_F32 && D == 128)) return nullptr;
+    return c128 ? "la_bwd_c128w16_kernel" : "la_bwd_kernel";
+}
+
 la_status la_time_next_launch(void *start_event, void *stop_event) {
     if ((start_event == nullptr) != (stop_event == nullptr)) return LA_ERR_INVALID;
     pending_ev[0] = reinterpret_cast<hipEvent_t>(start_event);

@@ -300,7 +300,7 @@ __global__ __launch_bounds__(W16_THREADS, 1) void la_bwd_c128w16_kernel(
                 mma(acc, ktr[pp][jc], dph[jc]);
                 mma(acc, ktr[pp][jc], dpl[jc]);
             }
-            __builtin_nontemporal_store(pack4(acc), reinterpret_cast<bf16x4 *>(dqrow + 16 * (2 * h + pp)));
+            store_bf16x4(dqrow + 16 * (2 * h + pp), pack4(acc));
         }
     }
     // reverse state: Sh += Q_b^T dN_b as C[c][p] = sum_t dN[t][c] Q[t][p], zh += Q_b^T dden_b;
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(W16_THREADS, 1) void la_bwd_c128w16_kernel(
             for (int x = 0; x < 4; ++x) {
                 floatx4 y = acc[x];
                 if constexpr (DK) y += *reinterpret_cast<const floatx4 *>(zh + 64 * B + 16 * x + 4 * g);
-                __builtin_nontemporal_store(pack4(y), reinterpret_cast<bf16x4 *>(row + 16 * x));
+                store_bf16x4(row + 16 * x, pack4(y));
             }
         };
         if (inter_phase) {  // phase 5, block 0: against Sh_0

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_kernel(
     const float inv = __builtin_amdgcn_rcpf(den_intra + dn[0]);
     bf16 *orow = o + (tok0 + 64 * blk + 16 * tq + r) * D + 4 * g;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) __builtin_nontemporal_store(pack4(nm[c] * inv), reinterpret_cast<bf16x4 *>(orow + 16 * c));
+    for (int c = 0; c < 4; ++c) store_bf16x4(orow + 16 * c, pack4(nm[c] * inv));
     advance(1);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {

@@ -115,6 +115,18 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Store of four bf16 outputs (8 bytes per lane; the four lanes of an accumulator row write
+// 32 contiguous bytes per instruction).  Non-temporal by default: on the headline shapes
+// they are faster than write-back stores, at the price of partial-sector writes (more HBM
+// write bytes than the tensor size); LA_BF16_NT_STORES=0 selects write-back stores.
+#ifndef LA_BF16_NT_STORES
+#define LA_BF16_NT_STORES 1
+#endif
+__device__ __forceinline__ void store_bf16x4(bf16 *p, const bf16x4 &x) {
+    if (LA_BF16_NT_STORES) __builtin_nontemporal_store(x, reinterpret_cast<bf16x4 *>(p));
+    else *reinterpret_cast<bf16x4 *>(p) = x;
+}
+
 // bf16x4 of four fp32 values (round to nearest even)
 __device__ __forceinline__ bf16x4 pack4(const floatx4 &x) {
     const bf16x2 a{(bf16)x[0], (bf16)x[1]}, b{(bf16)x[2], (bf16)x[3]};

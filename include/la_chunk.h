@@ -123,6 +123,15 @@ int la_abi_version(void);
  */
 la_status la_time_next_launch(void *start_event, void *stop_event);
 
+/*
+ * Measurement aid: the name of the kernel that la_chunk_fwd (backward = 0) or
+ * la_chunk_bwd (backward = 1) launches for element type dt, chunk length C and
+ * head dimension D, as it appears (demangled, template arguments aside) in
+ * profiler output.  A static string; NULL when the configuration is not
+ * supported.  Does not touch the device.
+ */
+const char *la_kernel_name(int backward, la_dtype dt, int C, int D);
+
 #ifdef __cplusplus
 }
 #endif

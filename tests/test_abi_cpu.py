@@ -32,8 +32,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["la_abi_version", "la_chunk_bwd", "la_chunk_fwd", "la_status_str",
-                                    "la_time_next_launch"]
+    assert declared_functions() == ["la_abi_version", "la_chunk_bwd", "la_chunk_fwd", "la_kernel_name",
+                                    "la_status_str", "la_time_next_launch"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -42,6 +42,15 @@ def test_library_exports_every_declared_symbol(lib):
     out = os.popen(f"nm -D --defined-only {lac.lib_path()}").read()
     for name in declared_functions():
         assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_kernel_names(lib):
+    assert lac.kernel_name(False, "bf16", 128, 64) == "la_fwd_c128_kernel"
+    assert lac.kernel_name(True, "bf16", 128, 64) == "la_bwd_c128w16_kernel"
+    assert lac.kernel_name(False, "bf16", 100, 128) == "la_fwd_kernel"
+    assert lac.kernel_name(True, "float32", 128, 64) == "la_bwd_kernel"
+    assert lac.kernel_name(True, "float32", 128, 128) is None
+    assert lac.kernel_name(False, "bf16", 128, 96) is None
 
 
 def test_version_and_status_strings(lib):
