@@ -12,11 +12,13 @@
 // Work split (8 waves, two per SIMD): wave w owns query tile tq of block w / 4 (the
 // second block's tiles in reverse, so the two waves of a SIMD carry one long and one
 // short causal row range) and state tiles (key-feature tiles pt0, pt0 + 2; value tile
-// ct).  Three phases separated by two barriers:
-//   A  stage K, V into LDS; write the bf16 copy of S_0^T and the split row of z_0
-//   B  S_1 (copy + split z_1), then S_out stored; scores, the fp32 row sums of P,
-//      and the intra-block numerator
-//   C  the inter-block terms against S_b, z_b; o = num / den stored.
+// ct).  Block 0 and the state are loaded first and block 1's keys and values last, so
+// that block 0's outputs are computed while the rest arrives.  Three phases separated by
+// two barriers:
+//   A  stage block 0's K, V; write the bf16 copy of S_0 and the split row of z_0
+//   B  S_1 (copy + split z_1); block 0's outputs (scores, fp32 row sums, intra-block and
+//      inter-block numerator, o stored); stage block 1's K, V
+//   C  block 1's outputs against S_1; S_out = S_1 + K_1^T V_1 stored.
 // The row sums of P come straight from the fp32 accumulators (lanes hold one query
 // each); P enters the numerator MFMA as a split hi + lo operand; the state copy is
 // a plain bf16 operand (its term has no cancellation against the others); z_b is a
@@ -24,6 +26,7 @@
 #include "la_tile.h"
 #include "la_launch.h"
 #include <hip/hip_ext.h>
+#include <type_traits>
 
 namespace lachunk {
 
@@ -65,13 +68,9 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_kernel(
     const int pt[2] = {pt0, pt0 + 2};
     const uint32_t tr_c = TL.tr_at(ct), tr_p[2] = {TL.tr_at(pt0), TL.tr_at(pt0 + 2)}, nat_c = TL.nat_at(ct);
 
-    // ---- prologue: every load of the chunk issued before anything waits
-    bf16x8 kst[2], vst[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        kst[b] = gload<bf16x8>(kr, b * TBYTES + tid * 16);
-        vst[b] = gload<bf16x8>(vr, b * TBYTES + tid * 16);
-    }
+    // ---- prologue: every load issued before anything waits, block 0 and the state first, so
+    // that block 0's work can start while block 1's keys and values are still arriving
+    bf16x8 kst0 = gload<bf16x8>(kr, tid * 16), vst0 = gload<bf16x8>(vr, tid * 16);
     bf16x8 qf[2];  // this wave's 16 queries: row t = r, k = key feature
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) qf[kc] = ldfrag_g<bf16>(qr, (64 * blk + 16 * tq) * D + 32 * kc, D, lane);
@@ -82,15 +81,10 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_kernel(
         const float zv = ct == 0 ? gload<float>(zres, (16 * pt[i] + r) * 4) : 0.f;
         zr[i] = floatx4{zv, zv, zv, zv};
     }
+    bf16x8 kst1 = gload<bf16x8>(kr, TBYTES + tid * 16), vst1 = gload<bf16x8>(vr, TBYTES + tid * 16);
     issue_fence();
 
-    // ---- phase A
     const uint32_t so = stage_off(tid);
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        *reinterpret_cast<bf16x8 *>(Kt + b * TBYTES + so) = kst[b];
-        *reinterpret_cast<bf16x8 *>(Vt + b * TBYTES + so) = vst[b];
-    }
     // bf16 copy of S_b (row p, column c) and the split row of z_b, from the state accumulators
     auto write_state = [&](int b) {
 #pragma unroll
@@ -105,10 +99,7 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_kernel(
             }
         }
     };
-    write_state(0);
-    lds_barrier();
-
-    // ---- phase B.  State: S += K_b^T V_b as C[c][p] = sum_j V[j][c] K[j][p]; z += K_b^T 1
+    // State: S += K_b^T V_b as C[c][p] = sum_j V[j][c] K[j][p]; z += K_b^T 1
     const bf16x8 ones = ones_frag<bf16>();
     auto advance = [&](int b) {
         bf16x8 vt[2], kt[2][2];
@@ -126,72 +117,88 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_kernel(
                 if (ct == 0) mma(zr[i], ones, kt[kc][i]);
             }
     };
-    // intra-block part of this wave's outputs: operands first
-    const char *Kb = Kt + blk * TBYTES, *Vb = Vt + blk * TBYTES;
-    bf16x8 kf[4][2];
+    // this wave's outputs for block B (its own block): scores P^T[j][t] (lane: query t = r,
+    // key j = 16 jt + 4g + i) masked to j <= t; their fp32 row sums; num^T[c][t] =
+    // sum_j V^T[c][j] P[t][j] (P split) + sum_p S_B^T[c][p] q_t[p]; den = row sums + z_B . q_t
+    auto outputs = [&](auto b_tag) {
+        constexpr int B = decltype(b_tag)::value;
+        const char *Kb = Kt + B * TBYTES, *Vb = Vt + B * TBYTES, *STb = STt + B * TBYTES, *zb = zrow + 2 * B * 128;
+        bf16x8 kf[4][2];
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
+        for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) kf[jt][kc] = jt <= tq ? tfrag(Kb, TL, jt, kc) : qf[kc];
+            for (int kc = 0; kc < 2; ++kc) kf[jt][kc] = jt <= tq ? tfrag(Kb, TL, jt, kc) : qf[kc];
+        floatx4 sc[4];
+        float dsum = 0.f;
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            sc[jt] = zero4();
+            if (jt <= tq) {
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) mma(sc[jt], kf[jt][kc], qf[kc]);
+                if (jt == tq) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sc[jt][e] = 4 * g + e <= r ? sc[jt][e] : 0.f;
+                }
+                dsum += (sc[jt][0] + sc[jt][1]) + (sc[jt][2] + sc[jt][3]);
+            }
+        }
+        floatx4 nm[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) nm[c] = zero4();
+#pragma unroll
+        for (int jc = 0; jc < 2; ++jc) {
+            if (2 * jc <= tq) {
+                bf16x8 vf[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) vf[c] = tfrag_tr(Vb, TL.tr[c], jc);
+                const Split8 pf = split_acc(sc[2 * jc], sc[2 * jc + 1]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) mma_s(nm[c], vf[c], pf);
+            }
+        }
+        // inter-block terms against the state before this block (read before it is updated)
+        bf16x8 sf[2][4], zf[2][2];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) sf[kc][c] = tfrag_tr(STb, TL.tr[c], kc);
+            zf[kc][0] = rowfrag(zb, lane, kc);
+            zf[kc][1] = rowfrag(zb + 128, lane, kc);
+        }
+        floatx4 dn = zero4();
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) mma(nm[c], sf[kc][c], qf[kc]);
+            mma(dn, zf[kc][0], qf[kc]);
+            mma(dn, zf[kc][1], qf[kc]);
+        }
+        const float inv = __builtin_amdgcn_rcpf(gsum(dsum) + dn[0]);
+        bf16 *orow = o + (tok0 + 64 * B + 16 * tq + r) * D + 4 * g;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) store_bf16x4(orow + 16 * c, pack4(nm[c] * inv));
+    };
+    using Blk0 = std::integral_constant<int, 0>;
+    using Blk1 = std::integral_constant<int, 1>;
+
+    // ---- phase A: block 0's keys and values, the S_0 copy and z_0 row
+    *reinterpret_cast<bf16x8 *>(Kt + so) = kst0;
+    *reinterpret_cast<bf16x8 *>(Vt + so) = vst0;
+    write_state(0);
+    lds_barrier();
+
+    // ---- phase B: S_1 (copy, z_1 row); block 0's outputs (their state S_0 is ready); then
+    // block 1's keys and values, by now arrived
     advance(0);
     write_state(1);
-    // scores P^T[j][t] (lane: query t = r, key j = 16 jt + 4g + i), masked to j <= t
-    floatx4 sc[4];
-    float dsum = 0.f;
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-        sc[jt] = zero4();
-        if (jt <= tq) {
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) mma(sc[jt], kf[jt][kc], qf[kc]);
-            if (jt == tq) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sc[jt][e] = 4 * g + e <= r ? sc[jt][e] : 0.f;
-            }
-            dsum += (sc[jt][0] + sc[jt][1]) + (sc[jt][2] + sc[jt][3]);
-        }
-    }
-    // num^T[c][t] = sum_j V^T[c][j] P[t][j]: P (accumulators as operand, split) against V^T
-    floatx4 nm[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) nm[c] = zero4();
-#pragma unroll
-    for (int jc = 0; jc < 2; ++jc) {
-        if (2 * jc <= tq) {
-            bf16x8 vf[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) vf[c] = tfrag_tr(Vb, TL.tr[c], jc);
-            const Split8 pf = split_acc(sc[2 * jc], sc[2 * jc + 1]);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) mma_s(nm[c], vf[c], pf);
-        }
-    }
-    const float den_intra = gsum(dsum);
-    lds_barrier();  // the S_1 copy and z_1 row visible
+    if (blk == 0) outputs(Blk0{});
+    *reinterpret_cast<bf16x8 *>(Kt + TBYTES + so) = kst1;
+    *reinterpret_cast<bf16x8 *>(Vt + TBYTES + so) = vst1;
+    lds_barrier();
 
-    // ---- phase C: inter-block terms against the state before this block, then o;
-    // S_out = S_1 + K_1^T V_1 alongside
-    const char *STb = STt + blk * TBYTES, *zb = zrow + 2 * blk * 128;
-    bf16x8 sf[2][4], zf[2][2];
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) sf[kc][c] = tfrag_tr(STb, TL.tr[c], kc);
-        zf[kc][0] = rowfrag(zb, lane, kc);
-        zf[kc][1] = rowfrag(zb + 128, lane, kc);
-    }
-    floatx4 dn = zero4();
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) mma(nm[c], sf[kc][c], qf[kc]);
-        mma(dn, zf[kc][0], qf[kc]);
-        mma(dn, zf[kc][1], qf[kc]);
-    }
-    const float inv = __builtin_amdgcn_rcpf(den_intra + dn[0]);
-    bf16 *orow = o + (tok0 + 64 * blk + 16 * tq + r) * D + 4 * g;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) store_bf16x4(orow + 16 * c, pack4(nm[c] * inv));
+    // ---- phase C: block 1's outputs; S_out = S_1 + K_1^T V_1
+    if (blk == 1) outputs(Blk1{});
     advance(1);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
