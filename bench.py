@@ -2,8 +2,11 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-One step is one forward and one backward launch (the whole path) over one
-batch of seeded synthetic inputs already resident in device memory.  Steps
+One step is the whole path over one batch of seeded synthetic inputs already
+resident in device memory: the forward over each chunk of the sequence in order,
+carrying (S, z), then the backward over the chunks in reverse, carrying (dS, dz).
+The default workload (G=160 groups, one 128-token chunk, D=64, bf16) is one
+forward and one backward launch; `--workload` names the chained ones.  Steps
 rotate over enough buffer sets (>= 640 MB) that the 256 MB last-level cache
 cannot serve the traffic.  Two timed regions, each bracketed by device
 synchronisation:
@@ -34,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "tokens·groups/s for linear-attn fwd+bwd at G=160,C=128,D=64; % roofline"
+HEADLINE = "g160_c128_d64_bf16_fwdbwd"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
@@ -47,6 +51,20 @@ def algorithmic_bytes(G, C, D, esz, carry, upstream):
     fwd = 3 * tok + tok + (carry_b if carry else 0) + carry_b            # q,k,v,[S_in,z_in] -> o,S_out,z_out
     bwd = 4 * tok + 3 * tok + (carry_b if carry else 0) + (carry_b if upstream else 0) + carry_b
     return fwd, bwd
+
+
+def plan_launches(G, chunks, D, esz, carry):
+    """One step's launches as (kind, chunk length, algorithmic bytes, chunk index): the forward
+    over chunks 0..n-1 carrying (S, z), then the backward over chunks n-1..0 carrying (dS, dz).
+    A chunk after the first always has a carry in; every backward but the last chunk's has an
+    upstream (dS_out, dz_out)."""
+    n = len(chunks)
+    out = []
+    for i, C in enumerate(chunks):
+        out.append(("fwd", C, algorithmic_bytes(G, C, D, esz, carry or i > 0, False)[0], i))
+    for i in range(n - 1, -1, -1):
+        out.append(("bwd", chunks[i], algorithmic_bytes(G, chunks[i], D, esz, carry or i > 0, i < n - 1)[1], i))
+    return out
 
 
 def kernel_source_hash():
@@ -118,24 +136,30 @@ def counters_summary(d, workload, kernels):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(I, w, min_seconds=10.0):
-    """The fp64 oracle as it stands, on this host's cores, over the same workload, repeated."""
+def cpu_baseline(I, w, min_seconds=10.0, mac_budget=2e9):
+    """The fp64 oracle as it stands, on this host's cores, over the workload's first groups
+    (all of them when the workload is small), repeated; one call covers all the chunks."""
     import oracle
-    threads = os.cpu_count() or 1
-    args = [I[n] for n in ("q", "k", "v", "S_in", "z_in")]
+    per_group = w.T * w.D * w.D
+    g = w.G if w.G * per_group <= mac_budget else max(1, int(mac_budget // per_group))
+    threads = min(os.cpu_count() or 1, g)
+    sl = lambda x: None if x is None else x[:g]
+    args = [sl(I[n]) for n in ("q", "k", "v", "S_in", "z_in")]
+    dO = sl(I["dO"])
     times = []
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
         oracle.fwd(*args, nthreads=threads)
-        oracle.bwd(*args, I["dO"], nthreads=threads)
+        oracle.bwd(*args, dO, nthreads=threads)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start >= min_seconds and len(times) >= 3:
             break
     times.sort()
     med = times[len(times) // 2]
-    return {"value": w.G * w.T / med, "unit": "tokens·groups/s", "cores": threads, "kind": "oracle",
-            "sample": f"full {w.name} workload (G={w.G}, {w.T} tokens, D={w.D}), forward+backward in fp64, "
+    what = f"full {w.name} workload" if g == w.G else f"first {g} of the {w.G} groups of {w.name}"
+    return {"value": g * w.T / med, "unit": "tokens·groups/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what} (G={g}, {w.T} tokens, D={w.D}), forward+backward in fp64, "
                       f"median of {len(times)} repeats ({sum(times):.1f} s of CPU work)"}
 
 
@@ -157,7 +181,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="g160_c128_d64_bf16_fwdbwd")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--footprint-mb", type=float, default=640.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -175,9 +199,8 @@ def main():
         import causal_linear_attention_chunked_amd as lac
         from causal_linear_attention_chunked_amd import inputs as inp
         w = inp.workload(args.workload)
-        dt = "bf16" if w.dtype == "bf16" else "float32"
-        counters_summary(args.counters_summary, w.name,
-                         [lac.kernel_name(False, dt, w.T, w.D), lac.kernel_name(True, dt, w.T, w.D)])
+        names = {lac.kernel_name(b, w.dtype, C, w.D) for b in (False, True) for C in set(w.chunks)}
+        counters_summary(args.counters_summary, w.name, sorted(names))
         return
     import torch
     if args.copy_calibration:
@@ -188,32 +211,55 @@ def main():
 
     lac.load_library()
     w = inp.workload(args.workload)
-    if len(w.chunks) != 1 or not w.backward:
-        raise SystemExit("bench.py times single-chunk forward+backward workloads")
-    G, C, D = w.G, w.T, w.D
+    if not w.backward:
+        raise SystemExit("bench.py times forward+backward workloads")
     I = inp.workload_inputs(w)
     dev = torch.device("cuda:0")
     esz = 2 if w.dtype == "bf16" else 4
+    G, D = w.G, w.D
+    bounds = inp.chunk_bounds(w.chunks)
+    n = len(bounds)
     carry = I["S_in"] is not None
-    fwd_bytes, bwd_bytes = algorithmic_bytes(G, C, D, esz, carry, False)
-    set_bytes = fwd_bytes + bwd_bytes
-    nsets = max(2, math.ceil(args.footprint_mb * 1e6 / set_bytes))
 
-    def dev_copy(x):
-        return None if x is None else x.to(dev).contiguous()
+    launches = plan_launches(G, w.chunks, D, esz, carry)
+    set_bytes = sum(b for _, _, b, _ in launches)
+    nsets = max(1, math.ceil(args.footprint_mb * 1e6 / set_bytes))
 
-    sets = []
-    for _ in range(nsets):
-        s = {n: dev_copy(I[n]) for n in ("q", "k", "v", "S_in", "z_in", "dO")}
-        s["fout"] = (torch.empty_like(s["q"]), torch.empty((G, D, D), device=dev),
-                     torch.empty((G, D), device=dev))
-        s["bout"] = (torch.empty_like(s["q"]), torch.empty_like(s["q"]), torch.empty_like(s["q"]),
-                     torch.empty((G, D, D), device=dev), torch.empty((G, D), device=dev))
-        sets.append(s)
+    def new_set():
+        s = {"chunks": []}
+        for t0, t1 in bounds:
+            c = {x: I[x][:, t0:t1].to(dev).contiguous() for x in ("q", "k", "v", "dO")}
+            C = t1 - t0
+            c["fout"] = (torch.empty_like(c["q"]), torch.empty((G, D, D), device=dev),
+                         torch.empty((G, D), device=dev))
+            c["bout"] = (torch.empty_like(c["q"]), torch.empty_like(c["q"]), torch.empty_like(c["q"]),
+                         torch.empty((G, D, D), device=dev), torch.empty((G, D), device=dev))
+            s["chunks"].append(c)
+        s["S_in"] = None if I["S_in"] is None else I["S_in"].to(dev).contiguous()
+        s["z_in"] = None if I["z_in"] is None else I["z_in"].to(dev).contiguous()
+        return s
+
+    sets = [new_set() for _ in range(nsets)]
+
+    def carry_in(s, i):
+        if i == 0:
+            return s["S_in"], s["z_in"]
+        prev = s["chunks"][i - 1]["fout"]
+        return prev[1], prev[2]
+
+    def launch(s, kind, i):
+        c = s["chunks"][i]
+        S, z = carry_in(s, i)
+        if kind == "fwd":
+            lac.fwd(c["q"], c["k"], c["v"], S, z, out=c["fout"])
+        else:
+            up = s["chunks"][i + 1]["bout"] if i + 1 < n else None
+            lac.bwd(c["q"], c["k"], c["v"], S, z, c["dO"], None if up is None else up[3],
+                    None if up is None else up[4], out=c["bout"])
 
     def step(s):
-        lac.fwd(s["q"], s["k"], s["v"], s["S_in"], s["z_in"], out=s["fout"])
-        lac.bwd(s["q"], s["k"], s["v"], s["S_in"], s["z_in"], s["dO"], out=s["bout"])
+        for kind, _, _, i in launches:
+            launch(s, kind, i)
 
     for i in range(args.warmup):
         step(sets[i % nsets])
@@ -224,54 +270,63 @@ def main():
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
+    h0 = time.perf_counter()
     for i in range(K):
         step(sets[i % nsets])
+    host_s = time.perf_counter() - h0
     end.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / K
-    value = G * C / (ms_per_step / 1e3)
+    value = G * w.T / (ms_per_step / 1e3)
 
     # region 2: the same steps with dispatch-bound events on every launch
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in launches]
+          for _ in range(K)]
     torch.cuda.synchronize()
     for i in range(K):
         s = sets[i % nsets]
-        lac.time_next_launch(ev[i][0], ev[i][1])
-        lac.fwd(s["q"], s["k"], s["v"], s["S_in"], s["z_in"], out=s["fout"])
-        lac.time_next_launch(ev[i][2], ev[i][3])
-        lac.bwd(s["q"], s["k"], s["v"], s["S_in"], s["z_in"], s["dO"], out=s["bout"])
+        for (kind, _, _, c), e in zip(launches, ev[i]):
+            lac.time_next_launch(e[0], e[1])
+            launch(s, kind, c)
     torch.cuda.synchronize()
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    bwd_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
 
-    bwd_gbs = bwd_bytes / (bwd_ms / 1e3) / 1e9
-    fwd_gbs = fwd_bytes / (fwd_ms / 1e3) / 1e9
-    fwd_name = lac.kernel_name(False, w.dtype, C, D)
-    bwd_name = lac.kernel_name(True, w.dtype, C, D)
-    traffic = measured_traffic(w.name, bwd_name)
+    # per kernel: launches, total bytes and total time over the K steps
+    per = {}
+    for i in range(K):
+        for (kind, C, b, _), e in zip(launches, ev[i]):
+            name = lac.kernel_name(kind == "bwd", w.dtype, C, D)
+            p = per.setdefault(name, {"launches": 0, "bytes": 0, "ms": 0.0})
+            p["launches"] += 1
+            p["bytes"] += b
+            p["ms"] += e[0].elapsed_time(e[1])
+    kernels = {}
+    for name, p in per.items():
+        gbs = p["bytes"] / (p["ms"] / 1e3) / 1e9
+        kernels[name] = {"avg_us": p["ms"] * 1e3 / p["launches"], "launches_per_step": p["launches"] // K,
+                         "algorithmic_bytes": p["bytes"] / p["launches"], "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic(w.name, name)}
+    # the roofline names the kernel with the most time per step
+    top = max(per, key=lambda k: per[k]["ms"])
+    kt = kernels[top]
     out = {
-        "metric": METRIC, "value": value, "unit": "tokens·groups/s", "n_gpus": 1, "steps": K,
+        "metric": METRIC if w.name == HEADLINE else f"tokens·groups/s for linear-attn fwd+bwd, {w.name}",
+        "value": value, "unit": "tokens·groups/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "G": G, "C": C, "D": D, "block": w.block, "carry": w.carry,
+        "config": {"workload": w.name, "G": G, "T": w.T, "chunks": n, "C": max(w.chunks), "D": D,
+                   "block": w.block, "carry": w.carry, "launches_per_step": len(launches),
                    "buffer_sets": nsets, "footprint_mb": round(nsets * set_bytes / 1e6, 1),
-                   "graph_captured": False,
+                   "graph_captured": False, "host_enqueue_us_per_step": host_s * 1e6 / K,
                    "kernel_timing": "HIP events recorded on each kernel dispatch, separate timed loop"},
-        "roofline": {"bound": "hbm", "kernel": bwd_name, "achieved": bwd_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": bwd_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes": bwd_bytes, "avg_us": bwd_ms * 1e3},
-        "kernels": {fwd_name: {"avg_us": fwd_ms * 1e3, "algorithmic_bytes": fwd_bytes,
-                               "GB/s": fwd_gbs, "frac": fwd_gbs / HBM_PEAK_GBS,
-                               "traffic": measured_traffic(w.name, fwd_name)},
-                    bwd_name: {"avg_us": bwd_ms * 1e3, "algorithmic_bytes": bwd_bytes,
-                               "GB/s": bwd_gbs, "frac": bwd_gbs / HBM_PEAK_GBS, "traffic": traffic}},
-        "step_roofline_frac": (fwd_bytes + bwd_bytes) / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": top, "achieved": kt["GB/s"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": kt["frac"], "traffic": kt["traffic"],
+                     "algorithmic_bytes": kt["algorithmic_bytes"], "avg_us": kt["avg_us"]},
+        "kernels": kernels,
+        "step_roofline_frac": set_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
     }
     if not args.no_cpu_baseline:
-        Ic = {n: I[n] for n in ("q", "k", "v", "S_in", "z_in", "dO")}
-        out["cpu_baseline"] = cpu_baseline(Ic, w)
+        out["cpu_baseline"] = cpu_baseline(I, w)
     print(json.dumps(out), flush=True)
-
 
 if __name__ == "__main__":
     main()

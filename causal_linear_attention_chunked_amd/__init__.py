@@ -100,7 +100,8 @@ def time_next_launch(start_event, stop_event):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # ctypes passes a Python int or None for a c_void_p argument
+    return None if t is None else t.data_ptr()
 
 
 def _check(fn, status):
@@ -118,7 +119,16 @@ def _dtype_code(t):
 
 
 def _validate_tokens(names, tensors):
+    """(G, C, D, device index) of the token tensors, which must agree in shape, dtype and device
+    and be contiguous CUDA tensors.  The common case costs a few attribute reads per tensor."""
     ref = tensors[0]
+    shape, dtype, dev = ref.shape, ref.dtype, ref.get_device()
+    if len(shape) == 3 and dev >= 0:
+        for t in tensors:
+            if t.get_device() != dev or t.dtype is not dtype or t.shape != shape or not t.is_contiguous():
+                break
+        else:
+            return shape[0], shape[1], shape[2], dev
     if ref.dim() != 3:
         raise ValueError(f"{names[0]} must be (G, C, D), got {tuple(ref.shape)}")
     for n, t in zip(names, tensors):
@@ -129,64 +139,65 @@ def _validate_tokens(names, tensors):
                              f"{names[0]} {tuple(ref.shape)}/{ref.dtype}/{ref.device}")
         if not t.is_contiguous():
             raise ValueError(f"{n} must be contiguous")
+    raise AssertionError("unreachable")
 
 
-def _validate_state(name, t, shape, device):
+def _validate_state(name, t, shape, dev):
     import torch
     if t is None:
         return
-    if t.dtype != torch.float32 or tuple(t.shape) != shape or t.device != device or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shape} on {device}")
+    if t.dtype is not torch.float32 or t.shape != shape or t.get_device() != dev or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shape} on cuda:{dev}")
 
 
-def _stream(device):
+def _stream(dev):
+    """Raw handle of the current stream on device index ``dev``."""
     import torch
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    return torch._C._cuda_getCurrentRawStream(dev)
 
 
 def fwd(q, k, v, S_in=None, z_in=None, block: int = 64, out=None):
     """Forward over one chunk: returns (o, S_out, z_out).  ``out`` may supply them."""
-    import torch
-    lib = load_library()
-    _validate_tokens(("q", "k", "v"), (q, k, v))
-    G, C, D = q.shape
+    lib = _lib or load_library()
+    G, C, D, dev = _validate_tokens(("q", "k", "v"), (q, k, v))
     if (S_in is None) != (z_in is None):
         raise ValueError("S_in and z_in must be given together")
-    _validate_state("S_in", S_in, (G, D, D), q.device)
-    _validate_state("z_in", z_in, (G, D), q.device)
+    _validate_state("S_in", S_in, (G, D, D), dev)
+    _validate_state("z_in", z_in, (G, D), dev)
     if out is None:
+        import torch
         o = torch.empty_like(q)
         S_out = torch.empty((G, D, D), dtype=torch.float32, device=q.device)
         z_out = torch.empty((G, D), dtype=torch.float32, device=q.device)
     else:
         o, S_out, z_out = out
-    _check("la_chunk_fwd", lib.la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(S_in), _ptr(z_in),
-                                            _ptr(o), _ptr(S_out), _ptr(z_out), G, C, D, int(block),
-                                            _dtype_code(q), _stream(q.device)))
+    _check("la_chunk_fwd", lib.la_chunk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(S_in), _ptr(z_in),
+                                            o.data_ptr(), S_out.data_ptr(), z_out.data_ptr(), G, C, D, int(block),
+                                            _dtype_code(q), _stream(dev)))
     return o, S_out, z_out
 
 
 def bwd(q, k, v, S_in, z_in, dO, dS_out=None, dz_out=None, block: int = 64, out=None):
     """Backward over one chunk: returns (dq, dk, dv, dS_in, dz_in)."""
-    import torch
-    lib = load_library()
-    _validate_tokens(("q", "k", "v", "dO"), (q, k, v, dO))
-    G, C, D = q.shape
+    lib = _lib or load_library()
+    G, C, D, dev = _validate_tokens(("q", "k", "v", "dO"), (q, k, v, dO))
     if (S_in is None) != (z_in is None) or (dS_out is None) != (dz_out is None):
         raise ValueError("S_in/z_in and dS_out/dz_out must each be given together")
-    for n, t, shp in (("S_in", S_in, (G, D, D)), ("z_in", z_in, (G, D)),
-                      ("dS_out", dS_out, (G, D, D)), ("dz_out", dz_out, (G, D))):
-        _validate_state(n, t, shp, q.device)
+    _validate_state("S_in", S_in, (G, D, D), dev)
+    _validate_state("z_in", z_in, (G, D), dev)
+    _validate_state("dS_out", dS_out, (G, D, D), dev)
+    _validate_state("dz_out", dz_out, (G, D), dev)
     if out is None:
+        import torch
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
         dS_in = torch.empty((G, D, D), dtype=torch.float32, device=q.device)
         dz_in = torch.empty((G, D), dtype=torch.float32, device=q.device)
     else:
         dq, dk, dv, dS_in, dz_in = out
-    _check("la_chunk_bwd", lib.la_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(S_in), _ptr(z_in), _ptr(dO),
-                                            _ptr(dS_out), _ptr(dz_out), _ptr(dq), _ptr(dk), _ptr(dv),
-                                            _ptr(dS_in), _ptr(dz_in), G, C, D, int(block),
-                                            _dtype_code(q), _stream(q.device)))
+    _check("la_chunk_bwd", lib.la_chunk_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(S_in), _ptr(z_in),
+                                            dO.data_ptr(), _ptr(dS_out), _ptr(dz_out), dq.data_ptr(),
+                                            dk.data_ptr(), dv.data_ptr(), dS_in.data_ptr(), dz_in.data_ptr(),
+                                            G, C, D, int(block), _dtype_code(q), _stream(dev)))
     return dq, dk, dv, dS_in, dz_in
 
 
