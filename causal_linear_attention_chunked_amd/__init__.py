@@ -9,6 +9,7 @@ raises.  PyTorch supplies device memory and the current stream.
     o, S_out, z_out = fwd(q, k, v, S_in=None, z_in=None)
     dq, dk, dv, dS_in, dz_in = bwd(q, k, v, S_in, z_in, dO, dS_out=None, dz_out=None)
     time_next_launch(start_event, stop_event)   # kernel-only timing of the next call
+    o, (S_out, z_out) = linear_attention(q, k, v, S_in, z_in, chunk=128)   # differentiable (autograd)
 
 q, k, v, dO: contiguous (G, C, D) CUDA tensors, float32 or bfloat16 (one dtype
 for all); S: (G, D, D) float32 with S[p][c] (p key feature, c value feature);
@@ -20,7 +21,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["fwd", "bwd", "chain_fwd", "chain_bwd", "LachunkError", "lib_path", "load_library",
+__all__ = ["fwd", "bwd", "chain_fwd", "chain_bwd", "linear_attention", "chunk_attention", "ChunkFunction", "LachunkError", "lib_path", "load_library",
            "abi_version", "status_str", "time_next_launch", "kernel_name", "BWD_MAX_C"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -227,3 +228,11 @@ def chain_bwd(q_chunks, k_chunks, v_chunks, carries, dO_chunks, dS_out=None, dz_
         dqs[i], dks[i], dvs[i], gS, gz = bwd(q_chunks[i], k_chunks[i], v_chunks[i], S, z, dO_chunks[i],
                                              gS, gz, block)
     return dqs, dks, dvs, gS, gz
+
+
+def __getattr__(name):
+    # the autograd layer imports torch; load it on first use
+    if name in ("linear_attention", "chunk_attention", "ChunkFunction"):
+        from . import autograd
+        return getattr(autograd, name)
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")

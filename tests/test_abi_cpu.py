@@ -140,3 +140,11 @@ def test_python_binding_rejects_cpu_tensors(lib):
     q = torch.ones(2, 8, 64)
     with pytest.raises(ValueError):
         lac.fwd(q, q, q)
+
+
+def test_autograd_rejects_host_tensors():
+    import torch
+    import causal_linear_attention_chunked_amd as lac
+    x = torch.ones(1, 4, 64)
+    with pytest.raises(ValueError, match="CUDA"):
+        lac.linear_attention(x, x, x)

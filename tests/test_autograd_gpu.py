@@ -1,0 +1,61 @@
+"""GPU: the autograd layer (torch.autograd.Function over the HIP library) against the fp64 oracle.
+
+A scalar loss L = sum(o * dO) + <S_out, dS_out> + z_out . dz_out is back-propagated through a
+chunked sequence (ragged last chunk); the gradients of q, k, v, S_in, z_in must match the
+oracle's reverse scan for the same (dO, dS_out, dz_out), to the tolerance of tests/tol.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import causal_linear_attention_chunked_amd as lac
+from causal_linear_attention_chunked_amd import inputs as inp
+import oracle
+from tol import RTOL, check
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(dtype, carry, upstream, G=3, T=300, D=64, chunk=128, seed=11):
+    I = inp.make_inputs(G=G, T=T, D=D, dtype=dtype, carry=carry, backward=True, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    dS = torch.from_numpy(rng.standard_normal((G, D, D)).astype(np.float32)) if upstream else None
+    dz = torch.from_numpy(rng.standard_normal((G, D)).astype(np.float32)) if upstream else None
+    print(f"[case] autograd dtype={dtype} carry={carry} upstream={upstream} G={G} T={T} D={D} chunk={chunk}",
+          flush=True)
+    dev = "cuda:0"
+    leaf = lambda x: None if x is None else x.to(dev).clone().requires_grad_(True)
+    q, k, v = leaf(I["q"]), leaf(I["k"]), leaf(I["v"])
+    S_in, z_in = leaf(I["S_in"]), leaf(I["z_in"])
+    o, (S_out, z_out) = lac.linear_attention(q, k, v, S_in, z_in, chunk=chunk)
+    loss = (o.float() * I["dO"].to(dev).float()).sum()
+    if upstream:
+        loss = loss + (S_out * dS.to(dev)).sum() + (z_out * dz.to(dev)).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    ro, rS, rz = oracle.fwd(I["q"], I["k"], I["v"], I["S_in"], I["z_in"])
+    ref = oracle.bwd(I["q"], I["k"], I["v"], I["S_in"], I["z_in"], I["dO"], dS, dz)
+    tol = RTOL[dtype]
+    check("o", o, ro, tol)
+    check("S_out", S_out, rS, tol)
+    check("z_out", z_out, rz, tol)
+    for name, g, r in zip(("dq", "dk", "dv"), (q.grad, k.grad, v.grad), ref[:3]):
+        check(name, g, r, tol)
+    if carry == "zero":
+        assert S_in is None
+    else:
+        check("dS_in", S_in.grad, ref[3], tol)
+        check("dz_in", z_in.grad, ref[4], tol)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_autograd_prior_carry_upstream(gpu, dtype):
+    _case(dtype, "prior", True)
+
+
+def test_autograd_zero_carry_no_upstream(gpu):
+    _case("bf16", "zero", False, G=2, T=128)
+
+
+def test_autograd_wide_heads(gpu):
+    _case("bf16", "prior", True, G=2, T=200, D=128, chunk=100)
