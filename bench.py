@@ -53,6 +53,17 @@ def algorithmic_bytes(G, C, D, esz, carry, upstream):
     return fwd, bwd
 
 
+def plan_seq_launches(G, T, D, esz, carry, upstream=False):
+    """The two launches of a step through the sequence entry points: one forward over all the
+    chunks (carry in only if given, carry out) and one backward (the final carry in, the
+    upstream gradient if given, the carry gradient out); no carry between chunks moves."""
+    tok = G * T * D * esz
+    carry_b = G * (D * D + D) * 4
+    fwd = 4 * tok + (carry_b if carry else 0) + carry_b
+    bwd = 7 * tok + carry_b + (carry_b if upstream else 0) + carry_b
+    return [("seqfwd", T, fwd, 0), ("seqbwd", T, bwd, 0)]
+
+
 def plan_launches(G, chunks, D, esz, carry):
     """One step's launches as (kind, chunk length, algorithmic bytes, chunk index): the forward
     over chunks 0..n-1 carrying (S, z), then the backward over chunks n-1..0 carrying (dS, dz).
@@ -183,6 +194,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seq", action="store_true",
+                    help="run the workload through the sequence entry points (one launch per direction)")
     ap.add_argument("--footprint-mb", type=float, default=640.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only plain 256 MiB device-to-device copies (HBM counter calibration)")
@@ -200,7 +213,8 @@ def main():
         from causal_linear_attention_chunked_amd import inputs as inp
         w = inp.workload(args.workload)
         names = {lac.kernel_name(b, w.dtype, C, w.D) for b in (False, True) for C in set(w.chunks)}
-        counters_summary(args.counters_summary, w.name, sorted(names))
+        names |= {lac.seq_kernel_name(b, w.dtype, max(w.chunks), w.D) for b in (False, True)} - {None}
+        counters_summary(args.counters_summary, w.name + ("_seq" if args.seq else ""), sorted(names))
         return
     import torch
     if args.copy_calibration:
@@ -221,12 +235,28 @@ def main():
     n = len(bounds)
     carry = I["S_in"] is not None
 
-    launches = plan_launches(G, w.chunks, D, esz, carry)
+    tname = w.name + ("_seq" if args.seq else "")  # names the traffic record too
+    if args.seq:
+        if not lac.seq_supported(w.dtype, w.T, D, max(w.chunks)) or len(set(w.chunks)) != 1:
+            raise SystemExit(f"{w.name}: the sequence entry points do not take this workload")
+        launches = plan_seq_launches(G, w.T, D, esz, carry)
+    else:
+        launches = plan_launches(G, w.chunks, D, esz, carry)
     set_bytes = sum(b for _, _, b, _ in launches)
     nsets = max(1, math.ceil(args.footprint_mb * 1e6 / set_bytes))
 
     def new_set():
         s = {"chunks": []}
+        if args.seq:
+            s["seq"] = {x: I[x].to(dev).contiguous() for x in ("q", "k", "v", "dO")}
+            q = s["seq"]["q"]
+            s["seq"]["fout"] = (torch.empty_like(q), torch.empty((G, D, D), device=dev),
+                                torch.empty((G, D), device=dev))
+            s["seq"]["bout"] = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q),
+                                torch.empty((G, D, D), device=dev), torch.empty((G, D), device=dev))
+            s["S_in"] = None if I["S_in"] is None else I["S_in"].to(dev).contiguous()
+            s["z_in"] = None if I["z_in"] is None else I["z_in"].to(dev).contiguous()
+            return s
         for t0, t1 in bounds:
             c = {x: I[x][:, t0:t1].to(dev).contiguous() for x in ("q", "k", "v", "dO")}
             C = t1 - t0
@@ -248,6 +278,14 @@ def main():
         return prev[1], prev[2]
 
     def launch(s, kind, i):
+        if kind == "seqfwd":
+            x = s["seq"]
+            lac.seq_fwd(x["q"], x["k"], x["v"], s["S_in"], s["z_in"], out=x["fout"])
+            return
+        if kind == "seqbwd":
+            x = s["seq"]
+            lac.seq_bwd(x["q"], x["k"], x["v"], x["fout"][1], x["fout"][2], x["dO"], out=x["bout"])
+            return
         c = s["chunks"][i]
         S, z = carry_in(s, i)
         if kind == "fwd":
@@ -294,7 +332,8 @@ def main():
     per = {}
     for i in range(K):
         for (kind, C, b, _), e in zip(launches, ev[i]):
-            name = lac.kernel_name(kind == "bwd", w.dtype, C, D)
+            name = (lac.seq_kernel_name(kind == "seqbwd", w.dtype, max(w.chunks), D) if kind.startswith("seq")
+                    else lac.kernel_name(kind == "bwd", w.dtype, C, D))
             p = per.setdefault(name, {"launches": 0, "bytes": 0, "ms": 0.0})
             p["launches"] += 1
             p["bytes"] += b
@@ -304,18 +343,20 @@ def main():
         gbs = p["bytes"] / (p["ms"] / 1e3) / 1e9
         kernels[name] = {"avg_us": p["ms"] * 1e3 / p["launches"], "launches_per_step": p["launches"] // K,
                          "algorithmic_bytes": p["bytes"] / p["launches"], "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": measured_traffic(w.name, name)}
+                         "traffic": measured_traffic(tname, name)}
     # the roofline names the kernel with the most time per step
     top = max(per, key=lambda k: per[k]["ms"])
     kt = kernels[top]
     out = {
-        "metric": METRIC if w.name == HEADLINE else f"tokens·groups/s for linear-attn fwd+bwd, {w.name}",
+        "metric": (METRIC if w.name == HEADLINE and not args.seq
+                   else f"tokens·groups/s for linear-attn fwd+bwd, {tname}"),
         "value": value, "unit": "tokens·groups/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "G": G, "T": w.T, "chunks": n, "C": max(w.chunks), "D": D,
                    "block": w.block, "carry": w.carry, "launches_per_step": len(launches),
                    "buffer_sets": nsets, "footprint_mb": round(nsets * set_bytes / 1e6, 1),
+                   "entry_points": "la_seq_fwd/la_seq_bwd" if args.seq else "la_chunk_fwd/la_chunk_bwd",
                    "graph_captured": False, "host_enqueue_us_per_step": host_s * 1e6 / K,
                    "kernel_timing": "HIP events recorded on each kernel dispatch, separate timed loop"},
         "roofline": {"bound": "hbm", "kernel": top, "achieved": kt["GB/s"], "peak": HBM_PEAK_GBS,

@@ -8,11 +8,13 @@ raises.  PyTorch supplies device memory and the current stream.
 
     o, S_out, z_out = fwd(q, k, v, S_in=None, z_in=None)
     dq, dk, dv, dS_in, dz_in = bwd(q, k, v, S_in, z_in, dO, dS_out=None, dz_out=None)
+    o, S_out, z_out = seq_fwd(q, k, v, S_in, z_in, chunk=128)     # (G, T, D): all chunks, one launch
+    dq, dk, dv, dS_in, dz_in = seq_bwd(q, k, v, S_out, z_out, dO)   # from the final carry
     time_next_launch(start_event, stop_event)   # kernel-only timing of the next call
     o, (S_out, z_out) = linear_attention(q, k, v, S_in, z_in, chunk=128)   # differentiable (autograd)
 
-q, k, v, dO: contiguous (G, C, D) CUDA tensors, float32 or bfloat16 (one dtype
-for all); S: (G, D, D) float32 with S[p][c] (p key feature, c value feature);
+q, k, v, dO: contiguous (G, C, D) (one chunk) or (G, T, D) (a sequence) CUDA
+tensors, float32 or bfloat16 (one dtype for all); S: (G, D, D) float32 with S[p][c] (p key feature, c value feature);
 z: (G, D) float32.  See the header for the operation and its rules.
 """
 from __future__ import annotations
@@ -21,7 +23,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["fwd", "bwd", "chain_fwd", "chain_bwd", "linear_attention", "chunk_attention", "ChunkFunction", "LachunkError", "lib_path", "load_library",
+__all__ = ["fwd", "bwd", "seq_fwd", "seq_bwd", "seq_supported", "seq_kernel_name", "chain_fwd", "chain_bwd", "linear_attention", "chunk_attention", "ChunkFunction", "LachunkError", "lib_path", "load_library",
            "abi_version", "status_str", "time_next_launch", "kernel_name", "BWD_MAX_C"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +70,12 @@ def load_library():
         lib.la_time_next_launch.argtypes = [vp, vp]
         lib.la_kernel_name.restype = ctypes.c_char_p
         lib.la_kernel_name.argtypes = [i, i, i, i]
+        lib.la_seq_fwd.restype = i
+        lib.la_seq_fwd.argtypes = [vp] * 8 + [i] * 6 + [vp]
+        lib.la_seq_bwd.restype = i
+        lib.la_seq_bwd.argtypes = [vp] * 13 + [i] * 6 + [vp]
+        lib.la_seq_kernel_name.restype = ctypes.c_char_p
+        lib.la_seq_kernel_name.argtypes = [i, i, i, i]
         _lib = lib
         return lib
 
@@ -80,12 +88,28 @@ def status_str(s: int) -> str:
     return load_library().la_status_str(int(s)).decode()
 
 
+def _dt_code(dtype):
+    return LA_BF16 if str(dtype).replace("torch.", "") in ("bf16", "bfloat16") else LA_F32
+
+
 def kernel_name(backward: bool, dtype, C: int, D: int):
     """Name of the kernel a fwd (backward=False) or bwd call launches for this element type
     ("bf16"/"float32" or a torch dtype), chunk length and head dimension; None if unsupported."""
-    dt = LA_BF16 if str(dtype).replace("torch.", "") in ("bf16", "bfloat16") else LA_F32
-    name = load_library().la_kernel_name(int(bool(backward)), dt, int(C), int(D))
+    name = load_library().la_kernel_name(int(bool(backward)), _dt_code(dtype), int(C), int(D))
     return None if name is None else name.decode()
+
+
+def seq_kernel_name(backward: bool, dtype, chunk: int, D: int):
+    """Name of the kernel seq_fwd / seq_bwd launch for this element type, chunk length and D."""
+    name = load_library().la_seq_kernel_name(int(bool(backward)), _dt_code(dtype), int(chunk), int(D))
+    return None if name is None else name.decode()
+
+
+def seq_supported(dtype, T: int, D: int, chunk: int) -> bool:
+    """Whether seq_fwd / seq_bwd take a (G, T, D) sequence in chunks of ``chunk`` tokens:
+    bf16, D = 64, 128-token chunks, whole chunks only (T below 2^24)."""
+    return (_dt_code(dtype) == LA_BF16 and D == 64 and chunk == 128 and T > 0 and T % chunk == 0
+            and T < (1 << 24))
 
 
 def time_next_launch(start_event, stop_event):
@@ -199,6 +223,57 @@ def bwd(q, k, v, S_in, z_in, dO, dS_out=None, dz_out=None, block: int = 64, out=
                                             dO.data_ptr(), _ptr(dS_out), _ptr(dz_out), dq.data_ptr(),
                                             dk.data_ptr(), dv.data_ptr(), dS_in.data_ptr(), dz_in.data_ptr(),
                                             G, C, D, int(block), _dtype_code(q), _stream(dev)))
+    return dq, dk, dv, dS_in, dz_in
+
+
+def seq_fwd(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int = 64, out=None):
+    """Forward over a whole (G, T, D) sequence of chunks in one launch, carry on chip:
+    returns (o, S_out, z_out), equal to chaining fwd over the chunks."""
+    lib = _lib or load_library()
+    G, T, D, dev = _validate_tokens(("q", "k", "v"), (q, k, v))
+    if (S_in is None) != (z_in is None):
+        raise ValueError("S_in and z_in must be given together")
+    _validate_state("S_in", S_in, (G, D, D), dev)
+    _validate_state("z_in", z_in, (G, D), dev)
+    if out is None:
+        import torch
+        o = torch.empty_like(q)
+        S_out = torch.empty((G, D, D), dtype=torch.float32, device=q.device)
+        z_out = torch.empty((G, D), dtype=torch.float32, device=q.device)
+    else:
+        o, S_out, z_out = out
+    _check("la_seq_fwd", lib.la_seq_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(S_in), _ptr(z_in),
+                                        o.data_ptr(), S_out.data_ptr(), z_out.data_ptr(), G, T, D, int(chunk),
+                                        int(block), _dtype_code(q), _stream(dev)))
+    return o, S_out, z_out
+
+
+def seq_bwd(q, k, v, S_last, z_last, dO, dS_out=None, dz_out=None, chunk: int = 128, block: int = 64, out=None):
+    """Backward over a whole sequence in one launch, last chunk first, reverse state on chip.
+    (S_last, z_last) is the carry after the last chunk: seq_fwd's (S_out, z_out).
+    Returns (dq, dk, dv, dS_in, dz_in)."""
+    lib = _lib or load_library()
+    G, T, D, dev = _validate_tokens(("q", "k", "v", "dO"), (q, k, v, dO))
+    if S_last is None or z_last is None:
+        raise ValueError("S_last and z_last (the forward's final carry) are required")
+    if (dS_out is None) != (dz_out is None):
+        raise ValueError("dS_out and dz_out must be given together")
+    _validate_state("S_last", S_last, (G, D, D), dev)
+    _validate_state("z_last", z_last, (G, D), dev)
+    _validate_state("dS_out", dS_out, (G, D, D), dev)
+    _validate_state("dz_out", dz_out, (G, D), dev)
+    if out is None:
+        import torch
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        dS_in = torch.empty((G, D, D), dtype=torch.float32, device=q.device)
+        dz_in = torch.empty((G, D), dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv, dS_in, dz_in = out
+    _check("la_seq_bwd", lib.la_seq_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), S_last.data_ptr(),
+                                        z_last.data_ptr(), dO.data_ptr(), _ptr(dS_out), _ptr(dz_out),
+                                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dS_in.data_ptr(),
+                                        dz_in.data_ptr(), G, T, D, int(chunk), int(block), _dtype_code(q),
+                                        _stream(dev)))
     return dq, dk, dv, dS_in, dz_in
 
 

@@ -8,10 +8,12 @@ from one chunk to the next.  This module gives that op a backward:
 
 q, k, v are (G, T, D) CUDA tensors (bf16 or fp32; q and k already positive, e.g.
 elu(x) + 1); S_in (G, D, D) and z_in (G, D) are fp32 or None for a zero carry.
-Every chunk is one forward launch; its backward is one backward launch that
-recomputes the chunk from its saved inputs (q, k, v and the carry that fed it),
-so nothing of size (G, C, D, D) or (G, C, C) is kept between the passes, the
-memory-flat principle of the page's section 1.  Gradients flow to q, k, v and,
+Where the library's sequence entry points take the shape (bf16, D = 64, whole
+128-token chunks) the sequence is one forward and one backward launch with the
+carry kept on chip; otherwise every chunk is one forward launch and its backward
+one backward launch that recomputes the chunk from its saved inputs (q, k, v and
+the carry that fed it).  Either way nothing of size (G, C, D, D) or (G, C, C) is
+kept between the passes, the memory-flat principle of the page's section 1.  Gradients flow to q, k, v and,
 when given, S_in and z_in; a loss on S_out / z_out reaches them too.
 
 The arithmetic runs in the HIP library only: CPU tensors raise.
@@ -22,6 +24,9 @@ import torch
 
 from . import bwd as _bwd
 from . import fwd as _fwd
+from . import seq_bwd as _seq_bwd
+from . import seq_fwd as _seq_fwd
+from . import seq_supported as _seq_supported
 
 
 class ChunkFunction(torch.autograd.Function):
@@ -56,6 +61,39 @@ class ChunkFunction(torch.autograd.Function):
         return dq, dk, dv, dS_in, dz_in, None
 
 
+class SeqFunction(torch.autograd.Function):
+    """A whole sequence of chunks in one launch per direction (the library's sequence entry
+    points); saves the inputs and the final carry, from which the backward recovers the
+    state before each chunk."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, S_in, z_in, chunk, block):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        o, S_out, z_out = _seq_fwd(q, k, v, S_in, z_in, chunk, block)
+        ctx.chunk, ctx.block = chunk, block
+        ctx.has_carry = S_in is not None
+        ctx.save_for_backward(q, k, v, S_out, z_out)
+        return o, S_out, z_out
+
+    @staticmethod
+    def backward(ctx, do, dS_out, dz_out):
+        q, k, v, S_out, z_out = ctx.saved_tensors
+        G, T, D = q.shape
+        if do is None:
+            do = torch.zeros_like(q)
+        if dS_out is None and dz_out is not None:
+            dS_out = torch.zeros((G, D, D), dtype=torch.float32, device=q.device)
+        if dz_out is None and dS_out is not None:
+            dz_out = torch.zeros((G, D), dtype=torch.float32, device=q.device)
+        dS_out = None if dS_out is None else dS_out.float().contiguous()
+        dz_out = None if dz_out is None else dz_out.float().contiguous()
+        dq, dk, dv, dS_in, dz_in = _seq_bwd(q, k, v, S_out, z_out, do.to(q.dtype).contiguous(), dS_out, dz_out,
+                                            ctx.chunk, ctx.block)
+        if not ctx.has_carry:
+            dS_in = dz_in = None
+        return dq, dk, dv, dS_in, dz_in, None, None
+
+
 def chunk_attention(q, k, v, S_in=None, z_in=None, block: int = 64):
     """Differentiable single-chunk op: returns (o, S_out, z_out)."""
     _check_device(q)
@@ -73,6 +111,9 @@ def linear_attention(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int
     T = q.shape[1]
     if T == 0:
         return q.new_empty(q.shape), (S_in, z_in)
+    if _seq_supported(q.dtype, T, q.shape[2], chunk) and block == 64:
+        o, S, z = SeqFunction.apply(q, k, v, S_in, z_in, chunk, block)
+        return o, (S, z)
     outs = []
     S, z = S_in, z_in
     for t0 in range(0, T, chunk):

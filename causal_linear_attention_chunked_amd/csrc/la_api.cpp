@@ -61,6 +61,18 @@ la_status common_checks(int G, int C, int D, int block, la_dtype dt, Sizes *sz) 
     return LA_OK;
 }
 
+// Sequence entry points: the supported set (bf16, D = 64, 128-token chunks, whole chunks).
+la_status seq_checks(int G, int T, int D, int chunk, int block, la_dtype dt, Sizes *sz) {
+    if (G < 1 || T < 1 || chunk < 1) return LA_ERR_INVALID;
+    la_status st = common_checks(G, chunk, D, block, dt, sz);
+    if (st != LA_OK) return st;
+    if (dt != LA_BF16 || D != 64 || chunk != 128 || T % chunk != 0 || T >= (1 << 24)) return LA_ERR_UNSUPPORTED;
+    size_t a, b;
+    if (!mul_ok((size_t)G, (size_t)T, &a) || !mul_ok(a, (size_t)D * 2, &b)) return LA_ERR_INVALID;
+    sz->tok = b;
+    return LA_OK;
+}
+
 // every output span against every input span and every other output span
 la_status alias_checks(const Span *in, int nin, const Span *out, int nout) {
     for (int i = 0; i < nout; ++i) {
@@ -143,6 +155,52 @@ la_status la_chunk_bwd(const void *q, const void *k, const void *v, const float 
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
+la_status la_seq_fwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in, void *o,
+                     float *S_out, float *z_out, int G, int T, int D, int chunk, int block, la_dtype dt,
+                     void *stream) {
+    const TakenEvents te;
+    Sizes sz;
+    la_status st = seq_checks(G, T, D, chunk, block, dt, &sz);
+    if (st != LA_OK) return st;
+    if (!q || !k || !v || !o || !S_out || !z_out) return LA_ERR_INVALID;
+    if ((S_in == nullptr) != (z_in == nullptr)) return LA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, S_in, z_in, o, S_out, z_out};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return LA_ERR_ALIGN;
+    const Span in[] = {span(q, sz.tok), span(k, sz.tok), span(v, sz.tok), span(S_in, sz.st), span(z_in, sz.z)};
+    const Span out[] = {span(o, sz.tok), span(S_out, sz.st), span(z_out, sz.z)};
+    st = alias_checks(in, 5, out, 3);
+    if (st != LA_OK) return st;
+    const hipError_t e = lachunk::launch_seq_fwd_c128(q, k, v, S_in, z_in, o, S_out, z_out, G, T / chunk,
+                                                      reinterpret_cast<hipStream_t>(stream), te.ev);
+    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
+
+la_status la_seq_bwd(const void *q, const void *k, const void *v, const float *S_last, const float *z_last,
+                     const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
+                     float *dS_in, float *dz_in, int G, int T, int D, int chunk, int block, la_dtype dt,
+                     void *stream) {
+    const TakenEvents te;
+    Sizes sz;
+    la_status st = seq_checks(G, T, D, chunk, block, dt, &sz);
+    if (st != LA_OK) return st;
+    if (!q || !k || !v || !S_last || !z_last || !dO || !dq || !dk || !dv || !dS_in || !dz_in) return LA_ERR_INVALID;
+    if ((dS_out == nullptr) != (dz_out == nullptr)) return LA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, S_last, z_last, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return LA_ERR_ALIGN;
+    const Span in[] = {span(q, sz.tok),    span(k, sz.tok),     span(v, sz.tok),     span(S_last, sz.st),
+                       span(z_last, sz.z), span(dO, sz.tok),    span(dS_out, sz.st), span(dz_out, sz.z)};
+    const Span out[] = {span(dq, sz.tok), span(dk, sz.tok), span(dv, sz.tok), span(dS_in, sz.st),
+                        span(dz_in, sz.z)};
+    st = alias_checks(in, 8, out, 5);
+    if (st != LA_OK) return st;
+    const hipError_t e =
+        lachunk::launch_seq_bwd_c128(q, k, v, S_last, z_last, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, G,
+                                     T / chunk, reinterpret_cast<hipStream_t>(stream), te.ev);
+    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
+
 const char *la_status_str(la_status s) {
     switch (s) {
         case LA_OK: return "ok";
@@ -163,6 +221,11 @@ const char *la_kernel_name(int backward, la_dtype dt, int C, int D) {
     if (!backward) return c128 ? "la_fwd_c128_kernel" : "la_fwd_kernel";
     if (C > LA_BWD_MAX_C || (dt == LA_F32 && D == 128)) return nullptr;
     return c128 ? "la_bwd_c128w16_kernel" : "la_bwd_kernel";
+}
+
+const char *la_seq_kernel_name(int backward, la_dtype dt, int chunk, int D) {
+    if (dt != LA_BF16 || D != 64 || chunk != 128) return nullptr;
+    return backward ? "la_seq_bwd_c128w16_kernel" : "la_seq_fwd_c128_kernel";
 }
 
 la_status la_time_next_launch(void *start_event, void *stop_event) {

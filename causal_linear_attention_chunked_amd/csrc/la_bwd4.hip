@@ -35,6 +35,13 @@
 //   4  dq; Sh_0 = Sh_1 + Q_1^T dN_1 (split copy), zh_0; pass 2 of block 1 and the
 //      intra-block part of pass 2 of block 0
 //   5  the inter-block part of pass 2 of block 0; dS_in = Sh_0 + Q_0^T dN_0
+//
+// Sequence mode (SEQ): one workgroup walks a group's n consecutive chunks last to first,
+// carrying the reverse state (Sh, zh) in registers from one chunk to the one before it.
+// The forward state comes from the carry after the last chunk instead of per-chunk
+// carries: going backwards, S_1 = S_end - K_1^T V_1 and S_0 = S_1 - K_0^T V_0 (exact
+// products of the inputs, summed in fp32), and S_0 is the previous chunk's S_end.  Chunk
+// c - 1's inputs are loaded into the staging registers while chunk c computes.
 #include "la_tile.h"
 #include "la_launch.h"
 #include <hip/hip_ext.h>
@@ -64,12 +71,19 @@ struct Bwd4Lds {
 };
 }  // namespace
 
-__global__ __launch_bounds__(W16_THREADS, 1) void la_bwd_c128w16_kernel(
+// bf16 fragment negated (sign bits flipped): acc += (-X) Y^T subtracts a product exactly
+__device__ __forceinline__ bf16x8 neg8(const bf16x8 &x) {
+    return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, x) ^ 0x80008000u);
+}
+
+// S_in, z_in: the carry before the chunk (single chunk) or after the last chunk (SEQ).
+template <bool SEQ>
+__device__ __forceinline__ void bwd_c128_body(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ S_in, const float *__restrict__ z_in, const bf16 *__restrict__ dO,
     const float *__restrict__ dS_out, const float *__restrict__ dz_out,
     bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
-    float *__restrict__ dS_in, float *__restrict__ dz_in) {
+    float *__restrict__ dS_in, float *__restrict__ dz_in, int nchunk) {
     using L = Bwd4Lds;
     constexpr int D = 64, C = 128;
     constexpr uint32_t CHUNK = C * D * 2;
@@ -91,26 +105,30 @@ __global__ __launch_bounds__(W16_THREADS, 1) void la_bwd_c128w16_kernel(
     // state tile: value tile ct, key-feature tile pt
     const int ct = w & 3, pt = w >> 2;
     const int grp = blockIdx.x;
-    const size_t tok0 = (size_t)grp * C;
-    const bool has_up = dS_out != nullptr;
-    const GRes qr(q + tok0 * D, CHUNK), kr(k + tok0 * D, CHUNK), vr(v + tok0 * D, CHUNK), gr(dO + tok0 * D, CHUNK);
+    const int n = SEQ ? nchunk : 1;
+    const size_t gtok0 = (size_t)grp * n * C;  // the group's n chunks, contiguous
+    const uint32_t seq_bytes = (uint32_t)n * CHUNK;
+    const GRes qr(q + gtok0 * D, seq_bytes), kr(k + gtok0 * D, seq_bytes), vr(v + gtok0 * D, seq_bytes),
+        gr(dO + gtok0 * D, seq_bytes);
     const float *const dummy = dS_in;  // a valid base for an empty range
     const GRes sres(S_in ? (const void *)(S_in + (size_t)grp * D * D) : dummy, S_in ? D * D * 4 : 0);
     const GRes zres(z_in ? (const void *)(z_in + (size_t)grp * D) : dummy, z_in ? D * 4 : 0);
-    const GRes shres(has_up ? (const void *)(dS_out + (size_t)grp * D * D) : dummy, has_up ? D * D * 4 : 0);
+    const GRes shres(dS_out ? (const void *)(dS_out + (size_t)grp * D * D) : dummy, dS_out ? D * D * 4 : 0);
     const GRes zhres(dz_out ? (const void *)(dz_out + (size_t)grp * D) : dummy, dz_out ? D * 4 : 0);
-    const TileLanes TL(lane);
-    const uint32_t tr_c = TL.tr_at(ct), tr_p = TL.tr_at(pt), nat_c = TL.nat_at(ct);
 
     // ---- prologue: every load issued before anything waits.  Thread tid stages 16 bytes of
     // Q, K, V and dO of block tid / 512.
     const int sb = tid >> 9;
     const uint32_t gso = sb * TBYTES + (tid & 511) * 16;
     bf16x8 st[4];
-    st[0] = gload<bf16x8>(qr, gso);
-    st[1] = gload<bf16x8>(kr, gso);
-    st[2] = gload<bf16x8>(vr, gso);
-    st[3] = gload<bf16x8>(gr, gso);
+    auto load_stage = [&](int c) {
+        const uint32_t o = (uint32_t)c * CHUNK + gso;
+        st[0] = gload<bf16x8>(qr, o);
+        st[1] = gload<bf16x8>(kr, o);
+        st[2] = gload<bf16x8>(vr, o);
+        st[3] = gload<bf16x8>(gr, o);
+    };
+    load_stage(n - 1);
     // state accumulators C[c][p] (lane: p = 16 pt + r, c = 16 ct + 4g + e): S and Sh
     floatx4 Sacc, Sh, zr, zhr;
     {
@@ -124,328 +142,401 @@ __global__ __launch_bounds__(W16_THREADS, 1) void la_bwd_c128w16_kernel(
     }
     issue_fence();
 
-    // ---- phase 0
-    {
-        const uint32_t so = sb * TBYTES + stage_off(tid & 511);
-        *reinterpret_cast<bf16x8 *>(smem + L::QT + so) = st[0];
-        *reinterpret_cast<bf16x8 *>(smem + L::KT + so) = st[1];
-        *reinterpret_cast<bf16x8 *>(smem + L::VT + so) = st[2];
-        *reinterpret_cast<bf16x8 *>(smem + L::GT + so) = st[3];
-    }
-    // split copy of the wave's state tile (C[c][p] accumulator), stored [p][c] (hi, lo tiles)
-    auto write_split = [&](char *hi, char *lo, const floatx4 &acc) {
-        bf16x4 hh, ll;
-        split4(acc, hh, ll);
-        tstore_acc(hi, nat_c, pt, hh);
-        tstore_acc(lo, nat_c, pt, ll);
-    };
-    auto write_z = [&](float *dst, const floatx4 &zz) {
-        if (ct == 0 && g == 0) dst[16 * pt + r] = zz[0];
-    };
-    write_split(tile(L::SS, 0), tile(L::SS, 1), Sacc);
-    write_z(zf, zr);
-    if (has_up) write_split(tile(L::SH1, 0), tile(L::SH1, 1), Sh);
-    write_z(zh + 64, zhr);
-    lds_barrier();
+    for (int c = n - 1; c >= 0; --c) {
+        // Lane-dependent offsets are derived afresh each chunk from an opaque copy of the thread
+        // index: hoisted out of the loop they would all stay live across it (and spill).
+        int tid_c = tid;
+        if (SEQ) asm volatile("" : "+v"(tid_c));
+        const int lane = tid_c & 63, r = lane & 15, g = lane >> 4;
+        const TileLanes TL(lane);
+        const uint32_t tr_c = TL.tr_at(ct), tr_p = TL.tr_at(pt), nat_c = TL.nat_at(ct);
+        const size_t tok0 = gtok0 + (size_t)c * C;
+        // the reverse state after this chunk is nonzero unless it is the last one without dS_out
+        const bool has_up = (SEQ && c < n - 1) || dS_out != nullptr;
 
-    // ---- phase 1.  S_1 = S_0 + K_0^T V_0 as C[c][p] = sum_j V[j][c] K[j][p]; z_1 = z_0 + K_0^T 1
-    const bf16x8 ones = ones_frag<bf16>();
-    {
-        bf16x8 vt[2], kt[2];
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            vt[kc] = tfrag_tr(tile(L::VT, 0), tr_c, kc);
-            kt[kc] = tfrag_tr(tile(L::KT, 0), tr_p, kc);
+        // ---- phase 0
+        {
+            const uint32_t so = sb * TBYTES + stage_off(tid_c & 511);
+            *reinterpret_cast<bf16x8 *>(smem + L::QT + so) = st[0];
+            *reinterpret_cast<bf16x8 *>(smem + L::KT + so) = st[1];
+            *reinterpret_cast<bf16x8 *>(smem + L::VT + so) = st[2];
+            *reinterpret_cast<bf16x8 *>(smem + L::GT + so) = st[3];
         }
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) mma(Sacc, vt[kc], kt[kc]);
-        if (ct == 0) {
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) mma(zr, ones, kt[kc]);
+        // the chunk before, in flight during this one.  Unconditional: for c = 0 the offsets lie
+        // past the buffer range (reads give zero, memory is not touched), and a load on every
+        // path lets the compiler count outstanding loads exactly instead of draining them all.
+        if (SEQ) load_stage(c - 1);
+        // split copy of the wave's state tile (C[c][p] accumulator), stored [p][c] (hi, lo tiles)
+        auto write_split = [&](char *hi, char *lo, const floatx4 &acc) {
+            bf16x4 hh, ll;
+            split4(acc, hh, ll);
+            tstore_acc(hi, nat_c, pt, hh);
+            tstore_acc(lo, nat_c, pt, ll);
+        };
+        auto write_z = [&](float *dst, const floatx4 &zz) {
+            if (ct == 0 && g == 0) dst[16 * pt + r] = zz[0];
+        };
+        if (!SEQ) {
+            write_split(tile(L::SS, 0), tile(L::SS, 1), Sacc);
+            write_z(zf, zr);
         }
-    }
-    // pass-1 operands: this wave's queries (row t = r, k = feature) and its two key tiles
-    bf16x8 qf[2], df[2], kfr[2][2], vfr[2][2];
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-        qf[kc] = tfrag(tile(L::QT, blk), TL, tq, kc);
-        df[kc] = tfrag(tile(L::GT, blk), TL, tq, kc);
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            kfr[jj][kc] = tfrag(tile(L::KT, blk), TL, 2 * h + jj, kc);
-            vfr[jj][kc] = tfrag(tile(L::VT, blk), TL, 2 * h + jj, kc);
-        }
-    }
-    // A^T, G^T (lane: query t = r, key j = 16 (2h + jj) + 4g + i), masked to j <= t
-    floatx4 aT[2], gT[2];
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        aT[jj] = zero4();
-        gT[jj] = zero4();
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            mma(aT[jj], kfr[jj][kc], qf[kc]);
-            mma(gT[jj], vfr[jj][kc], df[kc]);
-        }
-        const int j4 = 2 * h + jj;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bool keep = j4 < tq || (j4 == tq && 4 * g + e <= r);
-            aT[jj][e] = keep ? aT[jj][e] : 0.f;
-            gT[jj][e] = keep ? gT[jj][e] : 0.f;
-        }
-    }
-    write_split(tile(L::SS, 2), tile(L::SS, 3), Sacc);
-    write_z(zf + 64, zr);
-    lds_barrier();
+        if (has_up) write_split(tile(L::SH1, 0), tile(L::SH1, 1), Sh);
+        write_z(zh + 64, zhr);
+        lds_barrier();
 
-    // ---- phase 2.  H^T[p][t] = sum_c S_b[p][c] dO[t][c] for key-feature tiles 2h, 2h+1
-    // (lane: t = r, p = 16 (2h + pp) + 4g + i); partial row sums of this half
-    floatx4 hT[2], zv[2];
-    {
-        bf16x8 sh[2][2], sl[2][2];
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
+        // ---- phase 1.  Forward state of block b as C[c][p] = sum_j V[j][c] K[j][p] and z: in order,
+        // S_1 = S_0 + K_0^T V_0; in sequence mode backwards, S_1 = S_end - K_1^T V_1 (copy written
+        // here), then S_0 = S_1 - K_0^T V_0
+        const bf16x8 ones = ones_frag<bf16>();
+        auto state_step = [&](int b, bool sub) {
+            bf16x8 vt[2], kt[2];
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
-                sh[pp][kc] = tfrag(tile(L::SS, 2 * blk), TL, 2 * h + pp, kc);
-                sl[pp][kc] = tfrag(tile(L::SS, 2 * blk + 1), TL, 2 * h + pp, kc);
+                vt[kc] = tfrag_tr(tile(L::VT, b), tr_c, kc);
+                kt[kc] = tfrag_tr(tile(L::KT, b), tr_p, kc);
             }
+            const bf16x8 one = sub ? neg8(ones) : ones;
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-            hT[pp] = zero4();
+            for (int kc = 0; kc < 2; ++kc) mma(Sacc, sub ? neg8(vt[kc]) : vt[kc], kt[kc]);
+            if (ct == 0) {
 #pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                mma(hT[pp], sh[pp][kc], df[kc]);
-                mma(hT[pp], sl[pp][kc], df[kc]);
+                for (int kc = 0; kc < 2; ++kc) mma(zr, one, kt[kc]);
+            }
+        };
+        if (SEQ) {
+            state_step(1, true);
+            write_split(tile(L::SS, 2), tile(L::SS, 3), Sacc);
+            write_z(zf + 64, zr);
+            state_step(0, true);
+        } else {
+            state_step(0, false);
+        }
+        // pass-1 operands: this wave's queries (row t = r, k = feature) and its two key tiles
+        bf16x8 qf[2], df[2], kfr[2][2], vfr[2][2];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            qf[kc] = tfrag(tile(L::QT, blk), TL, tq, kc);
+            df[kc] = tfrag(tile(L::GT, blk), TL, tq, kc);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                kfr[jj][kc] = tfrag(tile(L::KT, blk), TL, 2 * h + jj, kc);
+                vfr[jj][kc] = tfrag(tile(L::VT, blk), TL, 2 * h + jj, kc);
             }
         }
-    }
-    {
-        float dpart = 0.f, rpart = 0.f;
-        const bf16x8 qh = h ? qf[1] : qf[0];  // key features 32h..32h+31 of q_t
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-            zv[pp] = *reinterpret_cast<const floatx4 *>(zf + 64 * blk + 16 * (2 * h + pp) + 4 * g);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // q_t[p] for p = 16 (2h + pp) + 4g + e: k-chunk h, slot 4 pp + e
-                const float qv = (float)qh[4 * pp + e];
-                dpart += qv * zv[pp][e];
-                rpart += qv * hT[pp][e];
-            }
-        }
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                dpart += aT[jj][e];
-                rpart += aT[jj][e] * gT[jj][e];
-            }
-        const float dsum = gsum(dpart), rsum = gsum(rpart);
-        if (g == 0) psum[(u * 2 + h) * 16 + r] = floatx2{dsum, rsum};
-    }
-    lds_barrier();
-
-    // ---- phase 3.  Row statistics from both halves; dP for this wave's key tiles
-    float inv, dden;
-    {
-        const floatx2 mine = psum[(u * 2 + h) * 16 + r], other = psum[(u * 2 + 1 - h) * 16 + r];
-        const float den = mine[0] + other[0];
-        inv = __builtin_amdgcn_rcpf(den);
-        const float rho = (mine[1] + other[1]) * inv;
-        dden = -rho * inv;
-        // dP^T[j][t] = inv (G - rho), masked; split; stored [t][j] for dq and pass 2
-        floatx4 d[2];
+        // A^T, G^T (lane: query t = r, key j = 16 (2h + jj) + 4g + i), masked to j <= t
+        floatx4 aT[2], gT[2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
+            aT[jj] = zero4();
+            gT[jj] = zero4();
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                mma(aT[jj], kfr[jj][kc], qf[kc]);
+                mma(gT[jj], vfr[jj][kc], df[kc]);
+            }
             const int j4 = 2 * h + jj;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const bool keep = j4 < tq || (j4 == tq && 4 * g + e <= r);
-                d[jj][e] = keep ? (gT[jj][e] - rho) * inv : 0.f;
+                aT[jj][e] = keep ? aT[jj][e] : 0.f;
+                gT[jj][e] = keep ? gT[jj][e] : 0.f;
             }
         }
-        const Split8 dps = split_acc(d[0], d[1]);
-        tstore_frag_at(tile(L::DP, 2 * blk), TL, tq, h, dps.hi);
-        tstore_frag_at(tile(L::DP, 2 * blk + 1), TL, tq, h, dps.lo);
-        if (h == 0 && g == 0) {
-            const int t = 64 * blk + 16 * tq + r;
-            invs[t] = inv;
-            rhos[t] = rho;
-            bf16x2 hh, ll;
-            split_pair(dden, 0.f, hh, ll);
-            ddr[t] = hh[0];
-            ddr[128 + t] = ll[0];
+        if (SEQ) {
+            write_split(tile(L::SS, 0), tile(L::SS, 1), Sacc);
+            write_z(zf, zr);
+        } else {
+            write_split(tile(L::SS, 2), tile(L::SS, 3), Sacc);
+            write_z(zf + 64, zr);
         }
-    }
-    lds_barrier();
+        lds_barrier();
 
-    // ---- phase 4.  dq^T[p][t] = sum_j K^T[p][j] dP[t][j] + inv H^T[p][t] + dden z_b[p]
-    {
-        bf16x8 dph[2], dpl[2], ktr[2][2];
+        // ---- phase 2.  H^T[p][t] = sum_c S_b[p][c] dO[t][c] for key-feature tiles 2h, 2h+1
+        // (lane: t = r, p = 16 (2h + pp) + 4g + i); partial row sums of this half
+        floatx4 hT[2], zv[2];
+        {
+            bf16x8 sh[2][2], sl[2][2];
 #pragma unroll
-        for (int jc = 0; jc < 2; ++jc) {
-            dph[jc] = tfrag(tile(L::DP, 2 * blk), TL, tq, jc);
-            dpl[jc] = tfrag(tile(L::DP, 2 * blk + 1), TL, tq, jc);
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp) ktr[pp][jc] = tfrag_tr(tile(L::KT, blk), TL.tr_at(2 * h + pp), jc);
-        }
-        bf16 *dqrow = dq + (tok0 + 64 * blk + 16 * tq + r) * D + 4 * g;
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-            floatx4 acc = hT[pp] * inv + dden * zv[pp];
-#pragma unroll
-            for (int jc = 0; jc < 2; ++jc) {
-                mma(acc, ktr[pp][jc], dph[jc]);
-                mma(acc, ktr[pp][jc], dpl[jc]);
-            }
-            store_bf16x4(dqrow + 16 * (2 * h + pp), pack4(acc));
-        }
-    }
-    // reverse state: Sh += Q_b^T dN_b as C[c][p] = sum_t dN[t][c] Q[t][p], zh += Q_b^T dden_b;
-    // dN^T (operand rows c, k = t) is dO^T scaled by inv_t
-    auto reverse = [&](int b) {
-        bf16x8 xg[2], qt[2];
-        floatx4 iv[2][2];
-#pragma unroll
-        for (int tc = 0; tc < 2; ++tc) {
-            xg[tc] = tfrag_tr(tile(L::GT, b), tr_c, tc);
-            qt[tc] = tfrag_tr(tile(L::QT, b), tr_p, tc);
-            iv[tc][0] = *reinterpret_cast<const floatx4 *>(invs + 64 * b + 32 * tc + 4 * g);
-            iv[tc][1] = *reinterpret_cast<const floatx4 *>(invs + 64 * b + 32 * tc + 16 + 4 * g);
-        }
-#pragma unroll
-        for (int tc = 0; tc < 2; ++tc) {
-            const bf16x8 x = xg[tc];
-            const floatx4 a0{(float)x[0] * iv[tc][0][0], (float)x[1] * iv[tc][0][1], (float)x[2] * iv[tc][0][2],
-                             (float)x[3] * iv[tc][0][3]};
-            const floatx4 a1{(float)x[4] * iv[tc][1][0], (float)x[5] * iv[tc][1][1], (float)x[6] * iv[tc][1][2],
-                             (float)x[7] * iv[tc][1][3]};
-            mma_s(Sh, split_acc(a0, a1), qt[tc]);
-        }
-        if (ct == 0) {
-#pragma unroll
-            for (int tc = 0; tc < 2; ++tc) {
-                mma(zhr, rowfrag(reinterpret_cast<const char *>(ddr + 64 * b), lane, tc), qt[tc]);
-                mma(zhr, rowfrag(reinterpret_cast<const char *>(ddr + 128 + 64 * b), lane, tc), qt[tc]);
-            }
-        }
-    };
-    reverse(1);
-    write_split(tile(L::SS, 0), tile(L::SS, 1), Sh);  // Sh_0 (the S_0 copy is no longer read)
-    write_z(zh, zhr);
-
-    // pass 2: wave w takes block (w / 4) % 2 and dv (w < 8, key tile w % 4) or dk (key tile
-    // 3 - w % 4: each SIMD holds a long and a short causal range of either output);
-    // accumulators dv^T[c][j] or dk^T[p][j] (lane: key j = r, column 16 x + 4g + i)
-    auto pass2 = [&](auto dk_tag, auto b_tag, bool inter_phase, floatx4 (&acc)[4], bf16x8 (&kv)[2]) {
-        constexpr bool DK = decltype(dk_tag)::value;
-        constexpr int B = decltype(b_tag)::value;
-        const int jt = DK ? 3 - (w & 3) : (w & 3);
-        auto inter = [&](const char *shh, const char *shl) {
-            bf16x8 sh[4][2], sl[4][2];
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
+            for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
-                    sh[x][kc] = DK ? tfrag(shh, TL, x, kc) : tfrag_tr(shh, TL.tr[x], kc);
-                    sl[x][kc] = DK ? tfrag(shl, TL, x, kc) : tfrag_tr(shl, TL.tr[x], kc);
+                    sh[pp][kc] = tfrag(tile(L::SS, 2 * blk), TL, 2 * h + pp, kc);
+                    sl[pp][kc] = tfrag(tile(L::SS, 2 * blk + 1), TL, 2 * h + pp, kc);
                 }
 #pragma unroll
-            for (int kc = 0; kc < 2; ++kc)
+            for (int pp = 0; pp < 2; ++pp) {
+                hT[pp] = zero4();
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    mma(hT[pp], sh[pp][kc], df[kc]);
+                    mma(hT[pp], sl[pp][kc], df[kc]);
+                }
+            }
+        }
+        {
+            float dpart = 0.f, rpart = 0.f;
+            const bf16x8 qh = h ? qf[1] : qf[0];  // key features 32h..32h+31 of q_t
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                zv[pp] = *reinterpret_cast<const floatx4 *>(zf + 64 * blk + 16 * (2 * h + pp) + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // q_t[p] for p = 16 (2h + pp) + 4g + e: k-chunk h, slot 4 pp + e
+                    const float qv = (float)qh[4 * pp + e];
+                    dpart += qv * zv[pp][e];
+                    rpart += qv * hT[pp][e];
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dpart += aT[jj][e];
+                    rpart += aT[jj][e] * gT[jj][e];
+                }
+            const float dsum = gsum(dpart), rsum = gsum(rpart);
+            if (g == 0) psum[(u * 2 + h) * 16 + r] = floatx2{dsum, rsum};
+        }
+        lds_barrier();
+
+        // ---- phase 3.  Row statistics from both halves; dP for this wave's key tiles
+        float inv, dden;
+        {
+            const floatx2 mine = psum[(u * 2 + h) * 16 + r], other = psum[(u * 2 + 1 - h) * 16 + r];
+            const float den = mine[0] + other[0];
+            inv = __builtin_amdgcn_rcpf(den);
+            const float rho = (mine[1] + other[1]) * inv;
+            dden = -rho * inv;
+            // dP^T[j][t] = inv (G - rho), masked; split; stored [t][j] for dq and pass 2
+            floatx4 d[2];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j4 = 2 * h + jj;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool keep = j4 < tq || (j4 == tq && 4 * g + e <= r);
+                    d[jj][e] = keep ? (gT[jj][e] - rho) * inv : 0.f;
+                }
+            }
+            const Split8 dps = split_acc(d[0], d[1]);
+            tstore_frag_at(tile(L::DP, 2 * blk), TL, tq, h, dps.hi);
+            tstore_frag_at(tile(L::DP, 2 * blk + 1), TL, tq, h, dps.lo);
+            if (h == 0 && g == 0) {
+                const int t = 64 * blk + 16 * tq + r;
+                invs[t] = inv;
+                rhos[t] = rho;
+                bf16x2 hh, ll;
+                split_pair(dden, 0.f, hh, ll);
+                ddr[t] = hh[0];
+                ddr[128 + t] = ll[0];
+            }
+        }
+        lds_barrier();
+
+        // ---- phase 4.  dq^T[p][t] = sum_j K^T[p][j] dP[t][j] + inv H^T[p][t] + dden z_b[p]
+        {
+            bf16x8 dph[2], dpl[2], ktr[2][2];
+#pragma unroll
+            for (int jc = 0; jc < 2; ++jc) {
+                dph[jc] = tfrag(tile(L::DP, 2 * blk), TL, tq, jc);
+                dpl[jc] = tfrag(tile(L::DP, 2 * blk + 1), TL, tq, jc);
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) ktr[pp][jc] = tfrag_tr(tile(L::KT, blk), TL.tr_at(2 * h + pp), jc);
+            }
+            bf16 *dqrow = dq + (tok0 + 64 * blk + 16 * tq + r) * D + 4 * g;
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                floatx4 acc = hT[pp] * inv + dden * zv[pp];
+#pragma unroll
+                for (int jc = 0; jc < 2; ++jc) {
+                    mma(acc, ktr[pp][jc], dph[jc]);
+                    mma(acc, ktr[pp][jc], dpl[jc]);
+                }
+                store_bf16x4<!SEQ>(dqrow + 16 * (2 * h + pp), pack4(acc));
+            }
+        }
+        // reverse state: Sh += Q_b^T dN_b as C[c][p] = sum_t dN[t][c] Q[t][p], zh += Q_b^T dden_b;
+        // dN^T (operand rows c, k = t) is dO^T scaled by inv_t
+        auto reverse = [&](int b) {
+            bf16x8 xg[2], qt[2];
+            floatx4 iv[2][2];
+#pragma unroll
+            for (int tc = 0; tc < 2; ++tc) {
+                xg[tc] = tfrag_tr(tile(L::GT, b), tr_c, tc);
+                qt[tc] = tfrag_tr(tile(L::QT, b), tr_p, tc);
+                iv[tc][0] = *reinterpret_cast<const floatx4 *>(invs + 64 * b + 32 * tc + 4 * g);
+                iv[tc][1] = *reinterpret_cast<const floatx4 *>(invs + 64 * b + 32 * tc + 16 + 4 * g);
+            }
+#pragma unroll
+            for (int tc = 0; tc < 2; ++tc) {
+                const bf16x8 x = xg[tc];
+                const floatx4 a0{(float)x[0] * iv[tc][0][0], (float)x[1] * iv[tc][0][1], (float)x[2] * iv[tc][0][2],
+                                 (float)x[3] * iv[tc][0][3]};
+                const floatx4 a1{(float)x[4] * iv[tc][1][0], (float)x[5] * iv[tc][1][1], (float)x[6] * iv[tc][1][2],
+                                 (float)x[7] * iv[tc][1][3]};
+                mma_s(Sh, split_acc(a0, a1), qt[tc]);
+            }
+            if (ct == 0) {
+#pragma unroll
+                for (int tc = 0; tc < 2; ++tc) {
+                    mma(zhr, rowfrag(reinterpret_cast<const char *>(ddr + 64 * b), lane, tc), qt[tc]);
+                    mma(zhr, rowfrag(reinterpret_cast<const char *>(ddr + 128 + 64 * b), lane, tc), qt[tc]);
+                }
+            }
+        };
+        reverse(1);
+        write_split(tile(L::SS, 0), tile(L::SS, 1), Sh);  // Sh_0 (the S_0 copy is no longer read)
+        write_z(zh, zhr);
+
+        // pass 2: wave w takes block (w / 4) % 2 and dv (w < 8, key tile w % 4) or dk (key tile
+        // 3 - w % 4: each SIMD holds a long and a short causal range of either output);
+        // accumulators dv^T[c][j] or dk^T[p][j] (lane: key j = r, column 16 x + 4g + i)
+        auto pass2 = [&](auto dk_tag, auto b_tag, bool inter_phase, floatx4 (&acc)[4], bf16x8 (&kv)[2]) {
+            constexpr bool DK = decltype(dk_tag)::value;
+            constexpr int B = decltype(b_tag)::value;
+            const int jt = DK ? 3 - (w & 3) : (w & 3);
+            auto inter = [&](const char *shh, const char *shl) {
+                if constexpr (SEQ) {
+                    // half the fragments at a time: the sequence loop has fewer registers to spare
+#pragma unroll
+                    for (int kc = 0; kc < 2; ++kc) {
+                        bf16x8 sh[4], sl[4];
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            sh[x] = DK ? tfrag(shh, TL, x, kc) : tfrag_tr(shh, TL.tr[x], kc);
+                            sl[x] = DK ? tfrag(shl, TL, x, kc) : tfrag_tr(shl, TL.tr[x], kc);
+                        }
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            mma(acc[x], sh[x], kv[kc]);
+                            mma(acc[x], sl[x], kv[kc]);
+                        }
+                    }
+                    return;
+                }
+                bf16x8 sh[4][2], sl[4][2];
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+#pragma unroll
+                    for (int kc = 0; kc < 2; ++kc) {
+                        sh[x][kc] = DK ? tfrag(shh, TL, x, kc) : tfrag_tr(shh, TL.tr[x], kc);
+                        sl[x][kc] = DK ? tfrag(shl, TL, x, kc) : tfrag_tr(shl, TL.tr[x], kc);
+                    }
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        mma(acc[x], sh[x][kc], kv[kc]);
+                        mma(acc[x], sl[x][kc], kv[kc]);
+                    }
+            };
+            auto store = [&]() {
+                bf16 *row = (DK ? dk : dv) + (tok0 + 64 * B + 16 * jt + r) * D + 4 * g;
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
-                    mma(acc[x], sh[x][kc], kv[kc]);
-                    mma(acc[x], sl[x][kc], kv[kc]);
+                    floatx4 y = acc[x];
+                    if constexpr (DK) y += *reinterpret_cast<const floatx4 *>(zh + 64 * B + 16 * x + 4 * g);
+                    store_bf16x4<!SEQ>(row + 16 * x, pack4(y));
                 }
-        };
-        auto store = [&]() {
-            bf16 *row = (DK ? dk : dv) + (tok0 + 64 * B + 16 * jt + r) * D + 4 * g;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                floatx4 y = acc[x];
-                if constexpr (DK) y += *reinterpret_cast<const floatx4 *>(zh + 64 * B + 16 * x + 4 * g);
-                store_bf16x4(row + 16 * x, pack4(y));
-            }
-        };
-        if (inter_phase) {  // phase 5, block 0: against Sh_0
-            inter(tile(L::SS, 0), tile(L::SS, 1));
-            store();
-            return;
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x) acc[x] = zero4();
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) kv[kc] = tfrag(tile(DK ? L::VT : L::KT, B), TL, jt, kc);
-        const uint32_t tr_jt = TL.tr_at(jt);
-#pragma unroll
-        for (int tc = 0; tc < 2; ++tc) {
-            if (2 * tc + 1 < jt) continue;  // every query of the slab precedes the key tile
-            bf16x8 xo[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) xo[x] = tfrag_tr(tile(DK ? L::QT : L::GT, B), TL.tr[x], tc);
-            Split8 y;
-            if constexpr (DK) {
-                // dP rows j, k = t, from the pass-1 copy
-                y = Split8{tfrag_tr(tile(L::DP, 2 * B), tr_jt, tc), tfrag_tr(tile(L::DP, 2 * B + 1), tr_jt, tc)};
-            } else {
-                // A[t][j] inv_t recomputed (lane: j = r, t = 32 tc + 16 hh + 4g + i), masked to t >= j
-                bf16x8 qa[2][2];
-                floatx4 iv[2], at[2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    iv[hh] = *reinterpret_cast<const floatx4 *>(invs + 64 * B + 32 * tc + 16 * hh + 4 * g);
-#pragma unroll
-                    for (int kc = 0; kc < 2; ++kc) qa[hh][kc] = tfrag(tile(L::QT, B), TL, 2 * tc + hh, kc);
-                }
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int t4 = 2 * tc + hh;
-                    at[hh] = zero4();
-#pragma unroll
-                    for (int kc = 0; kc < 2; ++kc) mma(at[hh], qa[hh][kc], kv[kc]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        at[hh][e] = (t4 > jt || (t4 == jt && 4 * g + e >= r)) ? at[hh][e] * iv[hh][e] : 0.f;
-                }
-                y = split_acc(at[0], at[1]);
+            };
+            if (inter_phase) {  // phase 5, block 0: against Sh_0
+                inter(tile(L::SS, 0), tile(L::SS, 1));
+                store();
+                return;
             }
 #pragma unroll
-            for (int x = 0; x < 4; ++x) mma_s(acc[x], xo[x], y);
+            for (int x = 0; x < 4; ++x) acc[x] = zero4();
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) kv[kc] = tfrag(tile(DK ? L::VT : L::KT, B), TL, jt, kc);
+            const uint32_t tr_jt = TL.tr_at(jt);
+#pragma unroll
+            for (int tc = 0; tc < 2; ++tc) {
+                if (2 * tc + 1 < jt) continue;  // every query of the slab precedes the key tile
+                bf16x8 xo[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) xo[x] = tfrag_tr(tile(DK ? L::QT : L::GT, B), TL.tr[x], tc);
+                Split8 y;
+                if constexpr (DK) {
+                    // dP rows j, k = t, from the pass-1 copy
+                    y = Split8{tfrag_tr(tile(L::DP, 2 * B), tr_jt, tc), tfrag_tr(tile(L::DP, 2 * B + 1), tr_jt, tc)};
+                } else {
+                    // A[t][j] inv_t recomputed (lane: j = r, t = 32 tc + 16 hh + 4g + i), masked to t >= j
+                    bf16x8 qa[2][2];
+                    floatx4 iv[2], at[2];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        iv[hh] = *reinterpret_cast<const floatx4 *>(invs + 64 * B + 32 * tc + 16 * hh + 4 * g);
+#pragma unroll
+                        for (int kc = 0; kc < 2; ++kc) qa[hh][kc] = tfrag(tile(L::QT, B), TL, 2 * tc + hh, kc);
+                    }
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int t4 = 2 * tc + hh;
+                        at[hh] = zero4();
+#pragma unroll
+                        for (int kc = 0; kc < 2; ++kc) mma(at[hh], qa[hh][kc], kv[kc]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            at[hh][e] = (t4 > jt || (t4 == jt && 4 * g + e >= r)) ? at[hh][e] * iv[hh][e] : 0.f;
+                    }
+                    y = split_acc(at[0], at[1]);
+                }
+#pragma unroll
+                for (int x = 0; x < 4; ++x) mma_s(acc[x], xo[x], y);
+            }
+            if (B == 1) {  // block 1 completes here, against Sh_1 = dS_out
+                if (has_up) inter(tile(L::SH1, 0), tile(L::SH1, 1));
+                store();
+            }
+        };
+        using T1 = std::integral_constant<bool, true>;
+        using F1 = std::integral_constant<bool, false>;
+        using B0 = std::integral_constant<int, 0>;
+        using B1 = std::integral_constant<int, 1>;
+        const int p2b = (w >> 2) & 1, p2dk = w >> 3;
+        floatx4 acc[4];
+        bf16x8 kv[2];
+        if (p2dk) {
+            if (p2b) pass2(T1{}, B1{}, false, acc, kv);
+            else pass2(T1{}, B0{}, false, acc, kv);
+        } else {
+            if (p2b) pass2(F1{}, B1{}, false, acc, kv);
+            else pass2(F1{}, B0{}, false, acc, kv);
         }
-        if (B == 1) {  // block 1 completes here, against Sh_1 = dS_out
-            if (has_up) inter(tile(L::SH1, 0), tile(L::SH1, 1));
-            store();
-        }
-    };
-    using T1 = std::integral_constant<bool, true>;
-    using F1 = std::integral_constant<bool, false>;
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
-    const int p2b = (w >> 2) & 1, p2dk = w >> 3;
-    floatx4 acc[4];
-    bf16x8 kv[2];
-    if (p2dk) {
-        if (p2b) pass2(T1{}, B1{}, false, acc, kv);
-        else pass2(T1{}, B0{}, false, acc, kv);
-    } else {
-        if (p2b) pass2(F1{}, B1{}, false, acc, kv);
-        else pass2(F1{}, B0{}, false, acc, kv);
-    }
-    lds_barrier();  // Sh_0, zh_0 visible
+        lds_barrier();  // Sh_0, zh_0 visible
 
-    // ---- phase 5
-    if (p2b == 0) {
-        if (p2dk) pass2(T1{}, B0{}, true, acc, kv);
-        else pass2(F1{}, B0{}, true, acc, kv);
-    }
-    reverse(0);
+        // ---- phase 5
+        if (p2b == 0) {
+            if (p2dk) pass2(T1{}, B0{}, true, acc, kv);
+            else pass2(F1{}, B0{}, true, acc, kv);
+        }
+        reverse(0);
+        // the tiles the next chunk's phase 0 writes are read up to here
+        if (SEQ && c > 0) lds_barrier();
+    }  // chunk loop
     {
         const int p = 16 * pt + r;
         __builtin_nontemporal_store(Sh, reinterpret_cast<floatx4 *>(dS_in + ((size_t)grp * D + p) * D + 16 * ct + 4 * g));
         if (ct == 0 && g == 0) __builtin_nontemporal_store(zhr[0], dz_in + (size_t)grp * D + p);
     }
+}
+
+__global__ __launch_bounds__(W16_THREADS, 1) void la_bwd_c128w16_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_in, const float *__restrict__ z_in, const bf16 *__restrict__ dO,
+    const float *__restrict__ dS_out, const float *__restrict__ dz_out,
+    bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
+    float *__restrict__ dS_in, float *__restrict__ dz_in) {
+    bwd_c128_body<false>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, 1);
+}
+
+__global__ __launch_bounds__(W16_THREADS, 1) void la_seq_bwd_c128w16_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_last, const float *__restrict__ z_last, const bf16 *__restrict__ dO,
+    const float *__restrict__ dS_out, const float *__restrict__ dz_out,
+    bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
+    float *__restrict__ dS_in, float *__restrict__ dz_in, int nchunk) {
+    bwd_c128_body<true>(q, k, v, S_last, z_last, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, nchunk);
 }
 
 hipError_t launch_bwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
@@ -454,6 +545,16 @@ hipError_t launch_bwd_c128(const void *q, const void *k, const void *v, const fl
     hipExtLaunchKernelGGL(la_bwd_c128w16_kernel, dim3((unsigned)G), dim3(W16_THREADS), 0, stream, ev[0], ev[1], 0,
                           (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_in, z_in, (const bf16 *)dO, dS_out,
                           dz_out, (bf16 *)dq, (bf16 *)dk, (bf16 *)dv, dS_in, dz_in);
+    return hipGetLastError();
+}
+
+hipError_t launch_seq_bwd_c128(const void *q, const void *k, const void *v, const float *S_last,
+                               const float *z_last, const void *dO, const float *dS_out, const float *dz_out,
+                               void *dq, void *dk, void *dv, float *dS_in, float *dz_in, int G, int nchunk,
+                               hipStream_t stream, const hipEvent_t ev[2]) {
+    hipExtLaunchKernelGGL(la_seq_bwd_c128w16_kernel, dim3((unsigned)G), dim3(W16_THREADS), 0, stream, ev[0], ev[1],
+                          0, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_last, z_last, (const bf16 *)dO,
+                          dS_out, dz_out, (bf16 *)dq, (bf16 *)dk, (bf16 *)dv, dS_in, dz_in, nchunk);
     return hipGetLastError();
 }
 

@@ -23,6 +23,13 @@
 // each); P enters the numerator MFMA as a split hi + lo operand; the state copy is
 // a plain bf16 operand (its term has no cancellation against the others); z_b is a
 // split row so the denominator's inter-block term is exact to about 16 bits.
+//
+// Sequence mode (SEQ): one workgroup walks a group's n consecutive chunks in order (the
+// carry across chunks of the page's section 2), the state staying in the wave's fp32
+// accumulators from one chunk to the next; chunk c + 1's keys, values and queries are
+// loaded into registers during chunk c (each into its staging registers as soon as they
+// are free, queries into spare ones), so they arrive while c computes.  Only the first
+// carry is read and the last one written.
 #include "la_tile.h"
 #include "la_launch.h"
 #include <hip/hip_ext.h>
@@ -41,10 +48,11 @@ struct Fwd2Lds {
 };
 }  // namespace
 
-__global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_kernel(
+template <bool SEQ>
+__device__ __forceinline__ void fwd_c128_body(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ S_in, const float *__restrict__ z_in,
-    bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out) {
+    bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out, int nchunk) {
     using L = Fwd2Lds;
     constexpr int D = 64, C = 128;
     constexpr uint32_t CHUNK = C * D * 2;
@@ -57,16 +65,17 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_kernel(
     const int tq = blk ? 3 - (w & 3) : (w & 3);
     const int ct = w & 3, pt0 = w >> 2;
     const int grp = blockIdx.x;
-    const size_t tok0 = (size_t)grp * C;
-    const GRes qr(q + tok0 * D, CHUNK), kr(k + tok0 * D, CHUNK), vr(v + tok0 * D, CHUNK);
+    const int n = SEQ ? nchunk : 1;
+    // the group's tokens: n chunks of C, contiguous ([G][n C][D])
+    const size_t gtok0 = (size_t)grp * n * C;
+    const uint32_t seq_bytes = (uint32_t)n * CHUNK;
+    const GRes qr(q + gtok0 * D, seq_bytes), kr(k + gtok0 * D, seq_bytes), vr(v + gtok0 * D, seq_bytes);
     // an absent carry is an empty range (reads give zero); the base only has to be a valid address
     const GRes sres(S_in ? (const void *)(S_in + (size_t)grp * D * D) : (const void *)S_out, S_in ? D * D * 4 : 0);
     const GRes zres(z_in ? (const void *)(z_in + (size_t)grp * D) : (const void *)z_out, z_in ? D * 4 : 0);
-    const TileLanes TL(lane);
     // this wave's state tiles: value tile ct, key-feature tiles pt[i] = pt0 + 2i, held as
     // accumulators C[c][p] (lane: p = 16 pt[i] + r, c = 16 ct + 4g + e)
     const int pt[2] = {pt0, pt0 + 2};
-    const uint32_t tr_c = TL.tr_at(ct), tr_p[2] = {TL.tr_at(pt0), TL.tr_at(pt0 + 2)}, nat_c = TL.nat_at(ct);
 
     // ---- prologue: every load issued before anything waits, block 0 and the state first, so
     // that block 0's work can start while block 1's keys and values are still arriving
@@ -83,123 +92,173 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_kernel(
     }
     bf16x8 kst1 = gload<bf16x8>(kr, TBYTES + tid * 16), vst1 = gload<bf16x8>(vr, TBYTES + tid * 16);
     issue_fence();
+    size_t tok0 = gtok0;  // first token of the current chunk
 
-    const uint32_t so = stage_off(tid);
-    // bf16 copy of S_b (row p, column c) and the split row of z_b, from the state accumulators
-    auto write_state = [&](int b) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            tstore_acc(STt + b * TBYTES, nat_c, pt[i], pack4(Sacc[i]));
-            if (ct == 0 && g == 0) {
-                bf16x2 hi, lo;
-                split_pair(zr[i][0], 0.f, hi, lo);
-                const int off = 2 * (16 * pt[i] + r);
-                *reinterpret_cast<bf16 *>(zrow + (2 * b) * 128 + off) = hi[0];
-                *reinterpret_cast<bf16 *>(zrow + (2 * b + 1) * 128 + off) = lo[0];
-            }
-        }
-    };
-    // State: S += K_b^T V_b as C[c][p] = sum_j V[j][c] K[j][p]; z += K_b^T 1
-    const bf16x8 ones = ones_frag<bf16>();
-    auto advance = [&](int b) {
-        bf16x8 vt[2], kt[2][2];
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            vt[kc] = tfrag_tr(Vt + b * TBYTES, tr_c, kc);
-#pragma unroll
-            for (int i = 0; i < 2; ++i) kt[kc][i] = tfrag_tr(Kt + b * TBYTES, tr_p[i], kc);
-        }
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                mma(Sacc[i], vt[kc], kt[kc][i]);
-                if (ct == 0) mma(zr[i], ones, kt[kc][i]);
-            }
-    };
-    // this wave's outputs for block B (its own block): scores P^T[j][t] (lane: query t = r,
-    // key j = 16 jt + 4g + i) masked to j <= t; their fp32 row sums; num^T[c][t] =
-    // sum_j V^T[c][j] P[t][j] (P split) + sum_p S_B^T[c][p] q_t[p]; den = row sums + z_B . q_t
-    auto outputs = [&](auto b_tag) {
-        constexpr int B = decltype(b_tag)::value;
-        const char *Kb = Kt + B * TBYTES, *Vb = Vt + B * TBYTES, *STb = STt + B * TBYTES, *zb = zrow + 2 * B * 128;
-        bf16x8 kf[4][2];
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) kf[jt][kc] = jt <= tq ? tfrag(Kb, TL, jt, kc) : qf[kc];
-        floatx4 sc[4];
-        float dsum = 0.f;
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            sc[jt] = zero4();
-            if (jt <= tq) {
-#pragma unroll
-                for (int kc = 0; kc < 2; ++kc) mma(sc[jt], kf[jt][kc], qf[kc]);
-                if (jt == tq) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sc[jt][e] = 4 * g + e <= r ? sc[jt][e] : 0.f;
-                }
-                dsum += (sc[jt][0] + sc[jt][1]) + (sc[jt][2] + sc[jt][3]);
-            }
-        }
-        floatx4 nm[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) nm[c] = zero4();
-#pragma unroll
-        for (int jc = 0; jc < 2; ++jc) {
-            if (2 * jc <= tq) {
-                bf16x8 vf[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) vf[c] = tfrag_tr(Vb, TL.tr[c], jc);
-                const Split8 pf = split_acc(sc[2 * jc], sc[2 * jc + 1]);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) mma_s(nm[c], vf[c], pf);
-            }
-        }
-        // inter-block terms against the state before this block (read before it is updated)
-        bf16x8 sf[2][4], zf[2][2];
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) sf[kc][c] = tfrag_tr(STb, TL.tr[c], kc);
-            zf[kc][0] = rowfrag(zb, lane, kc);
-            zf[kc][1] = rowfrag(zb + 128, lane, kc);
-        }
-        floatx4 dn = zero4();
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) mma(nm[c], sf[kc][c], qf[kc]);
-            mma(dn, zf[kc][0], qf[kc]);
-            mma(dn, zf[kc][1], qf[kc]);
-        }
-        const float inv = __builtin_amdgcn_rcpf(gsum(dsum) + dn[0]);
-        bf16 *orow = o + (tok0 + 64 * B + 16 * tq + r) * D + 4 * g;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) store_bf16x4(orow + 16 * c, pack4(nm[c] * inv));
-    };
     using Blk0 = std::integral_constant<int, 0>;
     using Blk1 = std::integral_constant<int, 1>;
 
-    // ---- phase A: block 0's keys and values, the S_0 copy and z_0 row
-    *reinterpret_cast<bf16x8 *>(Kt + so) = kst0;
-    *reinterpret_cast<bf16x8 *>(Vt + so) = vst0;
-    write_state(0);
-    lds_barrier();
+    for (int c = 0; c < n; ++c) {
+        // Lane-dependent offsets are derived afresh each chunk from an opaque copy of the
+        // thread index: hoisted out of the loop they would all stay live across it.
+        int tid_c = tid;
+        if (SEQ) asm volatile("" : "+v"(tid_c));
+        const int lane = tid_c & 63, r = lane & 15, g = lane >> 4;
+        const TileLanes TL(lane);
+        const uint32_t tr_c = TL.tr_at(ct), tr_p[2] = {TL.tr_at(pt0), TL.tr_at(pt0 + 2)}, nat_c = TL.nat_at(ct);
+        const uint32_t so = stage_off(tid_c);
+        // bf16 copy of S_b (row p, column c) and the split row of z_b, from the state accumulators
+        auto write_state = [&](int b) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                tstore_acc(STt + b * TBYTES, nat_c, pt[i], pack4(Sacc[i]));
+                if (ct == 0 && g == 0) {
+                    bf16x2 hi, lo;
+                    split_pair(zr[i][0], 0.f, hi, lo);
+                    const int off = 2 * (16 * pt[i] + r);
+                    *reinterpret_cast<bf16 *>(zrow + (2 * b) * 128 + off) = hi[0];
+                    *reinterpret_cast<bf16 *>(zrow + (2 * b + 1) * 128 + off) = lo[0];
+                }
+            }
+        };
+        // State: S += K_b^T V_b as C[c][p] = sum_j V[j][c] K[j][p]; z += K_b^T 1
+        const bf16x8 ones = ones_frag<bf16>();
+        auto advance = [&](int b) {
+            bf16x8 vt[2], kt[2][2];
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                vt[kc] = tfrag_tr(Vt + b * TBYTES, tr_c, kc);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) kt[kc][i] = tfrag_tr(Kt + b * TBYTES, tr_p[i], kc);
+            }
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    mma(Sacc[i], vt[kc], kt[kc][i]);
+                    if (ct == 0) mma(zr[i], ones, kt[kc][i]);
+                }
+        };
+        // this wave's outputs for block B (its own block), in two parts:
+        //   intra : scores P^T[j][t] (lane: query t = r, key j = 16 jt + 4g + i) masked to j <= t,
+        //           their fp32 row sums, and num^T[c][t] = sum_j V^T[c][j] P[t][j] (P split);
+        //   finish: num^T += sum_p S_B^T[c][p] q_t[p], den = row sums + z_B . q_t, o stored.
+        struct Part {
+            floatx4 nm[4];
+            float dsum;
+        };
+        auto intra = [&](auto b_tag, Part &pa) {
+            constexpr int B = decltype(b_tag)::value;
+            const char *Kb = Kt + B * TBYTES, *Vb = Vt + B * TBYTES;
+            bf16x8 kf[4][2];
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) kf[jt][kc] = jt <= tq ? tfrag(Kb, TL, jt, kc) : qf[kc];
+            floatx4 sc[4];
+            float dsum = 0.f;
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
+                sc[jt] = zero4();
+                if (jt <= tq) {
+#pragma unroll
+                    for (int kc = 0; kc < 2; ++kc) mma(sc[jt], kf[jt][kc], qf[kc]);
+                    if (jt == tq) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sc[jt][e] = 4 * g + e <= r ? sc[jt][e] : 0.f;
+                    }
+                    dsum += (sc[jt][0] + sc[jt][1]) + (sc[jt][2] + sc[jt][3]);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) pa.nm[c] = zero4();
+#pragma unroll
+            for (int jc = 0; jc < 2; ++jc) {
+                if (2 * jc <= tq) {
+                    bf16x8 vf[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) vf[c] = tfrag_tr(Vb, TL.tr[c], jc);
+                    const Split8 pf = split_acc(sc[2 * jc], sc[2 * jc + 1]);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) mma_s(pa.nm[c], vf[c], pf);
+                }
+            }
+            pa.dsum = dsum;
+        };
+        // inter-block terms against the state before this block (read before it is updated)
+        auto finish = [&](auto b_tag, Part &pa) {
+            constexpr int B = decltype(b_tag)::value;
+            const char *STb = STt + B * TBYTES, *zb = zrow + 2 * B * 128;
+            bf16x8 sf[2][4], zf[2][2];
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) sf[kc][c] = tfrag_tr(STb, TL.tr[c], kc);
+                zf[kc][0] = rowfrag(zb, lane, kc);
+                zf[kc][1] = rowfrag(zb + 128, lane, kc);
+            }
+            floatx4 dn = zero4();
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) mma(pa.nm[c], sf[kc][c], qf[kc]);
+                mma(dn, zf[kc][0], qf[kc]);
+                mma(dn, zf[kc][1], qf[kc]);
+            }
+            const float inv = __builtin_amdgcn_rcpf(gsum(pa.dsum) + dn[0]);
+            bf16 *orow = o + (tok0 + 64 * B + 16 * tq + r) * D + 4 * g;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) store_bf16x4<!SEQ>(orow + 16 * c, pack4(pa.nm[c] * inv));
+        };
+        auto outputs = [&](auto b_tag) {
+            Part pa;
+            intra(b_tag, pa);
+            finish(b_tag, pa);
+        };
+        // Sequence mode: the next chunk's operands are loaded while this chunk computes, each
+        // into its staging registers as soon as they are free (queries into spare ones).  The
+        // loads are unconditional: after the last chunk their offsets lie past the buffer
+        // range, which reads zeros without touching memory, and a load on every path lets
+        // the compiler count outstanding loads exactly instead of draining them all.
+        const uint32_t nb = (uint32_t)(c + 1) * CHUNK;
+        bf16x8 nq[2];
+        if (SEQ) {
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+                nq[kc] = ldfrag_g<bf16>(qr, (uint32_t)(c + 1) * C * D + (64 * blk + 16 * tq) * D + 32 * kc, D, lane);
+        }
 
-    // ---- phase B: S_1 (copy, z_1 row); block 0's outputs (their state S_0 is ready); then
-    // block 1's keys and values, by now arrived
-    advance(0);
-    write_state(1);
-    if (blk == 0) outputs(Blk0{});
-    *reinterpret_cast<bf16x8 *>(Kt + TBYTES + so) = kst1;
-    *reinterpret_cast<bf16x8 *>(Vt + TBYTES + so) = vst1;
-    lds_barrier();
+        // ---- phase A: block 0's keys and values, the S_0 copy and z_0 row
+        *reinterpret_cast<bf16x8 *>(Kt + so) = kst0;
+        *reinterpret_cast<bf16x8 *>(Vt + so) = vst0;
+        if (SEQ) {
+            kst0 = gload<bf16x8>(kr, nb + tid * 16);
+            vst0 = gload<bf16x8>(vr, nb + tid * 16);
+        }
+        write_state(0);
+        lds_barrier();
 
-    // ---- phase C: block 1's outputs; S_out = S_1 + K_1^T V_1
-    if (blk == 1) outputs(Blk1{});
-    advance(1);
+        // ---- phase B: S_1 (copy, z_1 row); block 0's outputs (their state S_0 is ready);
+        // then block 1's keys and values, by now arrived
+        advance(0);
+        write_state(1);
+        if (blk == 0) outputs(Blk0{});
+        *reinterpret_cast<bf16x8 *>(Kt + TBYTES + so) = kst1;
+        *reinterpret_cast<bf16x8 *>(Vt + TBYTES + so) = vst1;
+        if (SEQ) {
+            kst1 = gload<bf16x8>(kr, nb + TBYTES + tid * 16);
+            vst1 = gload<bf16x8>(vr, nb + TBYTES + tid * 16);
+        }
+        lds_barrier();
+
+        // ---- phase C: block 1's outputs; the state after the chunk, S_1 + K_1^T V_1
+        if (blk == 1) outputs(Blk1{});
+        advance(1);
+        if (SEQ) {
+            qf[0] = nq[0];
+            qf[1] = nq[1];
+            tok0 += C;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int p = 16 * pt[i] + r;
@@ -208,10 +267,34 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_kernel(
     }
 }
 
+__global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_in, const float *__restrict__ z_in,
+    bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out) {
+    fwd_c128_body<false>(q, k, v, S_in, z_in, o, S_out, z_out, 1);
+}
+
+// two workgroups per CU: one computes while the other waits at a barrier
+__global__ __launch_bounds__(NTHR, 2) void la_seq_fwd_c128_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_in, const float *__restrict__ z_in,
+    bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out, int nchunk) {
+    fwd_c128_body<true>(q, k, v, S_in, z_in, o, S_out, z_out, nchunk);
+}
+
 hipError_t launch_fwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
                            void *o, float *S_out, float *z_out, int G, hipStream_t stream, const hipEvent_t ev[2]) {
     hipExtLaunchKernelGGL(la_fwd_c128_kernel, dim3((unsigned)G), dim3(NTHR), 0, stream, ev[0], ev[1], 0,
                           (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_in, z_in, (bf16 *)o, S_out, z_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_seq_fwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
+                               void *o, float *S_out, float *z_out, int G, int nchunk, hipStream_t stream,
+                               const hipEvent_t ev[2]) {
+    hipExtLaunchKernelGGL(la_seq_fwd_c128_kernel, dim3((unsigned)G), dim3(NTHR), 0, stream, ev[0], ev[1], 0,
+                          (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_in, z_in, (bf16 *)o, S_out, z_out,
+                          nchunk);
     return hipGetLastError();
 }
 

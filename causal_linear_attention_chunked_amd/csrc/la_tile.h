@@ -116,14 +116,17 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Store of four bf16 outputs (8 bytes per lane; the four lanes of an accumulator row write
-// 32 contiguous bytes per instruction).  Non-temporal by default: on the headline shapes
-// they are faster than write-back stores, at the price of partial-sector writes (more HBM
-// write bytes than the tensor size); LA_BF16_NT_STORES=0 selects write-back stores.
+// 32 contiguous bytes per instruction).  Non-temporal (NT) or write-back.  A one-chunk
+// launch is faster with non-temporal stores, at the price of partial-sector writes (more
+// HBM write bytes than the tensor size); a workgroup that walks many chunks is much faster
+// with write-back stores, whose lines the L2 completes before they go out.
+// LA_BF16_NT_STORES=0 makes every store write-back.
 #ifndef LA_BF16_NT_STORES
 #define LA_BF16_NT_STORES 1
 #endif
+template <bool NT>
 __device__ __forceinline__ void store_bf16x4(bf16 *p, const bf16x4 &x) {
-    if (LA_BF16_NT_STORES) __builtin_nontemporal_store(x, reinterpret_cast<bf16x4 *>(p));
+    if (NT && LA_BF16_NT_STORES) __builtin_nontemporal_store(x, reinterpret_cast<bf16x4 *>(p));
     else *reinterpret_cast<bf16x4 *>(p) = x;
 }
 

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 2
+#define LA_ABI_VERSION 3
 #define LA_BWD_MAX_C 2048
 
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
@@ -104,6 +104,56 @@ la_status la_chunk_bwd(const void *q, const void *k, const void *v,
                        void *dq, void *dk, void *dv, float *dS_in, float *dz_in,
                        int G, int C, int D, int block, la_dtype dt, void *stream);
 
+/*
+ * Forward over a whole sequence: n = T / chunk consecutive chunks per group, in order,
+ * with the carry passed from each chunk to the next on chip (the carry across
+ * consecutive chunks of "Fractus-1B training optimization", section 2).  The result is
+ * that of n chained la_chunk_fwd calls over the chunks, but no carry between chunks
+ * goes through memory and the whole sequence is one launch.
+ *   q, k, v  : [G][T][D] dt, inputs; chunk c of a group is its tokens
+ *              c*chunk .. (c+1)*chunk - 1.
+ *   S_in     : [G][D][D] fp32 carry before the first chunk, or NULL (zero state).
+ *   z_in     : [G][D]    fp32, or NULL; NULL together with S_in.
+ *   o        : [G][T][D] dt, output.
+ *   S_out    : [G][D][D] fp32, state after the last chunk.
+ *   z_out    : [G][D]    fp32, normaliser after the last chunk.
+ * Supported: dt == LA_BF16, D == 64, chunk == 128, block == 64 and T a positive
+ * multiple of 128 below 2^24; anything else returns LA_ERR_UNSUPPORTED (chain
+ * la_chunk_fwd calls instead).
+ */
+la_status la_seq_fwd(const void *q, const void *k, const void *v,
+                     const float *S_in, const float *z_in,
+                     void *o, float *S_out, float *z_out,
+                     int G, int T, int D, int chunk, int block, la_dtype dt, void *stream);
+
+/*
+ * Backward over the same sequence for L = sum_t <dO_t, o_t> + <dS_out, S_out> +
+ * dz_out . z_out: the reverse scan from the last chunk to the first, with the reverse
+ * state passed on chip.
+ *   q, k, v  : [G][T][D] dt, the forward's inputs.
+ *   S_last   : [G][D][D] fp32, REQUIRED: the state after the last chunk, i.e. S_out of
+ *              the la_seq_fwd call on these inputs.
+ *   z_last   : [G][D]    fp32, REQUIRED: z_out of that call.
+ *              The forward state before each chunk is recovered from (S_last, z_last)
+ *              by subtracting the chunk's K^T V and K^T 1 (exact products of the
+ *              inputs, summed in fp32), so no per-chunk carries are kept between the
+ *              passes; the results differ from a chain of la_chunk_bwd calls only by
+ *              that fp32 rounding.  Passing anything but the forward's outputs gives
+ *              the gradient at a different initial carry.
+ *   dO       : [G][T][D] dt, gradient of o.
+ *   dS_out   : [G][D][D] fp32 gradient of S_out, or NULL.
+ *   dz_out   : [G][D]    fp32 gradient of z_out, or NULL; NULL together with dS_out.
+ *   dq,dk,dv : [G][T][D] dt, outputs.
+ *   dS_in    : [G][D][D] fp32 output, gradient of the carry before the first chunk.
+ *   dz_in    : [G][D]    fp32 output.
+ * Supported: as la_seq_fwd.
+ */
+la_status la_seq_bwd(const void *q, const void *k, const void *v,
+                     const float *S_last, const float *z_last,
+                     const void *dO, const float *dS_out, const float *dz_out,
+                     void *dq, void *dk, void *dv, float *dS_in, float *dz_in,
+                     int G, int T, int D, int chunk, int block, la_dtype dt, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *la_status_str(la_status s);
 
@@ -111,12 +161,12 @@ const char *la_status_str(la_status s);
 int la_abi_version(void);
 
 /*
- * Measurement hook for benchmarks and profilers: the next la_chunk_fwd or
- * la_chunk_bwd call made by the calling thread records start_event and
- * stop_event (hipEvent_t, created by the caller with timing enabled) on its
- * kernel dispatch itself, so hipEventElapsedTime(start, stop) is that kernel's
- * execution time with no marker packets in between.  Each of the two entry
- * points launches exactly one kernel.  The request is taken by that next call
+ * Measurement hook for benchmarks and profilers: the next la_chunk_fwd,
+ * la_chunk_bwd, la_seq_fwd or la_seq_bwd call made by the calling thread records
+ * start_event and stop_event (hipEvent_t, created by the caller with timing
+ * enabled) on its kernel dispatch itself, so hipEventElapsedTime(start, stop) is
+ * that kernel's execution time with no marker packets in between.  Each entry
+ * point launches exactly one kernel.  The request is taken by that next call
  * whatever its status; (NULL, NULL) clears it.  Returns LA_ERR_INVALID if only
  * one event is given.  The events are not validated: they must be live events
  * of the device the next call runs on.
@@ -131,6 +181,9 @@ la_status la_time_next_launch(void *start_event, void *stop_event);
  * supported.  Does not touch the device.
  */
 const char *la_kernel_name(int backward, la_dtype dt, int C, int D);
+
+/* The same for la_seq_fwd (backward = 0) and la_seq_bwd (backward = 1) at this chunk length. */
+const char *la_seq_kernel_name(int backward, la_dtype dt, int chunk, int D);
 
 #ifdef __cplusplus
 }

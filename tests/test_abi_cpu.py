@@ -33,7 +33,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["la_abi_version", "la_chunk_bwd", "la_chunk_fwd", "la_kernel_name",
-                                    "la_status_str", "la_time_next_launch"]
+                                    "la_seq_bwd", "la_seq_fwd", "la_seq_kernel_name", "la_status_str",
+                                    "la_time_next_launch"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -54,7 +55,7 @@ def test_kernel_names(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lac.abi_version() == 2
+    assert lac.abi_version() == 3
     for s in range(6):
         assert len(lac.status_str(s)) > 0
     assert lac.status_str(99) == "unknown status"
@@ -123,6 +124,53 @@ def test_fwd_chunk_beyond_32bit_offsets(lib):
     assert fwd_call(lib, G=1, C=(1 << 31) // (128 * 2), D=128) == UNSUPPORTED
     assert fwd_call(lib, G=1, C=(1 << 31) // (128 * 4) - 200, D=128, dt=0) == UNSUPPORTED
     assert bwd_call(lib, G=1, C=(1 << 31) // (64 * 2), D=64) == UNSUPPORTED
+
+
+def seq_fwd_call(lib, G=4, T=512, D=64, chunk=128, block=64, dt=1, **over):
+    args = {n: addr(i) for i, n in enumerate(["q", "k", "v", "S_in", "z_in", "o", "S_out", "z_out"])}
+    args.update(over)
+    return lib.la_seq_fwd(args["q"], args["k"], args["v"], args["S_in"], args["z_in"], args["o"],
+                          args["S_out"], args["z_out"], G, T, D, chunk, block, dt, None)
+
+
+def seq_bwd_call(lib, G=4, T=512, D=64, chunk=128, block=64, dt=1, **over):
+    names = ["q", "k", "v", "S_last", "z_last", "dO", "dS_out", "dz_out", "dq", "dk", "dv", "dS_in", "dz_in"]
+    args = {n: addr(i) for i, n in enumerate(names)}
+    args.update(over)
+    return lib.la_seq_bwd(*[args[n] for n in names], G, T, D, chunk, block, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(G=0), INVALID), (dict(T=0), INVALID), (dict(chunk=0), INVALID),
+    (dict(T=500), UNSUPPORTED),                          # not whole chunks
+    (dict(chunk=64, T=512), UNSUPPORTED), (dict(D=128), UNSUPPORTED), (dict(dt=0), UNSUPPORTED),
+    (dict(block=32), UNSUPPORTED), (dict(T=1 << 24), UNSUPPORTED),
+    (dict(q=None), INVALID), (dict(S_in=None), INVALID),
+    (dict(v=ctypes.c_void_p(BASE + 2 * STEP + 8)), ALIGN),
+    (dict(o=addr(1)), ALIAS), (dict(S_out=addr(3)), ALIAS),
+])
+def test_seq_fwd_rejects(lib, kw, status):
+    assert seq_fwd_call(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(G=0), INVALID), (dict(T=384 + 1), UNSUPPORTED), (dict(D=128), UNSUPPORTED),
+    (dict(S_last=None), INVALID), (dict(z_last=None), INVALID),   # the final carry is required
+    (dict(dS_out=None), INVALID),                        # dz_out without dS_out
+    (dict(dq=None), INVALID),
+    (dict(dk=ctypes.c_void_p(BASE + 9 * STEP + 4)), ALIGN),
+    (dict(dq=addr(5)), ALIAS), (dict(dS_in=addr(3)), ALIAS),
+])
+def test_seq_bwd_rejects(lib, kw, status):
+    assert seq_bwd_call(lib, **kw) == status
+
+
+def test_seq_kernel_names(lib):
+    assert lac.seq_kernel_name(False, "bf16", 128, 64) == "la_seq_fwd_c128_kernel"
+    assert lac.seq_kernel_name(True, "bf16", 128, 64) == "la_seq_bwd_c128w16_kernel"
+    assert lac.seq_kernel_name(True, "float32", 128, 64) is None
+    assert lac.seq_supported("bf16", 1024, 64, 128) and not lac.seq_supported("bf16", 1000, 64, 128)
+    assert not lac.seq_supported("float32", 1024, 64, 128) and not lac.seq_supported("bf16", 1024, 128, 128)
 
 
 def test_time_next_launch_pairs(lib):

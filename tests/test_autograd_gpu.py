@@ -59,3 +59,10 @@ def test_autograd_zero_carry_no_upstream(gpu):
 
 def test_autograd_wide_heads(gpu):
     _case("bf16", "prior", True, G=2, T=200, D=128, chunk=100)
+
+
+def test_autograd_sequence_entry_points(gpu):
+    # bf16, D = 64, whole 128-token chunks: one launch per direction through the sequence path
+    assert lac.seq_supported("bf16", 512, 64, 128)
+    _case("bf16", "prior", True, G=3, T=512)
+    _case("bf16", "zero", False, G=2, T=384)

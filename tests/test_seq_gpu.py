@@ -1,0 +1,121 @@
+"""GPU parity of the sequence entry points (la_seq_fwd / la_seq_bwd through the binding).
+
+Against the fp64 oracle (one call over the whole sequence is the chain of its chunks),
+to the tolerance of tests/tol.py; and against chained per-chunk calls: the forward
+must agree bit for bit (the same per-chunk arithmetic with the carry kept in
+registers), the backward to fp32 rounding (its forward states come from the final
+carry by subtraction).
+"""
+import numpy as np
+import pytest
+import torch
+
+import causal_linear_attention_chunked_amd as lac
+from causal_linear_attention_chunked_amd import inputs as inp
+import oracle
+from tol import RTOL, check
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev(x):
+    return None if x is None else x.to("cuda:0").contiguous()
+
+
+def upstream(G, D, seed):
+    rng = np.random.default_rng(seed)
+    return (torch.from_numpy(rng.standard_normal((G, D, D)).astype(np.float32)),
+            torch.from_numpy(rng.standard_normal((G, D)).astype(np.float32)))
+
+
+def run_seq(I, dS=None, dz=None):
+    q, k, v, dO = (dev(I[n]) for n in ("q", "k", "v", "dO"))
+    o, S_out, z_out = lac.seq_fwd(q, k, v, dev(I["S_in"]), dev(I["z_in"]))
+    dq, dk, dv, dS_in, dz_in = lac.seq_bwd(q, k, v, S_out, z_out, dO, dev(dS), dev(dz))
+    torch.cuda.synchronize()
+    return dict(o=o, S_out=S_out, z_out=z_out, dq=dq, dk=dk, dv=dv, dS_in=dS_in, dz_in=dz_in)
+
+
+def oracle_ref(I, dS=None, dz=None, groups=None):
+    sel = (lambda x: x) if groups is None else (lambda x: None if x is None else x[groups])
+    args = [sel(I[n]) for n in ("q", "k", "v", "S_in", "z_in")]
+    o, S_out, z_out = oracle.fwd(*args)
+    dq, dk, dv, dS_in, dz_in = oracle.bwd(*args, sel(I["dO"]), sel(dS), sel(dz))
+    return dict(o=o, S_out=S_out, z_out=z_out, dq=dq, dk=dk, dv=dv, dS_in=dS_in, dz_in=dz_in)
+
+
+def compare(res, ref, groups=None, label=""):
+    for name, r in ref.items():
+        g = res[name]
+        if groups is not None:
+            g = g[torch.as_tensor(groups, device=g.device)]
+        nw = check(f"{label}{name}", g, r, RTOL["bf16"])
+        say(f"  {label}{name}: normwise rel err {nw:.2e}")
+
+
+@pytest.mark.parametrize("G,nchunk,carry,up", [
+    (5, 5, "zero", False),
+    (3, 3, "prior", True),
+    (1, 1, "prior", False),
+    (2, 10, "zero", True),
+])
+def test_seq_against_oracle(gpu, G, nchunk, carry, up):
+    T = 128 * nchunk
+    say(f"[case] seq G={G} T={T} carry={carry} upstream={up}")
+    I = inp.make_inputs(G=G, T=T, D=64, dtype="bf16", carry=carry, backward=True, seed=7 + nchunk)
+    dS, dz = upstream(G, 64, 99) if up else (None, None)
+    compare(run_seq(I, dS, dz), oracle_ref(I, dS, dz))
+
+
+def test_seq_long_sequence(gpu):
+    # 64 chunks: the recovered forward states are 64 subtractions away from the final carry
+    G, T = 2, 128 * 64
+    say(f"[case] seq long G={G} T={T}")
+    I = inp.make_inputs(G=G, T=T, D=64, dtype="bf16", carry="prior", backward=True, seed=3)
+    dS, dz = upstream(G, 64, 5)
+    compare(run_seq(I, dS, dz), oracle_ref(I, dS, dz))
+
+
+def test_seq_eight_chunks_full_size(gpu):
+    # eight 128-token chunks at G = 1280, every group computed, a sample compared
+    w = inp.workload("g1280_8x128_d64_bf16_fwdbwd")
+    say(f"[case] seq full {w.name}")
+    I = inp.workload_inputs(w)
+    groups = [0, 1, 255, 256, 640, 1023, 1279]
+    compare(run_seq(I), oracle_ref(I, groups=groups), groups)
+
+
+def test_seq_matches_chained_calls(gpu):
+    G, n = 6, 4
+    T = 128 * n
+    say(f"[case] seq vs chain G={G} T={T}")
+    I = inp.make_inputs(G=G, T=T, D=64, dtype="bf16", carry="prior", backward=True, seed=21)
+    dS, dz = upstream(G, 64, 22)
+    res = run_seq(I, dS, dz)
+    bounds = inp.chunk_bounds([128] * n)
+    cut = lambda x: [dev(x)[:, a:b].contiguous() for a, b in bounds]
+    qc, kc, vc, gc = cut(I["q"]), cut(I["k"]), cut(I["v"]), cut(I["dO"])
+    outs, carries, (S_out, z_out) = lac.chain_fwd(qc, kc, vc, dev(I["S_in"]), dev(I["z_in"]))
+    dqs, dks, dvs, dS_in, dz_in = lac.chain_bwd(qc, kc, vc, carries, gc, dev(dS), dev(dz))
+    torch.cuda.synchronize()
+    # forward: bit for bit
+    assert torch.equal(res["o"], torch.cat(outs, 1))
+    assert torch.equal(res["S_out"], S_out) and torch.equal(res["z_out"], z_out)
+    # backward: within fp32 rounding of the recovered states (normwise)
+    for name, a, b in (("dq", res["dq"], torch.cat(dqs, 1)), ("dk", res["dk"], torch.cat(dks, 1)),
+                       ("dv", res["dv"], torch.cat(dvs, 1)), ("dS_in", res["dS_in"], dS_in),
+                       ("dz_in", res["dz_in"], dz_in)):
+        a, b = a.double(), b.double()
+        rel = float((a - b).norm() / b.norm())
+        say(f"  {name}: seq vs chain normwise {rel:.2e}")
+        assert rel < 2e-3, (name, rel)
+
+
+def test_seq_rejects_unsupported(gpu):
+    x = torch.ones(2, 200, 64, dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(lac.LachunkError, match="UNSUPPORTED"):
+        lac.seq_fwd(x, x, x)
