@@ -102,8 +102,9 @@ __device__ __forceinline__ void bwd_c128_body(
     const int u = w & 7, h = w >> 3;
     const int blk = u >> 2;
     const int tq = blk ? 3 - (u & 3) : (u & 3);
-    // state tile: value tile ct, key-feature tile pt
-    const int ct = w & 3, pt = w >> 2;
+    // state tile: value tile ct, key-feature tile pt.  The waves with ct = 0 also carry z and zh;
+    // rotating ct by pt puts one of them on each SIMD (wave w runs on SIMD w % 4).
+    const int pt = w >> 2, ct = (w + pt) & 3;
     const int grp = blockIdx.x;
     const int n = SEQ ? nchunk : 1;
     const size_t gtok0 = (size_t)grp * n * C;  // the group's n chunks, contiguous

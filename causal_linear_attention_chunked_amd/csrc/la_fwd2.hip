@@ -63,7 +63,9 @@ __device__ __forceinline__ void fwd_c128_body(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int blk = w >> 2;
     const int tq = blk ? 3 - (w & 3) : (w & 3);
-    const int ct = w & 3, pt0 = w >> 2;
+    // state tiles: value tile ct, key-feature tiles pt0 and pt0 + 2.  The waves with ct = 0 also
+    // carry z; rotating ct by pt0 puts them on different SIMDs (wave w runs on SIMD w % 4).
+    const int pt0 = w >> 2, ct = (w + pt0) & 3;
     const int grp = blockIdx.x;
     const int n = SEQ ? nchunk : 1;
     // the group's tokens: n chunks of C, contiguous ([G][n C][D])
