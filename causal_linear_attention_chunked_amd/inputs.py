@@ -99,17 +99,22 @@ def _feature(x: torch.Tensor) -> torch.Tensor:
 
 def make_inputs(G: int, T: int, D: int, dtype: str = "bf16", carry: str = "zero",
                 backward: bool = False, seed: int = 0, prior_len: int = 128,
-                groups: Optional[List[int]] = None) -> dict:
+                groups: Optional[List[int]] = None, features: str = "mapped") -> dict:
     """Draw one workload's tensors on the CPU.
 
     Returns a dict with ``q, k, v`` of shape (G, T, D) in the workload dtype,
     ``S_in`` (G, D, D) and ``z_in`` (G, D) in fp32 or ``None`` for a zero carry,
     and ``dO`` (G, T, D) for a backward workload.  ``groups`` keeps only the
     listed group rows after drawing the full tensors, so a sampled group holds
-    exactly the values it holds in the full-size draw.
+    exactly the values it holds in the full-size draw.  ``features="raw"`` leaves
+    q and k as the normal draws (rounded to the dtype) for an op that applies
+    elu(x) + 1 itself; the prior chunk's keys are mapped either way.
     """
     if carry not in ("zero", "prior"):
         raise ValueError(f"unknown carry recipe {carry!r}")
+    if features not in ("mapped", "raw"):
+        raise ValueError(f"unknown features option {features!r}")
+    fmap = _feature if features == "mapped" else (lambda x: x)
     gen = torch.Generator(device="cpu")
     gen.manual_seed(seed)
     tdt = _torch_dtype(dtype)
@@ -121,8 +126,8 @@ def make_inputs(G: int, T: int, D: int, dtype: str = "bf16", carry: str = "zero"
     if carry == "prior":
         kp = _feature(draw(prior_len)).to(tdt)
         vp = draw(prior_len).to(tdt)
-    q = _feature(draw(T)).to(tdt)
-    k = _feature(draw(T)).to(tdt)
+    q = fmap(draw(T)).to(tdt)
+    k = fmap(draw(T)).to(tdt)
     v = draw(T).to(tdt)
     dO = draw(T).to(tdt) if backward else None
 

@@ -11,8 +11,11 @@ no code with the GPU library and never imports it.
   matrix backward.
 * :mod:`oracle.exact`  -- exact rational brute force (fractions + dual numbers)
   for tiny shapes; writes the stored golden values.
+* :mod:`oracle.features` -- the positive feature map elu(x) + 1 in front of the op
+  (raw inputs in, gradients with respect to them out), by the chain rule.
 
 Every function cites the passage of "Fractus-1B training optimization" it
 follows.  Which pins cover which function is listed in the test suite.
 """
 from .core import build, fwd, bwd, lib_path, max_threads  # noqa: F401
+from . import features  # noqa: F401

@@ -20,6 +20,10 @@ to something independent of that code:
   P12      masked-einsum form (section 1) == oracle                     -> the oracle itself
   P13      central finite differences (fp64)                            -> all gradients
   matrix   whole-chunk matrix backward == reverse scan                  -> all gradients
+  F1       phi = elu + 1 at closed-form points; continuous at 0        -> oracle.features.elu1
+  F2       phi' against central differences of phi                     -> oracle.features.elu1_grad
+  F3       fused-map gradients against central differences of the
+           loss in the raw inputs (both signs of x)                    -> oracle.features.bwd
 """
 import json
 import os
@@ -244,6 +248,53 @@ def test_p13_finite_differences():
             assert abs(fd - g[idx]) <= 1e-6 * (1 + abs(g[idx])), (ai, idx, fd, g[idx])
 
 
+def test_f1_feature_map_closed_forms():
+    from oracle import features
+    x = np.array([0.0, 2.0, 0.5, -1.0, -30.0, 1e-12, -1e-12])
+    want = np.array([1.0, 3.0, 1.5, np.exp(-1.0), np.exp(-30.0), 1.0 + 1e-12, np.exp(-1e-12)])
+    np.testing.assert_allclose(features.elu1(x), want, rtol=1e-15, atol=0)
+    assert np.all(features.elu1(np.linspace(-20, 20, 1001)) > 0)
+    np.testing.assert_array_equal(features.elu1_grad(np.array([3.0, 1e-9])), [1.0, 1.0])
+    np.testing.assert_allclose(features.elu1_grad(np.array([-2.0, 0.0])), [np.exp(-2.0), 1.0], rtol=1e-15)
+
+
+def test_f2_feature_map_derivative():
+    from oracle import features
+    x = np.array([-4.0, -1.3, -0.2, 0.3, 1.7, 5.0])
+    h = 1e-6
+    fd = (features.elu1(x + h) - features.elu1(x - h)) / (2 * h)
+    np.testing.assert_allclose(features.elu1_grad(x), fd, rtol=1e-8)
+
+
+def test_f3_fused_map_gradients():
+    from oracle import features
+    G, T, D = 2, 9, 3
+    r = np.random.default_rng(31)
+    xq, xk = r.normal(size=(G, T, D)), r.normal(size=(G, T, D))   # both signs
+    _, _, v, S_in, z_in, dO, dS, dz = rng_inputs(G, T, D, seed=32)
+    grads = features.bwd(xq, xk, v, S_in, z_in, dO, dS, dz)
+
+    def L(xq_, xk_, v_, S_, z_):
+        o, So, zo = features.fwd(xq_, xk_, v_, S_, z_)
+        return (dO * o).sum() + (dS * So).sum() + (dz * zo).sum()
+
+    args = [xq, xk, v, S_in, z_in]
+    h = 1e-6
+    for ai, g in enumerate(grads):
+        x = args[ai]
+        for _ in range(10):
+            idx = tuple(int(r.integers(0, n)) for n in x.shape)
+            if ai < 2 and abs(x[idx]) < 10 * h:
+                continue  # the map has a kink at 0
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap, am = list(args), list(args)
+            ap[ai], am[ai] = xp, xm
+            fd = (L(*ap) - L(*am)) / (2 * h)
+            assert abs(fd - g[idx]) <= 1e-6 * (1 + abs(g[idx])), (ai, idx, fd, g[idx])
+
+
 def test_denominator_guard():
     q, k, v, *_ = rng_inputs(1, 4, 2, seed=13, carry=False)
     q[0, 2] = -q[0, 2]
@@ -278,3 +329,16 @@ def test_workload_table():
     assert w.T == 63 * 128 + 100 and w.chunks[-1] == 100 and w.D == 128
     assert inputs.workload("g1280_8x128_d64_bf16_fwdbwd").T == 1024
     assert inputs.workload("g160_c128_d64_bf16_fwdbwd").G == 160
+
+
+def test_raw_feature_inputs():
+    # raw draws: the mapped inputs are exactly elu(x)+1 of them (before rounding), same draw order
+    a = inputs.make_inputs(G=2, T=16, D=8, dtype="f32", carry="prior", backward=True, seed=4, prior_len=8)
+    b = inputs.make_inputs(G=2, T=16, D=8, dtype="f32", carry="prior", backward=True, seed=4, prior_len=8,
+                           features="raw")
+    from oracle import features
+    np.testing.assert_allclose(features.elu1(b["q"]), a["q"].numpy(), rtol=2e-7)
+    np.testing.assert_allclose(features.elu1(b["k"]), a["k"].numpy(), rtol=2e-7)
+    for key in ("v", "dO", "S_in", "z_in"):
+        assert np.array_equal(a[key].numpy(), b[key].numpy())
+    assert (b["q"] < 0).any() and (b["q"] > 0).any()
