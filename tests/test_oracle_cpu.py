@@ -332,13 +332,14 @@ def test_workload_table():
 
 
 def test_raw_feature_inputs():
-    # raw draws: the mapped inputs are exactly elu(x)+1 of them (before rounding), same draw order
+    # raw draws: the mapped inputs are elu(x)+1 of them, same draw order.  The mapped ones are
+    # computed in fp32 as (e^x - 1) + 1, whose last addition rounds to 2^-24 absolute.
     a = inputs.make_inputs(G=2, T=16, D=8, dtype="f32", carry="prior", backward=True, seed=4, prior_len=8)
     b = inputs.make_inputs(G=2, T=16, D=8, dtype="f32", carry="prior", backward=True, seed=4, prior_len=8,
                            features="raw")
     from oracle import features
-    np.testing.assert_allclose(features.elu1(b["q"]), a["q"].numpy(), rtol=2e-7)
-    np.testing.assert_allclose(features.elu1(b["k"]), a["k"].numpy(), rtol=2e-7)
+    np.testing.assert_allclose(features.elu1(b["q"]), a["q"].numpy(), rtol=2e-7, atol=1.2e-7)
+    np.testing.assert_allclose(features.elu1(b["k"]), a["k"].numpy(), rtol=2e-7, atol=1.2e-7)
     for key in ("v", "dO", "S_in", "z_in"):
         assert np.array_equal(a[key].numpy(), b[key].numpy())
     assert (b["q"] < 0).any() and (b["q"] > 0).any()
