@@ -24,6 +24,8 @@ to something independent of that code:
   F2       phi' against central differences of phi                     -> oracle.features.elu1_grad
   F3       fused-map gradients against central differences of the
            loss in the raw inputs (both signs of x)                    -> oracle.features.bwd
+  F4       rounding of the mapped features: round to nearest even at
+           bf16 halfway points; the rounded op is the plain op on them -> oracle.features.mapped
 """
 import json
 import os
@@ -293,6 +295,22 @@ def test_f3_fused_map_gradients():
             ap[ai], am[ai] = xp, xm
             fd = (L(*ap) - L(*am)) / (2 * h)
             assert abs(fd - g[idx]) <= 1e-6 * (1 + abs(g[idx])), (ai, idx, fd, g[idx])
+
+
+def test_f4_feature_rounding():
+    from oracle import features
+    # x > 0 maps to x + 1: 1 + 2^-8 is halfway between bf16 neighbours 1 and 1 + 2^-7 -> even (1.0);
+    # 1 + 3 * 2^-8 is halfway between 1 + 2^-7 and 1 + 2^-6 -> even (1 + 2^-6)
+    x = np.array([2.0 ** -8, 3 * 2.0 ** -8, 0.5])
+    np.testing.assert_array_equal(features.mapped(x, "bf16"), [1.0, 1.0 + 2.0 ** -6, 1.5])
+    np.testing.assert_array_equal(features.mapped(np.array([-1.0]), "f32"), [np.float32(np.exp(-1.0))])
+    r = np.random.default_rng(5)
+    xq, xk = r.normal(size=(1, 6, 3)), r.normal(size=(1, 6, 3))
+    v = r.normal(size=(1, 6, 3))
+    got = features.fwd(xq, xk, v, dtype="bf16")
+    want = oracle.fwd(features.mapped(xq, "bf16"), features.mapped(xk, "bf16"), v)
+    for a, b in zip(got, want):
+        np.testing.assert_array_equal(a, b)
 
 
 def test_denominator_guard():
