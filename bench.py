@@ -147,10 +147,15 @@ def counters_summary(d, workload, kernels):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(I, w, min_seconds=10.0, mac_budget=2e9):
+def cpu_baseline(I, w, min_seconds=10.0, mac_budget=2e9, feature=None):
     """The fp64 oracle as it stands, on this host's cores, over the workload's first groups
     (all of them when the workload is small), repeated; one call covers all the chunks."""
     import oracle
+    if feature == "elu1":
+        ofwd = lambda *a, nthreads: oracle.features.fwd(*a, dtype=w.dtype, nthreads=nthreads)
+        obwd = lambda *a, nthreads: oracle.features.bwd(*a, dtype=w.dtype, nthreads=nthreads)
+    else:
+        ofwd, obwd = oracle.fwd, oracle.bwd
     per_group = w.T * w.D * w.D
     g = w.G if w.G * per_group <= mac_budget else max(1, int(mac_budget // per_group))
     threads = min(os.cpu_count() or 1, g)
@@ -161,8 +166,8 @@ def cpu_baseline(I, w, min_seconds=10.0, mac_budget=2e9):
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        oracle.fwd(*args, nthreads=threads)
-        oracle.bwd(*args, dO, nthreads=threads)
+        ofwd(*args, nthreads=threads)
+        obwd(*args, dO, nthreads=threads)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start >= min_seconds and len(times) >= 3:
             break
@@ -196,6 +201,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seq", action="store_true",
                     help="run the workload through the sequence entry points (one launch per direction)")
+    ap.add_argument("--feature", choices=["elu1"], default=None,
+                    help="with --seq: raw q, k in, the feature map elu(x)+1 fused into the kernels")
     ap.add_argument("--footprint-mb", type=float, default=640.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only plain 256 MiB device-to-device copies (HBM counter calibration)")
@@ -213,8 +220,10 @@ def main():
         from causal_linear_attention_chunked_amd import inputs as inp
         w = inp.workload(args.workload)
         names = {lac.kernel_name(b, w.dtype, C, w.D) for b in (False, True) for C in set(w.chunks)}
-        names |= {lac.seq_kernel_name(b, w.dtype, max(w.chunks), w.D) for b in (False, True)} - {None}
-        counters_summary(args.counters_summary, w.name + ("_seq" if args.seq else ""), sorted(names))
+        names |= {lac.seq_kernel_name(b, w.dtype, max(w.chunks), w.D, f) for b in (False, True)
+                  for f in (None, "elu1")} - {None}
+        counters_summary(args.counters_summary, w.name + ("_seq" if args.seq else "")
+                         + (f"_{args.feature}" if args.feature else ""), sorted(names))
         return
     import torch
     if args.copy_calibration:
@@ -227,7 +236,10 @@ def main():
     w = inp.workload(args.workload)
     if not w.backward:
         raise SystemExit("bench.py times forward+backward workloads")
-    I = inp.workload_inputs(w)
+    if args.feature and not args.seq:
+        raise SystemExit("--feature runs through the sequence entry points: add --seq")
+    I = inp.make_inputs(G=w.G, T=w.T, D=w.D, dtype=w.dtype, carry=w.carry, backward=w.backward, seed=w.seed,
+                        prior_len=w.prior_len, features="raw" if args.feature else "mapped")
     dev = torch.device("cuda:0")
     esz = 2 if w.dtype == "bf16" else 4
     G, D = w.G, w.D
@@ -235,7 +247,7 @@ def main():
     n = len(bounds)
     carry = I["S_in"] is not None
 
-    tname = w.name + ("_seq" if args.seq else "")  # names the traffic record too
+    tname = w.name + ("_seq" if args.seq else "") + (f"_{args.feature}" if args.feature else "")  # and the traffic file
     if args.seq:
         if not lac.seq_supported(w.dtype, w.T, D, max(w.chunks)) or len(set(w.chunks)) != 1:
             raise SystemExit(f"{w.name}: the sequence entry points do not take this workload")
@@ -280,11 +292,12 @@ def main():
     def launch(s, kind, i):
         if kind == "seqfwd":
             x = s["seq"]
-            lac.seq_fwd(x["q"], x["k"], x["v"], s["S_in"], s["z_in"], out=x["fout"])
+            lac.seq_fwd(x["q"], x["k"], x["v"], s["S_in"], s["z_in"], out=x["fout"], feature=args.feature)
             return
         if kind == "seqbwd":
             x = s["seq"]
-            lac.seq_bwd(x["q"], x["k"], x["v"], x["fout"][1], x["fout"][2], x["dO"], out=x["bout"])
+            lac.seq_bwd(x["q"], x["k"], x["v"], x["fout"][1], x["fout"][2], x["dO"], out=x["bout"],
+                        feature=args.feature)
             return
         c = s["chunks"][i]
         S, z = carry_in(s, i)
@@ -332,7 +345,8 @@ def main():
     per = {}
     for i in range(K):
         for (kind, C, b, _), e in zip(launches, ev[i]):
-            name = (lac.seq_kernel_name(kind == "seqbwd", w.dtype, max(w.chunks), D) if kind.startswith("seq")
+            name = (lac.seq_kernel_name(kind == "seqbwd", w.dtype, max(w.chunks), D, args.feature)
+                    if kind.startswith("seq")
                     else lac.kernel_name(kind == "bwd", w.dtype, C, D))
             p = per.setdefault(name, {"launches": 0, "bytes": 0, "ms": 0.0})
             p["launches"] += 1
@@ -357,6 +371,7 @@ def main():
                    "block": w.block, "carry": w.carry, "launches_per_step": len(launches),
                    "buffer_sets": nsets, "footprint_mb": round(nsets * set_bytes / 1e6, 1),
                    "entry_points": "la_seq_fwd/la_seq_bwd" if args.seq else "la_chunk_fwd/la_chunk_bwd",
+                   "feature_map": args.feature or "applied by the caller",
                    "graph_captured": False, "host_enqueue_us_per_step": host_s * 1e6 / K,
                    "kernel_timing": "HIP events recorded on each kernel dispatch, separate timed loop"},
         "roofline": {"bound": "hbm", "kernel": top, "achieved": kt["GB/s"], "peak": HBM_PEAK_GBS,
@@ -366,7 +381,7 @@ def main():
         "step_roofline_frac": set_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(I, w)
+        out["cpu_baseline"] = cpu_baseline(I, w, feature=args.feature)
     print(json.dumps(out), flush=True)
 
 if __name__ == "__main__":

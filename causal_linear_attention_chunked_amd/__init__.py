@@ -71,11 +71,11 @@ def load_library():
         lib.la_kernel_name.restype = ctypes.c_char_p
         lib.la_kernel_name.argtypes = [i, i, i, i]
         lib.la_seq_fwd.restype = i
-        lib.la_seq_fwd.argtypes = [vp] * 8 + [i] * 6 + [vp]
+        lib.la_seq_fwd.argtypes = [vp] * 8 + [i] * 7 + [vp]
         lib.la_seq_bwd.restype = i
-        lib.la_seq_bwd.argtypes = [vp] * 13 + [i] * 6 + [vp]
+        lib.la_seq_bwd.argtypes = [vp] * 13 + [i] * 7 + [vp]
         lib.la_seq_kernel_name.restype = ctypes.c_char_p
-        lib.la_seq_kernel_name.argtypes = [i, i, i, i]
+        lib.la_seq_kernel_name.argtypes = [i, i, i, i, i]
         _lib = lib
         return lib
 
@@ -99,9 +99,20 @@ def kernel_name(backward: bool, dtype, C: int, D: int):
     return None if name is None else name.decode()
 
 
-def seq_kernel_name(backward: bool, dtype, chunk: int, D: int):
-    """Name of the kernel seq_fwd / seq_bwd launch for this element type, chunk length and D."""
-    name = load_library().la_seq_kernel_name(int(bool(backward)), _dt_code(dtype), int(chunk), int(D))
+FEATURES = {None: 0, "none": 0, "elu1": 1}
+
+
+def _feature_code(feature):
+    if feature not in FEATURES:
+        raise ValueError(f"unknown feature map {feature!r}; use None or 'elu1'")
+    return FEATURES[feature]
+
+
+def seq_kernel_name(backward: bool, dtype, chunk: int, D: int, feature=None):
+    """Name of the kernel seq_fwd / seq_bwd launch for this element type, chunk length, D and
+    feature map."""
+    name = load_library().la_seq_kernel_name(int(bool(backward)), _dt_code(dtype), int(chunk), int(D),
+                                             _feature_code(feature))
     return None if name is None else name.decode()
 
 
@@ -226,9 +237,10 @@ def bwd(q, k, v, S_in, z_in, dO, dS_out=None, dz_out=None, block: int = 64, out=
     return dq, dk, dv, dS_in, dz_in
 
 
-def seq_fwd(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int = 64, out=None):
+def seq_fwd(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int = 64, out=None, feature=None):
     """Forward over a whole (G, T, D) sequence of chunks in one launch, carry on chip:
-    returns (o, S_out, z_out), equal to chaining fwd over the chunks."""
+    returns (o, S_out, z_out), equal to chaining fwd over the chunks.  ``feature="elu1"``
+    takes raw q, k and applies elu(x) + 1 inside."""
     lib = _lib or load_library()
     G, T, D, dev = _validate_tokens(("q", "k", "v"), (q, k, v))
     if (S_in is None) != (z_in is None):
@@ -244,14 +256,16 @@ def seq_fwd(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int = 64, ou
         o, S_out, z_out = out
     _check("la_seq_fwd", lib.la_seq_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(S_in), _ptr(z_in),
                                         o.data_ptr(), S_out.data_ptr(), z_out.data_ptr(), G, T, D, int(chunk),
-                                        int(block), _dtype_code(q), _stream(dev)))
+                                        int(block), _feature_code(feature), _dtype_code(q), _stream(dev)))
     return o, S_out, z_out
 
 
-def seq_bwd(q, k, v, S_last, z_last, dO, dS_out=None, dz_out=None, chunk: int = 128, block: int = 64, out=None):
+def seq_bwd(q, k, v, S_last, z_last, dO, dS_out=None, dz_out=None, chunk: int = 128, block: int = 64, out=None,
+            feature=None):
     """Backward over a whole sequence in one launch, last chunk first, reverse state on chip.
     (S_last, z_last) is the carry after the last chunk: seq_fwd's (S_out, z_out).
-    Returns (dq, dk, dv, dS_in, dz_in)."""
+    Returns (dq, dk, dv, dS_in, dz_in); with ``feature="elu1"`` dq and dk are the gradients
+    of the raw inputs."""
     lib = _lib or load_library()
     G, T, D, dev = _validate_tokens(("q", "k", "v", "dO"), (q, k, v, dO))
     if S_last is None or z_last is None:
@@ -272,8 +286,8 @@ def seq_bwd(q, k, v, S_last, z_last, dO, dS_out=None, dz_out=None, chunk: int = 
     _check("la_seq_bwd", lib.la_seq_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), S_last.data_ptr(),
                                         z_last.data_ptr(), dO.data_ptr(), _ptr(dS_out), _ptr(dz_out),
                                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dS_in.data_ptr(),
-                                        dz_in.data_ptr(), G, T, D, int(chunk), int(block), _dtype_code(q),
-                                        _stream(dev)))
+                                        dz_in.data_ptr(), G, T, D, int(chunk), int(block), _feature_code(feature),
+                                        _dtype_code(q), _stream(dev)))
     return dq, dk, dv, dS_in, dz_in
 
 

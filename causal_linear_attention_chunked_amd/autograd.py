@@ -67,10 +67,10 @@ class SeqFunction(torch.autograd.Function):
     state before each chunk."""
 
     @staticmethod
-    def forward(ctx, q, k, v, S_in, z_in, chunk, block):
+    def forward(ctx, q, k, v, S_in, z_in, chunk, block, feature):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o, S_out, z_out = _seq_fwd(q, k, v, S_in, z_in, chunk, block)
-        ctx.chunk, ctx.block = chunk, block
+        o, S_out, z_out = _seq_fwd(q, k, v, S_in, z_in, chunk, block, feature=feature)
+        ctx.chunk, ctx.block, ctx.feature = chunk, block, feature
         ctx.has_carry = S_in is not None
         ctx.save_for_backward(q, k, v, S_out, z_out)
         return o, S_out, z_out
@@ -88,10 +88,10 @@ class SeqFunction(torch.autograd.Function):
         dS_out = None if dS_out is None else dS_out.float().contiguous()
         dz_out = None if dz_out is None else dz_out.float().contiguous()
         dq, dk, dv, dS_in, dz_in = _seq_bwd(q, k, v, S_out, z_out, do.to(q.dtype).contiguous(), dS_out, dz_out,
-                                            ctx.chunk, ctx.block)
+                                            ctx.chunk, ctx.block, feature=ctx.feature)
         if not ctx.has_carry:
             dS_in = dz_in = None
-        return dq, dk, dv, dS_in, dz_in, None, None
+        return dq, dk, dv, dS_in, dz_in, None, None, None
 
 
 def chunk_attention(q, k, v, S_in=None, z_in=None, block: int = 64):
@@ -100,9 +100,12 @@ def chunk_attention(q, k, v, S_in=None, z_in=None, block: int = 64):
     return ChunkFunction.apply(q, k, v, S_in, z_in, block)
 
 
-def linear_attention(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int = 64):
+def linear_attention(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int = 64, feature_map=None):
     """Causal linear attention over a (G, T, D) sequence in chunks of ``chunk`` tokens
-    (the last one ragged), carrying (S, z) across chunks.  Returns (o, (S_out, z_out))."""
+    (the last one ragged), carrying (S, z) across chunks.  Returns (o, (S_out, z_out)).
+    ``feature_map="elu1"``: q and k are raw inputs and elu(x) + 1 is applied inside the
+    kernels (fused; the shapes of the sequence path only), gradients flowing to the raw
+    inputs."""
     _check_device(q)
     if q.dim() != 3:
         raise ValueError(f"q must be (G, T, D), got {tuple(q.shape)}")
@@ -111,8 +114,15 @@ def linear_attention(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int
     T = q.shape[1]
     if T == 0:
         return q.new_empty(q.shape), (S_in, z_in)
-    if _seq_supported(q.dtype, T, q.shape[2], chunk) and block == 64:
-        o, S, z = SeqFunction.apply(q, k, v, S_in, z_in, chunk, block)
+    seq_ok = _seq_supported(q.dtype, T, q.shape[2], chunk) and block == 64
+    if feature_map not in (None, "none"):
+        if not seq_ok:
+            raise ValueError(f"the fused feature map {feature_map!r} runs in the sequence kernels only "
+                             "(bf16, D = 64, whole 128-token chunks)")
+        o, S, z = SeqFunction.apply(q, k, v, S_in, z_in, chunk, block, feature_map)
+        return o, (S, z)
+    if seq_ok:
+        o, S, z = SeqFunction.apply(q, k, v, S_in, z_in, chunk, block, None)
         return o, (S, z)
     outs = []
     S, z = S_in, z_in

@@ -156,10 +156,11 @@ la_status la_chunk_bwd(const void *q, const void *k, const void *v, const float 
 }
 
 la_status la_seq_fwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in, void *o,
-                     float *S_out, float *z_out, int G, int T, int D, int chunk, int block, la_dtype dt,
-                     void *stream) {
+                     float *S_out, float *z_out, int G, int T, int D, int chunk, int block, la_feature feature,
+                     la_dtype dt, void *stream) {
     const TakenEvents te;
     Sizes sz;
+    if (feature != LA_FEATURE_NONE && feature != LA_FEATURE_ELU1) return LA_ERR_INVALID;
     la_status st = seq_checks(G, T, D, chunk, block, dt, &sz);
     if (st != LA_OK) return st;
     if (!q || !k || !v || !o || !S_out || !z_out) return LA_ERR_INVALID;
@@ -172,16 +173,18 @@ la_status la_seq_fwd(const void *q, const void *k, const void *v, const float *S
     st = alias_checks(in, 5, out, 3);
     if (st != LA_OK) return st;
     const hipError_t e = lachunk::launch_seq_fwd_c128(q, k, v, S_in, z_in, o, S_out, z_out, G, T / chunk,
+                                                      feature == LA_FEATURE_ELU1,
                                                       reinterpret_cast<hipStream_t>(stream), te.ev);
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
 la_status la_seq_bwd(const void *q, const void *k, const void *v, const float *S_last, const float *z_last,
                      const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
-                     float *dS_in, float *dz_in, int G, int T, int D, int chunk, int block, la_dtype dt,
-                     void *stream) {
+                     float *dS_in, float *dz_in, int G, int T, int D, int chunk, int block, la_feature feature,
+                     la_dtype dt, void *stream) {
     const TakenEvents te;
     Sizes sz;
+    if (feature != LA_FEATURE_NONE && feature != LA_FEATURE_ELU1) return LA_ERR_INVALID;
     la_status st = seq_checks(G, T, D, chunk, block, dt, &sz);
     if (st != LA_OK) return st;
     if (!q || !k || !v || !S_last || !z_last || !dO || !dq || !dk || !dv || !dS_in || !dz_in) return LA_ERR_INVALID;
@@ -197,7 +200,8 @@ la_status la_seq_bwd(const void *q, const void *k, const void *v, const float *S
     if (st != LA_OK) return st;
     const hipError_t e =
         lachunk::launch_seq_bwd_c128(q, k, v, S_last, z_last, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, G,
-                                     T / chunk, reinterpret_cast<hipStream_t>(stream), te.ev);
+                                     T / chunk, feature == LA_FEATURE_ELU1, reinterpret_cast<hipStream_t>(stream),
+                                     te.ev);
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
@@ -223,8 +227,10 @@ const char *la_kernel_name(int backward, la_dtype dt, int C, int D) {
     return c128 ? "la_bwd_c128w16_kernel" : "la_bwd_kernel";
 }
 
-const char *la_seq_kernel_name(int backward, la_dtype dt, int chunk, int D) {
+const char *la_seq_kernel_name(int backward, la_dtype dt, int chunk, int D, la_feature feature) {
     if (dt != LA_BF16 || D != 64 || chunk != 128) return nullptr;
+    if (feature == LA_FEATURE_ELU1) return backward ? "la_seq_bwd_c128w16_elu1_kernel" : "la_seq_fwd_c128_elu1_kernel";
+    if (feature != LA_FEATURE_NONE) return nullptr;
     return backward ? "la_seq_bwd_c128w16_kernel" : "la_seq_fwd_c128_kernel";
 }
 

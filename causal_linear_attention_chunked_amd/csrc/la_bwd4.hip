@@ -77,7 +77,7 @@ __device__ __forceinline__ bf16x8 neg8(const bf16x8 &x) {
 }
 
 // S_in, z_in: the carry before the chunk (single chunk) or after the last chunk (SEQ).
-template <bool SEQ>
+template <bool SEQ, bool FM>
 __device__ __forceinline__ void bwd_c128_body(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ S_in, const float *__restrict__ z_in, const bf16 *__restrict__ dO,
@@ -158,8 +158,9 @@ __device__ __forceinline__ void bwd_c128_body(
         // ---- phase 0
         {
             const uint32_t so = sb * TBYTES + stage_off(tid_c & 511);
-            *reinterpret_cast<bf16x8 *>(smem + L::QT + so) = st[0];
-            *reinterpret_cast<bf16x8 *>(smem + L::KT + so) = st[1];
+            // fused feature map: raw queries and keys are mapped as they are staged
+            *reinterpret_cast<bf16x8 *>(smem + L::QT + so) = FM ? elu1_8(st[0]) : st[0];
+            *reinterpret_cast<bf16x8 *>(smem + L::KT + so) = FM ? elu1_8(st[1]) : st[1];
             *reinterpret_cast<bf16x8 *>(smem + L::VT + so) = st[2];
             *reinterpret_cast<bf16x8 *>(smem + L::GT + so) = st[3];
         }
@@ -353,6 +354,8 @@ __device__ __forceinline__ void bwd_c128_body(
                     mma(acc, ktr[pp][jc], dph[jc]);
                     mma(acc, ktr[pp][jc], dpl[jc]);
                 }
+                // fused feature map: the gradient of the raw query is dq phi'(x), phi' = min(1, phi)
+                if constexpr (FM) acc *= elu1_grad4(lds_b64(tile(L::QT, blk) + tq * 16 * TROW + TL.nat_at(2 * h + pp)));
                 store_bf16x4<!SEQ>(dqrow + 16 * (2 * h + pp), pack4(acc));
             }
         }
@@ -436,7 +439,10 @@ __device__ __forceinline__ void bwd_c128_body(
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
                     floatx4 y = acc[x];
-                    if constexpr (DK) y += *reinterpret_cast<const floatx4 *>(zh + 64 * B + 16 * x + 4 * g);
+                    if constexpr (DK) {
+                        y += *reinterpret_cast<const floatx4 *>(zh + 64 * B + 16 * x + 4 * g);
+                        if constexpr (FM) y *= elu1_grad4(lds_b64(tile(L::KT, B) + jt * 16 * TROW + TL.nat[x]));
+                    }
                     store_bf16x4<!SEQ>(row + 16 * x, pack4(y));
                 }
             };
@@ -528,7 +534,7 @@ __global__ __launch_bounds__(W16_THREADS, 1) void la_bwd_c128w16_kernel(
     const float *__restrict__ dS_out, const float *__restrict__ dz_out,
     bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
     float *__restrict__ dS_in, float *__restrict__ dz_in) {
-    bwd_c128_body<false>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, 1);
+    bwd_c128_body<false, false>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, 1);
 }
 
 __global__ __launch_bounds__(W16_THREADS, 1) void la_seq_bwd_c128w16_kernel(
@@ -537,7 +543,17 @@ __global__ __launch_bounds__(W16_THREADS, 1) void la_seq_bwd_c128w16_kernel(
     const float *__restrict__ dS_out, const float *__restrict__ dz_out,
     bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
     float *__restrict__ dS_in, float *__restrict__ dz_in, int nchunk) {
-    bwd_c128_body<true>(q, k, v, S_last, z_last, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, nchunk);
+    bwd_c128_body<true, false>(q, k, v, S_last, z_last, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, nchunk);
+}
+
+// the same with the feature map fused: dq and dk are the gradients of the raw inputs
+__global__ __launch_bounds__(W16_THREADS, 1) void la_seq_bwd_c128w16_elu1_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_last, const float *__restrict__ z_last, const bf16 *__restrict__ dO,
+    const float *__restrict__ dS_out, const float *__restrict__ dz_out,
+    bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
+    float *__restrict__ dS_in, float *__restrict__ dz_in, int nchunk) {
+    bwd_c128_body<true, true>(q, k, v, S_last, z_last, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, nchunk);
 }
 
 hipError_t launch_bwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
@@ -552,9 +568,9 @@ hipError_t launch_bwd_c128(const void *q, const void *k, const void *v, const fl
 hipError_t launch_seq_bwd_c128(const void *q, const void *k, const void *v, const float *S_last,
                                const float *z_last, const void *dO, const float *dS_out, const float *dz_out,
                                void *dq, void *dk, void *dv, float *dS_in, float *dz_in, int G, int nchunk,
-                               hipStream_t stream, const hipEvent_t ev[2]) {
-    hipExtLaunchKernelGGL(la_seq_bwd_c128w16_kernel, dim3((unsigned)G), dim3(W16_THREADS), 0, stream, ev[0], ev[1],
-                          0, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_last, z_last, (const bf16 *)dO,
+                               bool elu1, hipStream_t stream, const hipEvent_t ev[2]) {
+    hipExtLaunchKernelGGL(elu1 ? la_seq_bwd_c128w16_elu1_kernel : la_seq_bwd_c128w16_kernel, dim3((unsigned)G),
+                          dim3(W16_THREADS), 0, stream, ev[0], ev[1], 0, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_last, z_last, (const bf16 *)dO,
                           dS_out, dz_out, (bf16 *)dq, (bf16 *)dk, (bf16 *)dv, dS_in, dz_in, nchunk);
     return hipGetLastError();
 }

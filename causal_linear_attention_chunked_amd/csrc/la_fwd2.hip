@@ -48,7 +48,7 @@ struct Fwd2Lds {
 };
 }  // namespace
 
-template <bool SEQ>
+template <bool SEQ, bool FM>
 __device__ __forceinline__ void fwd_c128_body(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ S_in, const float *__restrict__ z_in,
@@ -222,6 +222,12 @@ __device__ __forceinline__ void fwd_c128_body(
         // range, which reads zeros without touching memory, and a load on every path lets
         // the compiler count outstanding loads exactly instead of draining them all.
         const uint32_t nb = (uint32_t)(c + 1) * CHUNK;
+        // fused feature map: raw queries and keys in, phi applied as they are used (keys at
+        // staging); the raw query fragments of this chunk are mapped here
+        if constexpr (FM) {
+            qf[0] = elu1_8(qf[0]);
+            qf[1] = elu1_8(qf[1]);
+        }
         bf16x8 nq[2];
         if (SEQ) {
 #pragma unroll
@@ -230,7 +236,7 @@ __device__ __forceinline__ void fwd_c128_body(
         }
 
         // ---- phase A: block 0's keys and values, the S_0 copy and z_0 row
-        *reinterpret_cast<bf16x8 *>(Kt + so) = kst0;
+        *reinterpret_cast<bf16x8 *>(Kt + so) = FM ? elu1_8(kst0) : kst0;
         *reinterpret_cast<bf16x8 *>(Vt + so) = vst0;
         if (SEQ) {
             kst0 = gload<bf16x8>(kr, nb + tid * 16);
@@ -244,7 +250,7 @@ __device__ __forceinline__ void fwd_c128_body(
         advance(0);
         write_state(1);
         if (blk == 0) outputs(Blk0{});
-        *reinterpret_cast<bf16x8 *>(Kt + TBYTES + so) = kst1;
+        *reinterpret_cast<bf16x8 *>(Kt + TBYTES + so) = FM ? elu1_8(kst1) : kst1;
         *reinterpret_cast<bf16x8 *>(Vt + TBYTES + so) = vst1;
         if (SEQ) {
             kst1 = gload<bf16x8>(kr, nb + TBYTES + tid * 16);
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ S_in, const float *__restrict__ z_in,
     bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out) {
-    fwd_c128_body<false>(q, k, v, S_in, z_in, o, S_out, z_out, 1);
+    fwd_c128_body<false, false>(q, k, v, S_in, z_in, o, S_out, z_out, 1);
 }
 
 // two workgroups per CU: one computes while the other waits at a barrier
@@ -281,7 +287,15 @@ __global__ __launch_bounds__(NTHR, 2) void la_seq_fwd_c128_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ S_in, const float *__restrict__ z_in,
     bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out, int nchunk) {
-    fwd_c128_body<true>(q, k, v, S_in, z_in, o, S_out, z_out, nchunk);
+    fwd_c128_body<true, false>(q, k, v, S_in, z_in, o, S_out, z_out, nchunk);
+}
+
+// the same with the feature map fused: q and k are the raw inputs x, the op uses elu(x) + 1
+__global__ __launch_bounds__(NTHR, 2) void la_seq_fwd_c128_elu1_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_in, const float *__restrict__ z_in,
+    bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out, int nchunk) {
+    fwd_c128_body<true, true>(q, k, v, S_in, z_in, o, S_out, z_out, nchunk);
 }
 
 hipError_t launch_fwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
@@ -292,11 +306,11 @@ hipError_t launch_fwd_c128(const void *q, const void *k, const void *v, const fl
 }
 
 hipError_t launch_seq_fwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
-                               void *o, float *S_out, float *z_out, int G, int nchunk, hipStream_t stream,
+                               void *o, float *S_out, float *z_out, int G, int nchunk, bool elu1, hipStream_t stream,
                                const hipEvent_t ev[2]) {
-    hipExtLaunchKernelGGL(la_seq_fwd_c128_kernel, dim3((unsigned)G), dim3(NTHR), 0, stream, ev[0], ev[1], 0,
-                          (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_in, z_in, (bf16 *)o, S_out, z_out,
-                          nchunk);
+    hipExtLaunchKernelGGL(elu1 ? la_seq_fwd_c128_elu1_kernel : la_seq_fwd_c128_kernel, dim3((unsigned)G), dim3(NTHR),
+                          0, stream, ev[0], ev[1], 0, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_in, z_in,
+                          (bf16 *)o, S_out, z_out, nchunk);
     return hipGetLastError();
 }
 

@@ -25,13 +25,14 @@ hipError_t launch_bwd_c128(const void *q, const void *k, const void *v, const fl
                            float *dS_in, float *dz_in, int G, hipStream_t stream, const hipEvent_t ev[2]);
 
 // The same kernels walking a group's nchunk consecutive 128-token chunks, carry on chip
-// (backward: S_last / z_last is the state after the last chunk).
+// (backward: S_last / z_last is the state after the last chunk); elu1: q and k are raw inputs
+// and the feature map elu(x) + 1 is applied inside.
 hipError_t launch_seq_fwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
-                               void *o, float *S_out, float *z_out, int G, int nchunk, hipStream_t stream,
+                               void *o, float *S_out, float *z_out, int G, int nchunk, bool elu1, hipStream_t stream,
                                const hipEvent_t ev[2]);
 hipError_t launch_seq_bwd_c128(const void *q, const void *k, const void *v, const float *S_last,
                                const float *z_last, const void *dO, const float *dS_out, const float *dz_out,
                                void *dq, void *dk, void *dv, float *dS_in, float *dz_in, int G, int nchunk,
-                               hipStream_t stream, const hipEvent_t ev[2]);
+                               bool elu1, hipStream_t stream, const hipEvent_t ev[2]);
 
 }  // namespace lachunk

@@ -130,6 +130,26 @@ __device__ __forceinline__ void store_bf16x4(bf16 *p, const bf16x4 &x) {
     else *reinterpret_cast<bf16x4 *>(p) = x;
 }
 
+// Positive feature map phi(x) = elu(x) + 1 (alpha = 1): x + 1 above zero, e^x below; eight bf16
+// inputs mapped in fp32 (e^x as 2^(x log2 e) on the transcendental unit) and rounded to bf16.
+__device__ __forceinline__ bf16x8 elu1_8(const bf16x8 &x) {
+    bf16x8 y;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float f = (float)x[i];
+        const float e = __builtin_amdgcn_exp2f(f * 1.4426950408889634f);
+        y[i] = (bf16)(f > 0.f ? f + 1.f : e);
+    }
+    return y;
+}
+// phi'(x) from the mapped value: 1 above zero (where phi > 1), e^x = phi below.
+__device__ __forceinline__ floatx4 elu1_grad4(const bf16x4 &phi) {
+    floatx4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __builtin_fminf((float)phi[i], 1.f);
+    return r;
+}
+
 // bf16x4 of four fp32 values (round to nearest even)
 __device__ __forceinline__ bf16x4 pack4(const floatx4 &x) {
     const bf16x2 a{(bf16)x[0], (bf16)x[1]}, b{(bf16)x[2], (bf16)x[3]};

@@ -55,6 +55,12 @@ extern "C" {
 
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 
+/* Feature map the sequence entry points may apply to q and k themselves. */
+typedef enum {
+    LA_FEATURE_NONE = 0,  /* q, k are the positive features */
+    LA_FEATURE_ELU1 = 1   /* q, k are raw inputs x; the op uses phi(x) = elu(x) + 1 (alpha = 1) */
+} la_feature;
+
 typedef enum {
     LA_OK = 0,
     LA_ERR_INVALID = 1,     /* NULL required pointer, G < 1, C < 1, half-given carry, size overflow */
@@ -117,14 +123,18 @@ la_status la_chunk_bwd(const void *q, const void *k, const void *v,
  *   o        : [G][T][D] dt, output.
  *   S_out    : [G][D][D] fp32, state after the last chunk.
  *   z_out    : [G][D]    fp32, normaliser after the last chunk.
+ *   feature  : LA_FEATURE_NONE, or LA_FEATURE_ELU1: q and k hold raw inputs x and the
+ *              op runs on phi(x) = elu(x) + 1 (x + 1 for x > 0, e^x otherwise),
+ *              computed in fp32 as the inputs are loaded and rounded to bf16 (the
+ *              positive feature map of the workloads, fused; section 1 needs q, k > 0).
  * Supported: dt == LA_BF16, D == 64, chunk == 128, block == 64 and T a positive
  * multiple of 128 below 2^24; anything else returns LA_ERR_UNSUPPORTED (chain
- * la_chunk_fwd calls instead).
+ * la_chunk_fwd calls instead).  A feature outside la_feature is LA_ERR_INVALID.
  */
 la_status la_seq_fwd(const void *q, const void *k, const void *v,
                      const float *S_in, const float *z_in,
                      void *o, float *S_out, float *z_out,
-                     int G, int T, int D, int chunk, int block, la_dtype dt, void *stream);
+                     int G, int T, int D, int chunk, int block, la_feature feature, la_dtype dt, void *stream);
 
 /*
  * Backward over the same sequence for L = sum_t <dO_t, o_t> + <dS_out, S_out> +
@@ -146,13 +156,16 @@ la_status la_seq_fwd(const void *q, const void *k, const void *v,
  *   dq,dk,dv : [G][T][D] dt, outputs.
  *   dS_in    : [G][D][D] fp32 output, gradient of the carry before the first chunk.
  *   dz_in    : [G][D]    fp32 output.
+ *   feature  : as in the forward call.  With LA_FEATURE_ELU1, dq and dk are the
+ *              gradients with respect to the raw inputs: dq phi'(x_q), dk phi'(x_k)
+ *              with phi'(x) = 1 for x > 0 and e^x otherwise (taken as min(1, phi)).
  * Supported: as la_seq_fwd.
  */
 la_status la_seq_bwd(const void *q, const void *k, const void *v,
                      const float *S_last, const float *z_last,
                      const void *dO, const float *dS_out, const float *dz_out,
                      void *dq, void *dk, void *dv, float *dS_in, float *dz_in,
-                     int G, int T, int D, int chunk, int block, la_dtype dt, void *stream);
+                     int G, int T, int D, int chunk, int block, la_feature feature, la_dtype dt, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *la_status_str(la_status s);
@@ -183,7 +196,7 @@ la_status la_time_next_launch(void *start_event, void *stop_event);
 const char *la_kernel_name(int backward, la_dtype dt, int C, int D);
 
 /* The same for la_seq_fwd (backward = 0) and la_seq_bwd (backward = 1) at this chunk length. */
-const char *la_seq_kernel_name(int backward, la_dtype dt, int chunk, int D);
+const char *la_seq_kernel_name(int backward, la_dtype dt, int chunk, int D, la_feature feature);
 
 #ifdef __cplusplus
 }

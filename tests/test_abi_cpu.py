@@ -126,18 +126,18 @@ def test_fwd_chunk_beyond_32bit_offsets(lib):
     assert bwd_call(lib, G=1, C=(1 << 31) // (64 * 2), D=64) == UNSUPPORTED
 
 
-def seq_fwd_call(lib, G=4, T=512, D=64, chunk=128, block=64, dt=1, **over):
+def seq_fwd_call(lib, G=4, T=512, D=64, chunk=128, block=64, feature=0, dt=1, **over):
     args = {n: addr(i) for i, n in enumerate(["q", "k", "v", "S_in", "z_in", "o", "S_out", "z_out"])}
     args.update(over)
     return lib.la_seq_fwd(args["q"], args["k"], args["v"], args["S_in"], args["z_in"], args["o"],
-                          args["S_out"], args["z_out"], G, T, D, chunk, block, dt, None)
+                          args["S_out"], args["z_out"], G, T, D, chunk, block, feature, dt, None)
 
 
-def seq_bwd_call(lib, G=4, T=512, D=64, chunk=128, block=64, dt=1, **over):
+def seq_bwd_call(lib, G=4, T=512, D=64, chunk=128, block=64, feature=0, dt=1, **over):
     names = ["q", "k", "v", "S_last", "z_last", "dO", "dS_out", "dz_out", "dq", "dk", "dv", "dS_in", "dz_in"]
     args = {n: addr(i) for i, n in enumerate(names)}
     args.update(over)
-    return lib.la_seq_bwd(*[args[n] for n in names], G, T, D, chunk, block, dt, None)
+    return lib.la_seq_bwd(*[args[n] for n in names], G, T, D, chunk, block, feature, dt, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -148,6 +148,7 @@ def seq_bwd_call(lib, G=4, T=512, D=64, chunk=128, block=64, dt=1, **over):
     (dict(q=None), INVALID), (dict(S_in=None), INVALID),
     (dict(v=ctypes.c_void_p(BASE + 2 * STEP + 8)), ALIGN),
     (dict(o=addr(1)), ALIAS), (dict(S_out=addr(3)), ALIAS),
+    (dict(feature=2), INVALID), (dict(feature=-1), INVALID), (dict(feature=1, D=128), UNSUPPORTED),
 ])
 def test_seq_fwd_rejects(lib, kw, status):
     assert seq_fwd_call(lib, **kw) == status
@@ -160,6 +161,7 @@ def test_seq_fwd_rejects(lib, kw, status):
     (dict(dq=None), INVALID),
     (dict(dk=ctypes.c_void_p(BASE + 9 * STEP + 4)), ALIGN),
     (dict(dq=addr(5)), ALIAS), (dict(dS_in=addr(3)), ALIAS),
+    (dict(feature=7), INVALID),
 ])
 def test_seq_bwd_rejects(lib, kw, status):
     assert seq_bwd_call(lib, **kw) == status
@@ -169,6 +171,10 @@ def test_seq_kernel_names(lib):
     assert lac.seq_kernel_name(False, "bf16", 128, 64) == "la_seq_fwd_c128_kernel"
     assert lac.seq_kernel_name(True, "bf16", 128, 64) == "la_seq_bwd_c128w16_kernel"
     assert lac.seq_kernel_name(True, "float32", 128, 64) is None
+    assert lac.seq_kernel_name(False, "bf16", 128, 64, "elu1") == "la_seq_fwd_c128_elu1_kernel"
+    assert lac.seq_kernel_name(True, "bf16", 128, 64, "elu1") == "la_seq_bwd_c128w16_elu1_kernel"
+    with pytest.raises(ValueError):
+        lac.seq_kernel_name(True, "bf16", 128, 64, "relu")
     assert lac.seq_supported("bf16", 1024, 64, 128) and not lac.seq_supported("bf16", 1000, 64, 128)
     assert not lac.seq_supported("float32", 1024, 64, 128) and not lac.seq_supported("bf16", 1024, 128, 128)
 

@@ -16,8 +16,9 @@ from tol import RTOL, check
 pytestmark = pytest.mark.gpu
 
 
-def _case(dtype, carry, upstream, G=3, T=300, D=64, chunk=128, seed=11):
-    I = inp.make_inputs(G=G, T=T, D=D, dtype=dtype, carry=carry, backward=True, seed=seed)
+def _case(dtype, carry, upstream, G=3, T=300, D=64, chunk=128, seed=11, feature_map=None):
+    I = inp.make_inputs(G=G, T=T, D=D, dtype=dtype, carry=carry, backward=True, seed=seed,
+                        features="raw" if feature_map else "mapped")
     rng = np.random.default_rng(seed + 1)
     dS = torch.from_numpy(rng.standard_normal((G, D, D)).astype(np.float32)) if upstream else None
     dz = torch.from_numpy(rng.standard_normal((G, D)).astype(np.float32)) if upstream else None
@@ -27,14 +28,19 @@ def _case(dtype, carry, upstream, G=3, T=300, D=64, chunk=128, seed=11):
     leaf = lambda x: None if x is None else x.to(dev).clone().requires_grad_(True)
     q, k, v = leaf(I["q"]), leaf(I["k"]), leaf(I["v"])
     S_in, z_in = leaf(I["S_in"]), leaf(I["z_in"])
-    o, (S_out, z_out) = lac.linear_attention(q, k, v, S_in, z_in, chunk=chunk)
+    o, (S_out, z_out) = lac.linear_attention(q, k, v, S_in, z_in, chunk=chunk, feature_map=feature_map)
     loss = (o.float() * I["dO"].to(dev).float()).sum()
     if upstream:
         loss = loss + (S_out * dS.to(dev)).sum() + (z_out * dz.to(dev)).sum()
     loss.backward()
     torch.cuda.synchronize()
-    ro, rS, rz = oracle.fwd(I["q"], I["k"], I["v"], I["S_in"], I["z_in"])
-    ref = oracle.bwd(I["q"], I["k"], I["v"], I["S_in"], I["z_in"], I["dO"], dS, dz)
+    if feature_map == "elu1":
+        # the features enter the op at its element type
+        ro, rS, rz = oracle.features.fwd(I["q"], I["k"], I["v"], I["S_in"], I["z_in"], dtype=dtype)
+        ref = oracle.features.bwd(I["q"], I["k"], I["v"], I["S_in"], I["z_in"], I["dO"], dS, dz, dtype=dtype)
+    else:
+        ro, rS, rz = oracle.fwd(I["q"], I["k"], I["v"], I["S_in"], I["z_in"])
+        ref = oracle.bwd(I["q"], I["k"], I["v"], I["S_in"], I["z_in"], I["dO"], dS, dz)
     tol = RTOL[dtype]
     check("o", o, ro, tol)
     check("S_out", S_out, rS, tol)
@@ -66,3 +72,7 @@ def test_autograd_sequence_entry_points(gpu):
     assert lac.seq_supported("bf16", 512, 64, 128)
     _case("bf16", "prior", True, G=3, T=512)
     _case("bf16", "zero", False, G=2, T=384)
+
+
+def test_autograd_fused_feature_map(gpu):
+    _case("bf16", "prior", True, G=3, T=384, feature_map="elu1")

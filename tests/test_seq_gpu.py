@@ -32,19 +32,24 @@ def upstream(G, D, seed):
             torch.from_numpy(rng.standard_normal((G, D)).astype(np.float32)))
 
 
-def run_seq(I, dS=None, dz=None):
+def run_seq(I, dS=None, dz=None, feature=None):
     q, k, v, dO = (dev(I[n]) for n in ("q", "k", "v", "dO"))
-    o, S_out, z_out = lac.seq_fwd(q, k, v, dev(I["S_in"]), dev(I["z_in"]))
-    dq, dk, dv, dS_in, dz_in = lac.seq_bwd(q, k, v, S_out, z_out, dO, dev(dS), dev(dz))
+    o, S_out, z_out = lac.seq_fwd(q, k, v, dev(I["S_in"]), dev(I["z_in"]), feature=feature)
+    dq, dk, dv, dS_in, dz_in = lac.seq_bwd(q, k, v, S_out, z_out, dO, dev(dS), dev(dz), feature=feature)
     torch.cuda.synchronize()
     return dict(o=o, S_out=S_out, z_out=z_out, dq=dq, dk=dk, dv=dv, dS_in=dS_in, dz_in=dz_in)
 
 
-def oracle_ref(I, dS=None, dz=None, groups=None):
+def oracle_ref(I, dS=None, dz=None, groups=None, feature=None):
     sel = (lambda x: x) if groups is None else (lambda x: None if x is None else x[groups])
     args = [sel(I[n]) for n in ("q", "k", "v", "S_in", "z_in")]
-    o, S_out, z_out = oracle.fwd(*args)
-    dq, dk, dv, dS_in, dz_in = oracle.bwd(*args, sel(I["dO"]), sel(dS), sel(dz))
+    if feature == "elu1":
+        # the features enter the op at its element type (bf16)
+        o, S_out, z_out = oracle.features.fwd(*args, dtype="bf16")
+        dq, dk, dv, dS_in, dz_in = oracle.features.bwd(*args, sel(I["dO"]), sel(dS), sel(dz), dtype="bf16")
+    else:
+        o, S_out, z_out = oracle.fwd(*args)
+        dq, dk, dv, dS_in, dz_in = oracle.bwd(*args, sel(I["dO"]), sel(dS), sel(dz))
     return dict(o=o, S_out=S_out, z_out=z_out, dq=dq, dk=dk, dv=dv, dS_in=dS_in, dz_in=dz_in)
 
 
@@ -115,7 +120,29 @@ def test_seq_matches_chained_calls(gpu):
         assert rel < 2e-3, (name, rel)
 
 
+@pytest.mark.parametrize("G,nchunk,carry,up", [(3, 3, "prior", True), (2, 10, "zero", False), (1, 1, "zero", True)])
+def test_seq_fused_feature_map(gpu, G, nchunk, carry, up):
+    # raw q, k (both signs); the op applies elu(x)+1 and returns gradients of the raw inputs
+    T = 128 * nchunk
+    say(f"[case] seq elu1 G={G} T={T} carry={carry} upstream={up}")
+    I = inp.make_inputs(G=G, T=T, D=64, dtype="bf16", carry=carry, backward=True, seed=40 + nchunk,
+                        features="raw")
+    dS, dz = upstream(G, 64, 41) if up else (None, None)
+    compare(run_seq(I, dS, dz, feature="elu1"), oracle_ref(I, dS, dz, feature="elu1"))
+
+
+def test_seq_fused_feature_map_full_size(gpu):
+    w = inp.workload("g1280_8x128_d64_bf16_fwdbwd")
+    say(f"[case] seq elu1 full {w.name}")
+    I = inp.make_inputs(G=w.G, T=w.T, D=w.D, dtype=w.dtype, carry=w.carry, backward=True, seed=w.seed,
+                        features="raw")
+    groups = [0, 511, 1279]
+    compare(run_seq(I, feature="elu1"), oracle_ref(I, groups=groups, feature="elu1"), groups)
+
+
 def test_seq_rejects_unsupported(gpu):
     x = torch.ones(2, 200, 64, dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(lac.LachunkError, match="UNSUPPORTED"):
         lac.seq_fwd(x, x, x)
+    with pytest.raises(ValueError):
+        lac.seq_fwd(x[:, :128], x[:, :128], x[:, :128], feature="relu")
