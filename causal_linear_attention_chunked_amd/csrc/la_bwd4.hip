@@ -57,10 +57,13 @@ struct Bwd4Lds {
     static constexpr int KT = QT + 2 * TBYTES;
     static constexpr int VT = KT + 2 * TBYTES;
     static constexpr int GT = VT + 2 * TBYTES;
+    // from 64 KB (addressed from base H1): split states and dP; from 128 KB (base H2): the
+    // rest.  Each region's offsets from its base fit the ds instructions' 16-bit offset field.
+    static constexpr int H1 = 0x10000, H2 = 0x20000;
     static constexpr int SS = GT + 2 * TBYTES;   // [b][hi, lo] split S_b; from phase 4: Sh_0 [hi, lo]
-    static constexpr int SH1 = SS + 4 * TBYTES;  // Sh_1 [hi, lo]
-    static constexpr int DP = SH1 + 2 * TBYTES;  // [b][hi, lo] split dP, stored [t][j]
-    static constexpr int ZF = DP + 4 * TBYTES;   // [b][64] z_b fp32
+    static constexpr int DP = SS + 4 * TBYTES;   // [b][hi, lo] split dP, stored [t][j]
+    static constexpr int SH1 = DP + 4 * TBYTES;  // Sh_1 [hi, lo]
+    static constexpr int ZF = SH1 + 2 * TBYTES;  // [b][64] z_b fp32
     static constexpr int ZH = ZF + 2 * 64 * 4;   // [b][64] zh_b fp32
     static constexpr int INV = ZH + 2 * 64 * 4;  // [128] inv_t
     static constexpr int RHO = INV + 128 * 4;    // [128] rho_t
@@ -68,6 +71,8 @@ struct Bwd4Lds {
     static constexpr int PS = DDR + 2 * 128 * 2; // [8 query tiles][2 halves][16 rows] (den, rho den) partials
     static constexpr int BYTES = PS + 8 * 2 * 16 * 8;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
+    static_assert(SS == H1 && DP + 4 * TBYTES <= H1 + 0x10000 && SH1 == H2 && BYTES <= H2 + 0x10000,
+                  "high regions within 64 KB of their bases");
 };
 }  // namespace
 
@@ -95,6 +100,11 @@ __device__ __forceinline__ void bwd_c128_body(
     bf16 *const ddr = reinterpret_cast<bf16 *>(smem + L::DDR);
     floatx2 *const psum = reinterpret_cast<floatx2 *>(smem + L::PS);
     auto tile = [&](int base, int b) -> char * { return smem + base + b * TBYTES; };
+    // Tiles of the high regions, relative to their bases (paired with TL1 / TL2 offsets).  The
+    // sequence loop has no registers to spare for the based offsets: there the bases are zero.
+    constexpr int H1 = SEQ ? 0 : L::H1, H2 = SEQ ? 0 : L::H2;
+    auto tile1 = [&](int base, int b) -> char * { return smem + base + b * TBYTES - H1; };
+    auto tile2 = [&](int base, int b) -> char * { return smem + base + b * TBYTES - H2; };
 
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -149,8 +159,11 @@ __device__ __forceinline__ void bwd_c128_body(
         int tid_c = tid;
         if (SEQ) asm volatile("" : "+v"(tid_c));
         const int lane = tid_c & 63, r = lane & 15, g = lane >> 4;
-        const TileLanes TL(lane);
-        const uint32_t tr_c = TL.tr_at(ct), tr_p = TL.tr_at(pt), nat_c = TL.nat_at(ct);
+        const TileLanes TL(lane), TL1(lane, SEQ ? 0u : opaque_v(H1)), TL2(lane, SEQ ? 0u : opaque_v(H2));
+        const uint32_t tr_c = TL.tr_at(ct), tr_p = TL.tr_at(pt);
+        // small arrays past H2: per-lane byte offsets from that base
+        const uint32_t g16 = TL2.base + 16 * g, g8 = TL2.base + 8 * g, r8 = TL2.base + 8 * r;
+        auto f4 = [&](int off) { return *reinterpret_cast<const floatx4 *>(smem - H2 + off + g16); };
         const size_t tok0 = gtok0 + (size_t)c * C;
         // the reverse state after this chunk is nonzero unless it is the last one without dS_out
         const bool has_up = (SEQ && c < n - 1) || dS_out != nullptr;
@@ -169,20 +182,20 @@ __device__ __forceinline__ void bwd_c128_body(
         // path lets the compiler count outstanding loads exactly instead of draining them all.
         if (SEQ) load_stage(c - 1);
         // split copy of the wave's state tile (C[c][p] accumulator), stored [p][c] (hi, lo tiles)
-        auto write_split = [&](char *hi, char *lo, const floatx4 &acc) {
+        auto write_split = [&](char *hi, char *lo, const floatx4 &acc, uint32_t natc) {
             bf16x4 hh, ll;
             split4(acc, hh, ll);
-            tstore_acc(hi, nat_c, pt, hh);
-            tstore_acc(lo, nat_c, pt, ll);
+            tstore_acc(hi, natc, pt, hh);
+            tstore_acc(lo, natc, pt, ll);
         };
         auto write_z = [&](float *dst, const floatx4 &zz) {
             if (ct == 0 && g == 0) dst[16 * pt + r] = zz[0];
         };
         if (!SEQ) {
-            write_split(tile(L::SS, 0), tile(L::SS, 1), Sacc);
+            write_split(tile1(L::SS, 0), tile1(L::SS, 1), Sacc, TL1.nat_at(ct));
             write_z(zf, zr);
         }
-        if (has_up) write_split(tile(L::SH1, 0), tile(L::SH1, 1), Sh);
+        if (has_up) write_split(tile2(L::SH1, 0), tile2(L::SH1, 1), Sh, TL2.nat_at(ct));
         write_z(zh + 64, zhr);
         lds_barrier();
 
@@ -207,7 +220,7 @@ __device__ __forceinline__ void bwd_c128_body(
         };
         if (SEQ) {
             state_step(1, true);
-            write_split(tile(L::SS, 2), tile(L::SS, 3), Sacc);
+            write_split(tile1(L::SS, 2), tile1(L::SS, 3), Sacc, TL1.nat_at(ct));
             write_z(zf + 64, zr);
             state_step(0, true);
         } else {
@@ -245,10 +258,10 @@ __device__ __forceinline__ void bwd_c128_body(
             }
         }
         if (SEQ) {
-            write_split(tile(L::SS, 0), tile(L::SS, 1), Sacc);
+            write_split(tile1(L::SS, 0), tile1(L::SS, 1), Sacc, TL1.nat_at(ct));
             write_z(zf, zr);
         } else {
-            write_split(tile(L::SS, 2), tile(L::SS, 3), Sacc);
+            write_split(tile1(L::SS, 2), tile1(L::SS, 3), Sacc, TL1.nat_at(ct));
             write_z(zf + 64, zr);
         }
         lds_barrier();
@@ -262,8 +275,8 @@ __device__ __forceinline__ void bwd_c128_body(
             for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
-                    sh[pp][kc] = tfrag(tile(L::SS, 2 * blk), TL, 2 * h + pp, kc);
-                    sl[pp][kc] = tfrag(tile(L::SS, 2 * blk + 1), TL, 2 * h + pp, kc);
+                    sh[pp][kc] = tfrag(tile1(L::SS, 2 * blk), TL1, 2 * h + pp, kc);
+                    sl[pp][kc] = tfrag(tile1(L::SS, 2 * blk + 1), TL1, 2 * h + pp, kc);
                 }
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
@@ -280,7 +293,7 @@ __device__ __forceinline__ void bwd_c128_body(
             const bf16x8 qh = h ? qf[1] : qf[0];  // key features 32h..32h+31 of q_t
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
-                zv[pp] = *reinterpret_cast<const floatx4 *>(zf + 64 * blk + 16 * (2 * h + pp) + 4 * g);
+                zv[pp] = f4(L::ZF + 4 * (64 * blk + 16 * (2 * h + pp)));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     // q_t[p] for p = 16 (2h + pp) + 4g + e: k-chunk h, slot 4 pp + e
@@ -304,7 +317,9 @@ __device__ __forceinline__ void bwd_c128_body(
         // ---- phase 3.  Row statistics from both halves; dP for this wave's key tiles
         float inv, dden;
         {
-            const floatx2 mine = psum[(u * 2 + h) * 16 + r], other = psum[(u * 2 + 1 - h) * 16 + r];
+            const floatx2 mine = *reinterpret_cast<const floatx2 *>(smem - H2 + L::PS + 8 * 16 * (u * 2 + h) + r8);
+            const floatx2 other =
+                *reinterpret_cast<const floatx2 *>(smem - H2 + L::PS + 8 * 16 * (u * 2 + 1 - h) + r8);
             const float den = mine[0] + other[0];
             inv = __builtin_amdgcn_rcpf(den);
             const float rho = (mine[1] + other[1]) * inv;
@@ -321,8 +336,8 @@ __device__ __forceinline__ void bwd_c128_body(
                 }
             }
             const Split8 dps = split_acc(d[0], d[1]);
-            tstore_frag_at(tile(L::DP, 2 * blk), TL, tq, h, dps.hi);
-            tstore_frag_at(tile(L::DP, 2 * blk + 1), TL, tq, h, dps.lo);
+            tstore_frag_at(tile1(L::DP, 2 * blk), TL1, tq, h, dps.hi);
+            tstore_frag_at(tile1(L::DP, 2 * blk + 1), TL1, tq, h, dps.lo);
             if (h == 0 && g == 0) {
                 const int t = 64 * blk + 16 * tq + r;
                 invs[t] = inv;
@@ -340,8 +355,8 @@ __device__ __forceinline__ void bwd_c128_body(
             bf16x8 dph[2], dpl[2], ktr[2][2];
 #pragma unroll
             for (int jc = 0; jc < 2; ++jc) {
-                dph[jc] = tfrag(tile(L::DP, 2 * blk), TL, tq, jc);
-                dpl[jc] = tfrag(tile(L::DP, 2 * blk + 1), TL, tq, jc);
+                dph[jc] = tfrag(tile1(L::DP, 2 * blk), TL1, tq, jc);
+                dpl[jc] = tfrag(tile1(L::DP, 2 * blk + 1), TL1, tq, jc);
 #pragma unroll
                 for (int pp = 0; pp < 2; ++pp) ktr[pp][jc] = tfrag_tr(tile(L::KT, blk), TL.tr_at(2 * h + pp), jc);
             }
@@ -368,8 +383,8 @@ __device__ __forceinline__ void bwd_c128_body(
             for (int tc = 0; tc < 2; ++tc) {
                 xg[tc] = tfrag_tr(tile(L::GT, b), tr_c, tc);
                 qt[tc] = tfrag_tr(tile(L::QT, b), tr_p, tc);
-                iv[tc][0] = *reinterpret_cast<const floatx4 *>(invs + 64 * b + 32 * tc + 4 * g);
-                iv[tc][1] = *reinterpret_cast<const floatx4 *>(invs + 64 * b + 32 * tc + 16 + 4 * g);
+                iv[tc][0] = f4(L::INV + 4 * (64 * b + 32 * tc));
+                iv[tc][1] = f4(L::INV + 4 * (64 * b + 32 * tc + 16));
             }
 #pragma unroll
             for (int tc = 0; tc < 2; ++tc) {
@@ -383,13 +398,16 @@ __device__ __forceinline__ void bwd_c128_body(
             if (ct == 0) {
 #pragma unroll
                 for (int tc = 0; tc < 2; ++tc) {
-                    mma(zhr, rowfrag(reinterpret_cast<const char *>(ddr + 64 * b), lane, tc), qt[tc]);
-                    mma(zhr, rowfrag(reinterpret_cast<const char *>(ddr + 128 + 64 * b), lane, tc), qt[tc]);
+                    // the dden row (hi, then lo) as an operand whose 16 rows are all that row
+                    for (int hl = 0; hl < 2; ++hl) {
+                        const char *p = smem - H2 + L::DDR + 2 * (128 * hl + 64 * b + 32 * tc) + g8;
+                        mma(zhr, __builtin_shufflevector(lds_b64(p), lds_b64(p + 32), 0, 1, 2, 3, 4, 5, 6, 7), qt[tc]);
+                    }
                 }
             }
         };
         reverse(1);
-        write_split(tile(L::SS, 0), tile(L::SS, 1), Sh);  // Sh_0 (the S_0 copy is no longer read)
+        write_split(tile1(L::SS, 0), tile1(L::SS, 1), Sh, TL1.nat_at(ct));  // Sh_0 (the S_0 copy is no longer read)
         write_z(zh, zhr);
 
         // pass 2: wave w takes block (w / 4) % 2 and dv (w < 8, key tile w % 4) or dk (key tile
@@ -399,7 +417,7 @@ __device__ __forceinline__ void bwd_c128_body(
             constexpr bool DK = decltype(dk_tag)::value;
             constexpr int B = decltype(b_tag)::value;
             const int jt = DK ? 3 - (w & 3) : (w & 3);
-            auto inter = [&](const char *shh, const char *shl) {
+            auto inter = [&](const char *shh, const char *shl, const TileLanes &TX) {
                 if constexpr (SEQ) {
                     // half the fragments at a time: the sequence loop has fewer registers to spare
 #pragma unroll
@@ -407,8 +425,8 @@ __device__ __forceinline__ void bwd_c128_body(
                         bf16x8 sh[4], sl[4];
 #pragma unroll
                         for (int x = 0; x < 4; ++x) {
-                            sh[x] = DK ? tfrag(shh, TL, x, kc) : tfrag_tr(shh, TL.tr[x], kc);
-                            sl[x] = DK ? tfrag(shl, TL, x, kc) : tfrag_tr(shl, TL.tr[x], kc);
+                            sh[x] = DK ? tfrag(shh, TX, x, kc) : tfrag_tr(shh, TX.tr[x], kc);
+                            sl[x] = DK ? tfrag(shl, TX, x, kc) : tfrag_tr(shl, TX.tr[x], kc);
                         }
 #pragma unroll
                         for (int x = 0; x < 4; ++x) {
@@ -423,8 +441,8 @@ __device__ __forceinline__ void bwd_c128_body(
                 for (int x = 0; x < 4; ++x)
 #pragma unroll
                     for (int kc = 0; kc < 2; ++kc) {
-                        sh[x][kc] = DK ? tfrag(shh, TL, x, kc) : tfrag_tr(shh, TL.tr[x], kc);
-                        sl[x][kc] = DK ? tfrag(shl, TL, x, kc) : tfrag_tr(shl, TL.tr[x], kc);
+                        sh[x][kc] = DK ? tfrag(shh, TX, x, kc) : tfrag_tr(shh, TX.tr[x], kc);
+                        sl[x][kc] = DK ? tfrag(shl, TX, x, kc) : tfrag_tr(shl, TX.tr[x], kc);
                     }
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc)
@@ -440,14 +458,14 @@ __device__ __forceinline__ void bwd_c128_body(
                 for (int x = 0; x < 4; ++x) {
                     floatx4 y = acc[x];
                     if constexpr (DK) {
-                        y += *reinterpret_cast<const floatx4 *>(zh + 64 * B + 16 * x + 4 * g);
+                        y += f4(L::ZH + 4 * (64 * B + 16 * x));
                         if constexpr (FM) y *= elu1_grad4(lds_b64(tile(L::KT, B) + jt * 16 * TROW + TL.nat[x]));
                     }
                     store_bf16x4<!SEQ>(row + 16 * x, pack4(y));
                 }
             };
             if (inter_phase) {  // phase 5, block 0: against Sh_0
-                inter(tile(L::SS, 0), tile(L::SS, 1));
+                inter(tile1(L::SS, 0), tile1(L::SS, 1), TL1);
                 store();
                 return;
             }
@@ -455,7 +473,7 @@ __device__ __forceinline__ void bwd_c128_body(
             for (int x = 0; x < 4; ++x) acc[x] = zero4();
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) kv[kc] = tfrag(tile(DK ? L::VT : L::KT, B), TL, jt, kc);
-            const uint32_t tr_jt = TL.tr_at(jt);
+            const uint32_t tr_jt = TL1.tr_at(jt);
 #pragma unroll
             for (int tc = 0; tc < 2; ++tc) {
                 if (2 * tc + 1 < jt) continue;  // every query of the slab precedes the key tile
@@ -465,14 +483,14 @@ __device__ __forceinline__ void bwd_c128_body(
                 Split8 y;
                 if constexpr (DK) {
                     // dP rows j, k = t, from the pass-1 copy
-                    y = Split8{tfrag_tr(tile(L::DP, 2 * B), tr_jt, tc), tfrag_tr(tile(L::DP, 2 * B + 1), tr_jt, tc)};
+                    y = Split8{tfrag_tr(tile1(L::DP, 2 * B), tr_jt, tc), tfrag_tr(tile1(L::DP, 2 * B + 1), tr_jt, tc)};
                 } else {
                     // A[t][j] inv_t recomputed (lane: j = r, t = 32 tc + 16 hh + 4g + i), masked to t >= j
                     bf16x8 qa[2][2];
                     floatx4 iv[2], at[2];
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
-                        iv[hh] = *reinterpret_cast<const floatx4 *>(invs + 64 * B + 32 * tc + 16 * hh + 4 * g);
+                        iv[hh] = f4(L::INV + 4 * (64 * B + 32 * tc + 16 * hh));
 #pragma unroll
                         for (int kc = 0; kc < 2; ++kc) qa[hh][kc] = tfrag(tile(L::QT, B), TL, 2 * tc + hh, kc);
                     }
@@ -492,7 +510,7 @@ __device__ __forceinline__ void bwd_c128_body(
                 for (int x = 0; x < 4; ++x) mma_s(acc[x], xo[x], y);
             }
             if (B == 1) {  // block 1 completes here, against Sh_1 = dS_out
-                if (has_up) inter(tile(L::SH1, 0), tile(L::SH1, 1));
+                if (has_up) inter(tile2(L::SH1, 0), tile2(L::SH1, 1), TL2);
                 store();
             }
         };

@@ -35,11 +35,16 @@ __device__ __forceinline__ int swz(int row) { return ((row ^ (row >> 1)) & 7) <<
 //           storage rows 4g + m of a 16-row slab (add 16 * slab * TROW).
 // nat[] / tr[] hold the four values for compile-time indices; nat_at() / tr_at() compute
 // one for a run-time index (an array indexed at run time would live in scratch memory).
+// `base` is added to every offset: tiles at 64 KB and above are addressed as (tile - base) +
+// offset with base held opaquely in a register, so that the ds instructions' 16-bit offset
+// field takes the rest (otherwise every access pays an add).
 struct TileLanes {
     int rrow, ln, trow, lt, g, sr;
+    uint32_t base;
     uint32_t nat[4], tr[4];
-    __device__ __forceinline__ explicit TileLanes(int lane) {
+    __device__ __forceinline__ explicit TileLanes(int lane, uint32_t base_ = 0) {
         const int r = lane & 15, g = lane >> 4, m = (lane & 15) >> 2, a = lane & 3;
+        base = base_;
         rrow = r * TROW;
         this->g = g;
         sr = swz(r);
@@ -52,9 +57,15 @@ struct TileLanes {
             tr[u] = tr_at(u);
         }
     }
-    __device__ __forceinline__ uint32_t nat_at(int u) const { return rrow + 8 * ((4 * u) ^ ln); }
-    __device__ __forceinline__ uint32_t tr_at(int u) const { return trow + 8 * ((4 * u) ^ lt); }
+    __device__ __forceinline__ uint32_t nat_at(int u) const { return base + rrow + 8 * ((4 * u) ^ ln); }
+    __device__ __forceinline__ uint32_t tr_at(int u) const { return base + trow + 8 * ((4 * u) ^ lt); }
 };
+
+// A uniform value in a register the compiler cannot see through (for TileLanes::base).
+__device__ __forceinline__ uint32_t opaque_v(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
 
 // Volatile, so that the two 8-byte halves of different fragments are never merged into one
 // ds_read2 (which would land them in the wrong registers and cost a v_mov per dword).
