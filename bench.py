@@ -10,12 +10,15 @@ forward and one backward launch; `--workload` names the chained ones.  Steps
 rotate over enough buffer sets (>= 640 MB) that the 256 MB last-level cache
 cannot serve the traffic.  Two timed regions, each bracketed by device
 synchronisation:
-  1. K plain steps: the throughput `value` and `ms_per_step`;
+  1. K plain steps in five consecutive runs: the median run's time per step gives `value`
+     and `ms_per_step`;
   2. K more steps in which every launch carries a pair of HIP events recorded
      on its kernel dispatch (la_time_next_launch): the per-kernel durations
      behind the roofline.  Those events cost host time per launch, which is why
      they stay out of region 1.
-Prints one JSON line.
+Then, for context only: K steps on a single buffer set (its inputs warm in the cache,
+`config.warm_single_set_ms_per_step`) and a 1 GiB device copy (`roofline.copy_GBs_measured`,
+the practical ceiling beside the 8 TB/s peak).  Prints one JSON line.
 
     python bench.py --copy-calibration   # one plain device copy of known size, for counter scaling
     python bench.py --counters-summary DIR
@@ -179,6 +182,26 @@ def cpu_baseline(I, w, min_seconds=10.0, mac_budget=2e9, feature=None):
                       f"median of {len(times)} repeats ({sum(times):.1f} s of CPU work)"}
 
 
+def copy_bandwidth(torch, gib=1, reps=5):
+    """HBM bandwidth of a plain device-to-device copy of `gib` GiB (bytes read + written per
+    second), the best of `reps`: the practical ceiling beside the 8 TB/s peak."""
+    n = gib * (1 << 30) // 4
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    return 2 * n * 4 / (best / 1e3) / 1e9
+
+
 def copy_calibration(torch, mib=256, reps=5):
     """Plain copies of a known byte count: what FETCH_SIZE / WRITE_SIZE read for them scales the
     counters taken on the kernels to bytes."""
@@ -317,17 +340,25 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    # region 1: plain steps
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # region 1: plain steps, K in all, timed in up to five consecutive runs (the median run's
+    # per-step time is the result; the mean over all K is reported beside it)
+    R = min(5, K)
+    sizes = [K // R + (1 if r < K % R else 0) for r in range(R)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R)]
     torch.cuda.synchronize()
-    start.record()
     h0 = time.perf_counter()
-    for i in range(K):
-        step(sets[i % nsets])
+    i = 0
+    for (a, b), nsteps in zip(evs, sizes):
+        a.record()
+        for _ in range(nsteps):
+            step(sets[i % nsets])
+            i += 1
+        b.record()
     host_s = time.perf_counter() - h0
-    end.record()
     torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / K
+    per_run = sorted(a.elapsed_time(b) / nsteps for (a, b), nsteps in zip(evs, sizes))
+    ms_per_step = per_run[len(per_run) // 2]
+    ms_per_step_mean = sum(a.elapsed_time(b) for a, b in evs) / K
     value = G * w.T / (ms_per_step / 1e3)
 
     # region 2: the same steps with dispatch-bound events on every launch
@@ -340,6 +371,18 @@ def main():
             lac.time_next_launch(e[0], e[1])
             launch(s, kind, c)
     torch.cuda.synchronize()
+
+    # warm: the same steps on one buffer set, whose inputs then sit in the last-level cache
+    # (labelled; not the measurement)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(K):
+        step(sets[0])
+    b.record()
+    torch.cuda.synchronize()
+    warm_ms = a.elapsed_time(b) / K
+    copy_gbs = copy_bandwidth(torch)
 
     # per kernel: launches, total bytes and total time over the K steps
     per = {}
@@ -371,12 +414,15 @@ def main():
                    "block": w.block, "carry": w.carry, "launches_per_step": len(launches),
                    "buffer_sets": nsets, "footprint_mb": round(nsets * set_bytes / 1e6, 1),
                    "entry_points": "la_seq_fwd/la_seq_bwd" if args.seq else "la_chunk_fwd/la_chunk_bwd",
+                   "timed_runs": R, "ms_per_step_runs": per_run, "ms_per_step_mean": ms_per_step_mean,
+                   "warm_single_set_ms_per_step": warm_ms,
                    "feature_map": args.feature or "applied by the caller",
                    "graph_captured": False, "host_enqueue_us_per_step": host_s * 1e6 / K,
                    "kernel_timing": "HIP events recorded on each kernel dispatch, separate timed loop"},
         "roofline": {"bound": "hbm", "kernel": top, "achieved": kt["GB/s"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kt["frac"], "traffic": kt["traffic"],
-                     "algorithmic_bytes": kt["algorithmic_bytes"], "avg_us": kt["avg_us"]},
+                     "algorithmic_bytes": kt["algorithmic_bytes"], "avg_us": kt["avg_us"],
+                     "copy_GBs_measured": copy_gbs, "frac_of_copy": kt["GB/s"] / copy_gbs},
         "kernels": kernels,
         "step_roofline_frac": set_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
     }
