@@ -150,9 +150,20 @@ def counters_summary(d, workload, kernels):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(I, w, min_seconds=10.0, mac_budget=2e9, feature=None):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(I, w, min_seconds=10.0, mac_budget=2e9, feature=None, single_seconds=5.0):
     """The fp64 oracle as it stands, on this host's cores, over the workload's first groups
-    (all of them when the workload is small), repeated; one call covers all the chunks."""
+    (all of them when the workload is small), repeated; one call covers all the chunks.  Also
+    timed on one thread, over at most `single_seconds`."""
     import oracle
     if feature == "elu1":
         ofwd = lambda *a, nthreads: oracle.features.fwd(*a, dtype=w.dtype, nthreads=nthreads)
@@ -176,10 +187,19 @@ def cpu_baseline(I, w, min_seconds=10.0, mac_budget=2e9, feature=None):
             break
     times.sort()
     med = times[len(times) // 2]
+    # one thread: the first groups only, scaled to tokens.groups/s
+    g1 = max(1, min(g, int(g * single_seconds / max(med * threads, 1e-9))))
+    a1 = [None if x is None else x[:g1] for x in args]
+    t0 = time.perf_counter()
+    ofwd(*a1, nthreads=1)
+    obwd(*a1, None if dO is None else dO[:g1], nthreads=1)
+    t1 = time.perf_counter() - t0
     what = f"full {w.name} workload" if g == w.G else f"first {g} of the {w.G} groups of {w.name}"
     return {"value": g * w.T / med, "unit": "tokens·groups/s", "cores": threads, "kind": "oracle",
             "sample": f"{what} (G={g}, {w.T} tokens, D={w.D}), forward+backward in fp64, "
-                      f"median of {len(times)} repeats ({sum(times):.1f} s of CPU work)"}
+                      f"median of {len(times)} repeats ({sum(times):.1f} s of CPU work)",
+            "single_thread_value": g1 * w.T / t1, "single_thread_sample": f"first {g1} groups, one run",
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count()}
 
 
 def copy_bandwidth(torch, gib=1, reps=5):
@@ -426,6 +446,12 @@ def main():
         "kernels": kernels,
         "step_roofline_frac": set_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
     }
+    if w.name == HEADLINE and not args.seq:
+        # the pages' own figure for this shape (context, another machine, not the target): their
+        # CPU micro-benchmark of the chunked form, fp32, forward+backward 72.4 ms at G=160, C=128, D=64
+        out["context"] = {"pages_cpu_fwdbwd_tokens_groups_per_s": 160 * 128 / 72.4e-3,
+                          "source": "Fractus-1B training optimization, CPU benchmark of the chunked form "
+                                    "(fp32 PyTorch, CPU model not stated)"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(I, w, feature=args.feature)
     print(json.dumps(out), flush=True)
