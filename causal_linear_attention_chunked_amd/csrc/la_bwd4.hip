@@ -76,11 +76,6 @@ struct Bwd4Lds {
 };
 }  // namespace
 
-// bf16 fragment negated (sign bits flipped): acc += (-X) Y^T subtracts a product exactly
-__device__ __forceinline__ bf16x8 neg8(const bf16x8 &x) {
-    return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, x) ^ 0x80008000u);
-}
-
 // S_in, z_in: the carry before the chunk (single chunk) or after the last chunk (SEQ).
 template <bool SEQ, bool FM>
 __device__ __forceinline__ void bwd_c128_body(
@@ -142,6 +137,14 @@ __device__ __forceinline__ void bwd_c128_body(
     load_stage(n - 1);
     // state accumulators C[c][p] (lane: p = 16 pt + r, c = 16 ct + 4g + e): S and Sh
     floatx4 Sacc, Sh, zr, zhr;
+    // Sequence mode: the forward state recovered from the final carry is kept as the unevaluated
+    // sum (Sacc + Scomp, zr + zcomp).  Early in a long sequence the state is far smaller than the
+    // final carry it is recovered from (z grows with every token), so the plain fp32 differences
+    // would leave errors relative to the final carry; the compensation terms keep the rounding
+    // error of every subtraction (an exact two-difference), leaving the state accurate relative
+    // to itself.
+    floatx4 Scomp = zero4();
+    float zcomp = 0.f;  // the four entries of z's accumulator are equal; one is carried
     {
         const uint32_t so = ((16 * pt + r) * D + 16 * ct + 4 * g) * 4;
         Sacc = gload<floatx4>(sres, so);
@@ -203,28 +206,42 @@ __device__ __forceinline__ void bwd_c128_body(
         // S_1 = S_0 + K_0^T V_0; in sequence mode backwards, S_1 = S_end - K_1^T V_1 (copy written
         // here), then S_0 = S_1 - K_0^T V_0
         const bf16x8 ones = ones_frag<bf16>();
-        auto state_step = [&](int b, bool sub) {
+        auto state_step = [&](int b) {
             bf16x8 vt[2], kt[2];
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
                 vt[kc] = tfrag_tr(tile(L::VT, b), tr_c, kc);
                 kt[kc] = tfrag_tr(tile(L::KT, b), tr_p, kc);
             }
-            const bf16x8 one = sub ? neg8(ones) : ones;
+            if constexpr (SEQ) {
+                // the block's K^T V and K^T 1 in fresh accumulators, then subtracted exactly
+                floatx4 P = zero4(), Pz = zero4();
 #pragma unroll
-            for (int kc = 0; kc < 2; ++kc) mma(Sacc, sub ? neg8(vt[kc]) : vt[kc], kt[kc]);
-            if (ct == 0) {
+                for (int kc = 0; kc < 2; ++kc) mma(P, vt[kc], kt[kc]);
+                two_diff4(Sacc, Scomp, P);
+                if (ct == 0) {
 #pragma unroll
-                for (int kc = 0; kc < 2; ++kc) mma(zr, one, kt[kc]);
+                    for (int kc = 0; kc < 2; ++kc) mma(Pz, ones, kt[kc]);
+                    float z0 = zr[0];
+                    two_diff(z0, zcomp, Pz[0]);
+                    zr[0] = z0;
+                }
+            } else {
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) mma(Sacc, vt[kc], kt[kc]);
+                if (ct == 0) {
+#pragma unroll
+                    for (int kc = 0; kc < 2; ++kc) mma(zr, ones, kt[kc]);
+                }
             }
         };
         if (SEQ) {
-            state_step(1, true);
-            write_split(tile1(L::SS, 2), tile1(L::SS, 3), Sacc, TL1.nat_at(ct));
-            write_z(zf + 64, zr);
-            state_step(0, true);
+            state_step(1);
+            write_split(tile1(L::SS, 2), tile1(L::SS, 3), Sacc + Scomp, TL1.nat_at(ct));
+            write_z(zf + 64, floatx4{zr[0] + zcomp, 0.f, 0.f, 0.f});
+            state_step(0);
         } else {
-            state_step(0, false);
+            state_step(0);
         }
         // pass-1 operands: this wave's queries (row t = r, k = feature) and its two key tiles
         bf16x8 qf[2], df[2], kfr[2][2], vfr[2][2];
@@ -258,8 +275,8 @@ __device__ __forceinline__ void bwd_c128_body(
             }
         }
         if (SEQ) {
-            write_split(tile1(L::SS, 0), tile1(L::SS, 1), Sacc, TL1.nat_at(ct));
-            write_z(zf, zr);
+            write_split(tile1(L::SS, 0), tile1(L::SS, 1), Sacc + Scomp, TL1.nat_at(ct));
+            write_z(zf, floatx4{zr[0] + zcomp, 0.f, 0.f, 0.f});
         } else {
             write_split(tile1(L::SS, 2), tile1(L::SS, 3), Sacc, TL1.nat_at(ct));
             write_z(zf + 64, zr);

@@ -85,12 +85,16 @@ __device__ __forceinline__ void fwd_c128_body(
     bf16x8 qf[2];  // this wave's 16 queries: row t = r, k = key feature
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) qf[kc] = ldfrag_g<bf16>(qr, (64 * blk + 16 * tq) * D + 32 * kc, D, lane);
-    floatx4 Sacc[2], zr[2];
+    // z is carried as the unevaluated sum zr + zc, each block's K^T 1 added exactly (two-sum):
+    // it grows with every token, and the sequence backward recovers early normalisers from the
+    // final one by subtraction, so z_out must be accurate to its last bit, not to the rounding
+    // of thousands of additions
+    floatx4 Sacc[2];
+    float zr[2], zc[2] = {0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         Sacc[i] = gload<floatx4>(sres, ((16 * pt[i] + r) * D + 16 * ct + 4 * g) * 4);
-        const float zv = ct == 0 ? gload<float>(zres, (16 * pt[i] + r) * 4) : 0.f;
-        zr[i] = floatx4{zv, zv, zv, zv};
+        zr[i] = ct == 0 ? gload<float>(zres, (16 * pt[i] + r) * 4) : 0.f;
     }
     bf16x8 kst1 = gload<bf16x8>(kr, TBYTES + tid * 16), vst1 = gload<bf16x8>(vr, TBYTES + tid * 16);
     issue_fence();
@@ -115,7 +119,7 @@ __device__ __forceinline__ void fwd_c128_body(
                 tstore_acc(STt + b * TBYTES, nat_c, pt[i], pack4(Sacc[i]));
                 if (ct == 0 && g == 0) {
                     bf16x2 hi, lo;
-                    split_pair(zr[i][0], 0.f, hi, lo);
+                    split_pair(zr[i] + zc[i], 0.f, hi, lo);
                     const int off = 2 * (16 * pt[i] + r);
                     *reinterpret_cast<bf16 *>(zrow + (2 * b) * 128 + off) = hi[0];
                     *reinterpret_cast<bf16 *>(zrow + (2 * b + 1) * 128 + off) = lo[0];
@@ -135,10 +139,16 @@ __device__ __forceinline__ void fwd_c128_body(
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
+                for (int i = 0; i < 2; ++i) mma(Sacc[i], vt[kc], kt[kc][i]);
+            if (ct == 0) {
+#pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    mma(Sacc[i], vt[kc], kt[kc][i]);
-                    if (ct == 0) mma(zr[i], ones, kt[kc][i]);
+                    floatx4 pz = zero4();  // the block's K^T 1 (all four entries equal)
+#pragma unroll
+                    for (int kc = 0; kc < 2; ++kc) mma(pz, ones, kt[kc][i]);
+                    two_sum(zr[i], zc[i], pz[0]);
                 }
+            }
         };
         // this wave's outputs for block B (its own block), in two parts:
         //   intra : scores P^T[j][t] (lane: query t = r, key j = 16 jt + 4g + i) masked to j <= t,
@@ -271,7 +281,7 @@ __device__ __forceinline__ void fwd_c128_body(
     for (int i = 0; i < 2; ++i) {
         const int p = 16 * pt[i] + r;
         __builtin_nontemporal_store(Sacc[i], reinterpret_cast<floatx4 *>(S_out + ((size_t)grp * D + p) * D + 16 * ct + 4 * g));
-        if (ct == 0 && g == 0) __builtin_nontemporal_store(zr[i][0], z_out + (size_t)grp * D + p);
+        if (ct == 0 && g == 0) __builtin_nontemporal_store(zr[i] + zc[i], z_out + (size_t)grp * D + p);
     }
 }
 

@@ -161,6 +161,27 @@ __device__ __forceinline__ floatx4 elu1_grad4(const bf16x4 &phi) {
     return r;
 }
 
+// a -= p exactly as the unevaluated sum a + c: the rounding error of the fp32 difference
+// (Knuth's two-sum on a and -p) is added to the compensation term c.
+__device__ __forceinline__ void two_diff(float &a, float &c, float p) {
+    const float x = a, y = -p;
+    const float s = x + y;
+    const float yy = s - x;
+    const float err = (x - (s - yy)) + (y - yy);
+    a = s;
+    c += err;
+}
+__device__ __forceinline__ void two_sum(float &a, float &c, float p) { two_diff(a, c, -p); }
+__device__ __forceinline__ void two_diff4(floatx4 &a, floatx4 &c, const floatx4 &p) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float ae = a[e], ce = c[e];
+        two_diff(ae, ce, p[e]);
+        a[e] = ae;
+        c[e] = ce;
+    }
+}
+
 // bf16x4 of four fp32 values (round to nearest even)
 __device__ __forceinline__ bf16x4 pack4(const floatx4 &x) {
     const bf16x2 a{(bf16)x[0], (bf16)x[1]}, b{(bf16)x[2], (bf16)x[3]};

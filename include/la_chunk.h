@@ -114,8 +114,10 @@ la_status la_chunk_bwd(const void *q, const void *k, const void *v,
  * Forward over a whole sequence: n = T / chunk consecutive chunks per group, in order,
  * with the carry passed from each chunk to the next on chip (the carry across
  * consecutive chunks of "Fractus-1B training optimization", section 2).  The result is
- * that of n chained la_chunk_fwd calls over the chunks, but no carry between chunks
- * goes through memory and the whole sequence is one launch.
+ * that of n chained la_chunk_fwd calls over the chunks (the state S bit for bit; the
+ * normaliser z carries its fp32 compensation term from chunk to chunk instead of being
+ * rounded at each boundary), but no carry between chunks goes through memory and the
+ * whole sequence is one launch.
  *   q, k, v  : [G][T][D] dt, inputs; chunk c of a group is its tokens
  *              c*chunk .. (c+1)*chunk - 1.
  *   S_in     : [G][D][D] fp32 carry before the first chunk, or NULL (zero state).

@@ -119,6 +119,25 @@ def test_fp32_wide_heads_forward(gpu):
     compare(res, run_oracle(I, False), "f32")
 
 
+# ---------------------------------------------------------------- maximum sizes
+
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+def test_longest_backward_chunk(gpu, dtype, D):
+    # the backward's limit: LA_BWD_MAX_C tokens in one call (per-token den and dden held on chip)
+    C = lac.BWD_MAX_C
+    I = inp.make_inputs(G=2, T=C, D=D, dtype=dtype, carry="prior", backward=True, seed=51)
+    say(f"[case] longest backward chunk C={C} dtype={dtype} D={D}")
+    compare(run_gpu(I, [C], True), run_oracle(I, True), dtype)
+
+
+def test_whole_sequence_in_one_forward_call(gpu):
+    # the wide-head sequence (8164 tokens, ragged 36-token tail) as a single forward chunk
+    T = 63 * 128 + 100
+    I = inp.make_inputs(G=2, T=T, D=128, dtype="bf16", carry="prior", backward=False, seed=52)
+    say(f"[case] one forward call over T={T} at D=128")
+    compare(run_gpu(I, [T], False), run_oracle(I, False), "bf16")
+
+
 # ---------------------------------------------------------------- ragged, short and long chunks
 
 @pytest.mark.parametrize("C", [1, 5, 37, 63, 64, 65, 100, 127, 128, 130, 192, 200, 256])
