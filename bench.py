@@ -57,13 +57,14 @@ def algorithmic_bytes(G, C, D, esz, carry, upstream):
 
 
 def plan_seq_launches(G, T, D, esz, carry, upstream=False):
-    """The two launches of a step through the sequence entry points: one forward over all the
-    chunks (carry in only if given, carry out) and one backward (the final carry in, the
-    upstream gradient if given, the carry gradient out); no carry between chunks moves."""
+    """The two launches of a step through the sequence entry points, as the autograd layer makes
+    them: one forward over all the chunks (carry in only if given; the final carry and its
+    remainders out) and one backward (the final carry and its remainders in, the upstream
+    gradient if given, the carry gradient out); no carry between chunks moves."""
     tok = G * T * D * esz
     carry_b = G * (D * D + D) * 4
-    fwd = 4 * tok + (carry_b if carry else 0) + carry_b
-    bwd = 7 * tok + carry_b + (carry_b if upstream else 0) + carry_b
+    fwd = 4 * tok + (carry_b if carry else 0) + 2 * carry_b
+    bwd = 7 * tok + 2 * carry_b + (carry_b if upstream else 0) + carry_b
     return [("seqfwd", T, fwd, 0), ("seqbwd", T, bwd, 0)]
 
 
@@ -306,6 +307,7 @@ def main():
             s["seq"] = {x: I[x].to(dev).contiguous() for x in ("q", "k", "v", "dO")}
             q = s["seq"]["q"]
             s["seq"]["fout"] = (torch.empty_like(q), torch.empty((G, D, D), device=dev),
+                                torch.empty((G, D), device=dev), torch.empty((G, D, D), device=dev),
                                 torch.empty((G, D), device=dev))
             s["seq"]["bout"] = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q),
                                 torch.empty((G, D, D), device=dev), torch.empty((G, D), device=dev))
@@ -335,12 +337,13 @@ def main():
     def launch(s, kind, i):
         if kind == "seqfwd":
             x = s["seq"]
-            lac.seq_fwd(x["q"], x["k"], x["v"], s["S_in"], s["z_in"], out=x["fout"], feature=args.feature)
+            lac.seq_fwd(x["q"], x["k"], x["v"], s["S_in"], s["z_in"], out=x["fout"], feature=args.feature,
+                        residual=True)
             return
         if kind == "seqbwd":
             x = s["seq"]
             lac.seq_bwd(x["q"], x["k"], x["v"], x["fout"][1], x["fout"][2], x["dO"], out=x["bout"],
-                        feature=args.feature)
+                        feature=args.feature, S_res=x["fout"][3], z_res=x["fout"][4])
             return
         c = s["chunks"][i]
         S, z = carry_in(s, i)

@@ -71,9 +71,9 @@ def load_library():
         lib.la_kernel_name.restype = ctypes.c_char_p
         lib.la_kernel_name.argtypes = [i, i, i, i]
         lib.la_seq_fwd.restype = i
-        lib.la_seq_fwd.argtypes = [vp] * 8 + [i] * 7 + [vp]
+        lib.la_seq_fwd.argtypes = [vp] * 10 + [i] * 7 + [vp]
         lib.la_seq_bwd.restype = i
-        lib.la_seq_bwd.argtypes = [vp] * 13 + [i] * 7 + [vp]
+        lib.la_seq_bwd.argtypes = [vp] * 15 + [i] * 7 + [vp]
         lib.la_seq_kernel_name.restype = ctypes.c_char_p
         lib.la_seq_kernel_name.argtypes = [i, i, i, i, i]
         _lib = lib
@@ -116,11 +116,22 @@ def seq_kernel_name(backward: bool, dtype, chunk: int, D: int, feature=None):
     return None if name is None else name.decode()
 
 
-def seq_supported(dtype, T: int, D: int, chunk: int) -> bool:
+SEQ_D64_MAX_T = 1 << 20    # LA_SEQ_D64_MAX_T
+SEQ_D128_MAX_T = 16384     # LA_SEQ_D128_MAX_T
+
+
+def seq_supported(dtype, T: int, D: int, chunk: int, feature=None) -> bool:
     """Whether seq_fwd / seq_bwd take a (G, T, D) sequence in chunks of ``chunk`` tokens:
-    bf16, D = 64, 128-token chunks, whole chunks only (T below 2^24)."""
-    return (_dt_code(dtype) == LA_BF16 and D == 64 and chunk == 128 and T > 0 and T % chunk == 0
-            and T < (1 << 24))
+    bf16, and either D = 64 with 128-token chunks, whole chunks only (T up to SEQ_D64_MAX_T), or
+    D = 128 with chunks a multiple of 64 tokens, the last one possibly shorter, T up to
+    SEQ_D128_MAX_T and no fused feature map."""
+    if _dt_code(dtype) != LA_BF16 or T < 1:
+        return False
+    if D == 64:
+        return chunk == 128 and T % chunk == 0 and T <= SEQ_D64_MAX_T
+    if D == 128:
+        return chunk >= 64 and chunk % 64 == 0 and T <= SEQ_D128_MAX_T and _feature_code(feature) == 0
+    return False
 
 
 def time_next_launch(start_event, stop_event):
@@ -237,10 +248,13 @@ def bwd(q, k, v, S_in, z_in, dO, dS_out=None, dz_out=None, block: int = 64, out=
     return dq, dk, dv, dS_in, dz_in
 
 
-def seq_fwd(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int = 64, out=None, feature=None):
+def seq_fwd(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int = 64, out=None, feature=None,
+            residual: bool = False):
     """Forward over a whole (G, T, D) sequence of chunks in one launch, carry on chip:
     returns (o, S_out, z_out), equal to chaining fwd over the chunks.  ``feature="elu1"``
-    takes raw q, k and applies elu(x) + 1 inside."""
+    takes raw q, k and applies elu(x) + 1 inside.  ``residual=True`` also returns the final
+    carry's remainders (S_res, z_res): its exact value is S_out + S_res, z_out + z_res, and
+    seq_bwd takes them to recover the early states accurately."""
     lib = _lib or load_library()
     G, T, D, dev = _validate_tokens(("q", "k", "v"), (q, k, v))
     if (S_in is None) != (z_in is None):
@@ -252,18 +266,22 @@ def seq_fwd(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int = 64, ou
         o = torch.empty_like(q)
         S_out = torch.empty((G, D, D), dtype=torch.float32, device=q.device)
         z_out = torch.empty((G, D), dtype=torch.float32, device=q.device)
+        S_res = torch.empty((G, D, D), dtype=torch.float32, device=q.device) if residual else None
+        z_res = torch.empty((G, D), dtype=torch.float32, device=q.device) if residual else None
     else:
-        o, S_out, z_out = out
+        o, S_out, z_out, S_res, z_res = out if residual else (*out, None, None)
     _check("la_seq_fwd", lib.la_seq_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(S_in), _ptr(z_in),
-                                        o.data_ptr(), S_out.data_ptr(), z_out.data_ptr(), G, T, D, int(chunk),
-                                        int(block), _feature_code(feature), _dtype_code(q), _stream(dev)))
-    return o, S_out, z_out
+                                        o.data_ptr(), S_out.data_ptr(), z_out.data_ptr(), _ptr(S_res), _ptr(z_res),
+                                        G, T, D, int(chunk), int(block), _feature_code(feature), _dtype_code(q),
+                                        _stream(dev)))
+    return (o, S_out, z_out, S_res, z_res) if residual else (o, S_out, z_out)
 
 
 def seq_bwd(q, k, v, S_last, z_last, dO, dS_out=None, dz_out=None, chunk: int = 128, block: int = 64, out=None,
-            feature=None):
+            feature=None, S_res=None, z_res=None):
     """Backward over a whole sequence in one launch, last chunk first, reverse state on chip.
-    (S_last, z_last) is the carry after the last chunk: seq_fwd's (S_out, z_out).
+    (S_last, z_last) is the carry after the last chunk: seq_fwd's (S_out, z_out); (S_res,
+    z_res), optional, its remainders from seq_fwd(..., residual=True).
     Returns (dq, dk, dv, dS_in, dz_in); with ``feature="elu1"`` dq and dk are the gradients
     of the raw inputs."""
     lib = _lib or load_library()
@@ -276,6 +294,10 @@ def seq_bwd(q, k, v, S_last, z_last, dO, dS_out=None, dz_out=None, chunk: int = 
     _validate_state("z_last", z_last, (G, D), dev)
     _validate_state("dS_out", dS_out, (G, D, D), dev)
     _validate_state("dz_out", dz_out, (G, D), dev)
+    if (S_res is None) != (z_res is None):
+        raise ValueError("S_res and z_res must be given together")
+    _validate_state("S_res", S_res, (G, D, D), dev)
+    _validate_state("z_res", z_res, (G, D), dev)
     if out is None:
         import torch
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
@@ -284,7 +306,8 @@ def seq_bwd(q, k, v, S_last, z_last, dO, dS_out=None, dz_out=None, chunk: int = 
     else:
         dq, dk, dv, dS_in, dz_in = out
     _check("la_seq_bwd", lib.la_seq_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), S_last.data_ptr(),
-                                        z_last.data_ptr(), dO.data_ptr(), _ptr(dS_out), _ptr(dz_out),
+                                        z_last.data_ptr(), _ptr(S_res), _ptr(z_res), dO.data_ptr(), _ptr(dS_out),
+                                        _ptr(dz_out),
                                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dS_in.data_ptr(),
                                         dz_in.data_ptr(), G, T, D, int(chunk), int(block), _feature_code(feature),
                                         _dtype_code(q), _stream(dev)))

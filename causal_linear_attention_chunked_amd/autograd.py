@@ -8,9 +8,9 @@ from one chunk to the next.  This module gives that op a backward:
 
 q, k, v are (G, T, D) CUDA tensors (bf16 or fp32; q and k already positive, e.g.
 elu(x) + 1); S_in (G, D, D) and z_in (G, D) are fp32 or None for a zero carry.
-Where the library's sequence entry points take the shape (bf16, D = 64, whole
-128-token chunks) the sequence is one forward and one backward launch with the
-carry kept on chip; otherwise every chunk is one forward launch and its backward
+Where the library's sequence entry points take the shape (bf16; D = 64 in whole
+128-token chunks, or D = 128 in chunks of a multiple of 64 tokens) the sequence is
+one forward and one backward launch with the carry kept on chip; otherwise every chunk is one forward launch and its backward
 one backward launch that recomputes the chunk from its saved inputs (q, k, v and
 the carry that fed it).  Either way nothing of size (G, C, D, D) or (G, C, C) is
 kept between the passes, the memory-flat principle of the page's section 1.  Gradients flow to q, k, v and,
@@ -63,21 +63,22 @@ class ChunkFunction(torch.autograd.Function):
 
 class SeqFunction(torch.autograd.Function):
     """A whole sequence of chunks in one launch per direction (the library's sequence entry
-    points); saves the inputs and the final carry, from which the backward recovers the
-    state before each chunk."""
+    points); saves the inputs and the final carry with its remainders, from which the
+    backward recovers the state before each chunk."""
 
     @staticmethod
     def forward(ctx, q, k, v, S_in, z_in, chunk, block, feature):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o, S_out, z_out = _seq_fwd(q, k, v, S_in, z_in, chunk, block, feature=feature)
+        o, S_out, z_out, S_res, z_res = _seq_fwd(q, k, v, S_in, z_in, chunk, block, feature=feature,
+                                                 residual=True)
         ctx.chunk, ctx.block, ctx.feature = chunk, block, feature
         ctx.has_carry = S_in is not None
-        ctx.save_for_backward(q, k, v, S_out, z_out)
+        ctx.save_for_backward(q, k, v, S_out, z_out, S_res, z_res)
         return o, S_out, z_out
 
     @staticmethod
     def backward(ctx, do, dS_out, dz_out):
-        q, k, v, S_out, z_out = ctx.saved_tensors
+        q, k, v, S_out, z_out, S_res, z_res = ctx.saved_tensors
         G, T, D = q.shape
         if do is None:
             do = torch.zeros_like(q)
@@ -88,7 +89,7 @@ class SeqFunction(torch.autograd.Function):
         dS_out = None if dS_out is None else dS_out.float().contiguous()
         dz_out = None if dz_out is None else dz_out.float().contiguous()
         dq, dk, dv, dS_in, dz_in = _seq_bwd(q, k, v, S_out, z_out, do.to(q.dtype).contiguous(), dS_out, dz_out,
-                                            ctx.chunk, ctx.block, feature=ctx.feature)
+                                            ctx.chunk, ctx.block, feature=ctx.feature, S_res=S_res, z_res=z_res)
         if not ctx.has_carry:
             dS_in = dz_in = None
         return dq, dk, dv, dS_in, dz_in, None, None, None
@@ -114,8 +115,9 @@ def linear_attention(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int
     T = q.shape[1]
     if T == 0:
         return q.new_empty(q.shape), (S_in, z_in)
-    seq_ok = _seq_supported(q.dtype, T, q.shape[2], chunk) and block == 64
-    if feature_map not in (None, "none"):
+    fm = None if feature_map in (None, "none") else feature_map
+    seq_ok = _seq_supported(q.dtype, T, q.shape[2], chunk, fm) and block == 64
+    if fm is not None:
         if not seq_ok:
             raise ValueError(f"the fused feature map {feature_map!r} runs in the sequence kernels only "
                              "(bf16, D = 64, whole 128-token chunks)")

@@ -32,6 +32,8 @@ Span span(const void *p, size_t bytes) {
 
 bool aligned16(const void *p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+constexpr int BK_TOKENS = 64;  // the block of the blocked form
+
 struct Sizes {
     size_t tok, st, z;  // bytes of one token tensor, one state tensor, one normaliser
 };
@@ -61,12 +63,18 @@ la_status common_checks(int G, int C, int D, int block, la_dtype dt, Sizes *sz) 
     return LA_OK;
 }
 
-// Sequence entry points: the supported set (bf16, D = 64, 128-token chunks, whole chunks).
-la_status seq_checks(int G, int T, int D, int chunk, int block, la_dtype dt, Sizes *sz) {
+// Sequence entry points: the supported sets.  D = 64: bf16, 128-token chunks, whole chunks, T
+// up to LA_SEQ_D64_MAX_T.  D = 128: bf16, chunks a multiple of the 64-token block (the last one
+// may be ragged), T up to LA_SEQ_D128_MAX_T, no fused feature map.
+la_status seq_checks(int G, int T, int D, int chunk, int block, la_dtype dt, la_feature feature, Sizes *sz) {
     if (G < 1 || T < 1 || chunk < 1) return LA_ERR_INVALID;
+    if (feature != LA_FEATURE_NONE && feature != LA_FEATURE_ELU1) return LA_ERR_INVALID;
     la_status st = common_checks(G, chunk, D, block, dt, sz);
     if (st != LA_OK) return st;
-    if (dt != LA_BF16 || D != 64 || chunk != 128 || T % chunk != 0 || T >= (1 << 24)) return LA_ERR_UNSUPPORTED;
+    if (dt != LA_BF16) return LA_ERR_UNSUPPORTED;
+    if (D == 64 && (chunk != 128 || T % chunk != 0 || T > LA_SEQ_D64_MAX_T)) return LA_ERR_UNSUPPORTED;
+    if (D == 128 && (chunk % BK_TOKENS != 0 || T > LA_SEQ_D128_MAX_T || feature != LA_FEATURE_NONE))
+        return LA_ERR_UNSUPPORTED;
     size_t a, b;
     if (!mul_ok((size_t)G, (size_t)T, &a) || !mul_ok(a, (size_t)D * 2, &b)) return LA_ERR_INVALID;
     sz->tok = b;
@@ -156,52 +164,58 @@ la_status la_chunk_bwd(const void *q, const void *k, const void *v, const float 
 }
 
 la_status la_seq_fwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in, void *o,
-                     float *S_out, float *z_out, int G, int T, int D, int chunk, int block, la_feature feature,
-                     la_dtype dt, void *stream) {
+                     float *S_out, float *z_out, float *S_res, float *z_res, int G, int T, int D, int chunk,
+                     int block, la_feature feature, la_dtype dt, void *stream) {
     const TakenEvents te;
     Sizes sz;
-    if (feature != LA_FEATURE_NONE && feature != LA_FEATURE_ELU1) return LA_ERR_INVALID;
-    la_status st = seq_checks(G, T, D, chunk, block, dt, &sz);
+    la_status st = seq_checks(G, T, D, chunk, block, dt, feature, &sz);
     if (st != LA_OK) return st;
     if (!q || !k || !v || !o || !S_out || !z_out) return LA_ERR_INVALID;
-    if ((S_in == nullptr) != (z_in == nullptr)) return LA_ERR_INVALID;
-    const void *ptrs[] = {q, k, v, S_in, z_in, o, S_out, z_out};
+    if ((S_in == nullptr) != (z_in == nullptr) || (S_res == nullptr) != (z_res == nullptr)) return LA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, S_in, z_in, o, S_out, z_out, S_res, z_res};
     for (const void *p : ptrs)
         if (!aligned16(p)) return LA_ERR_ALIGN;
     const Span in[] = {span(q, sz.tok), span(k, sz.tok), span(v, sz.tok), span(S_in, sz.st), span(z_in, sz.z)};
-    const Span out[] = {span(o, sz.tok), span(S_out, sz.st), span(z_out, sz.z)};
-    st = alias_checks(in, 5, out, 3);
+    const Span out[] = {span(o, sz.tok), span(S_out, sz.st), span(z_out, sz.z), span(S_res, sz.st),
+                        span(z_res, sz.z)};
+    st = alias_checks(in, 5, out, 5);
     if (st != LA_OK) return st;
-    const hipError_t e = lachunk::launch_seq_fwd_c128(q, k, v, S_in, z_in, o, S_out, z_out, G, T / chunk,
-                                                      feature == LA_FEATURE_ELU1,
-                                                      reinterpret_cast<hipStream_t>(stream), te.ev);
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // D = 128: the general forward's sequence mode walks the whole sequence in one pass
+    const hipError_t e =
+        D == 128 ? lachunk::launch_seq_fwd_d128(q, k, v, S_in, z_in, o, S_out, z_out, S_res, z_res, G, T, s, te.ev)
+                 : lachunk::launch_seq_fwd_c128(q, k, v, S_in, z_in, o, S_out, z_out, S_res, z_res, G, T / chunk,
+                                                feature == LA_FEATURE_ELU1, s, te.ev);
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
 la_status la_seq_bwd(const void *q, const void *k, const void *v, const float *S_last, const float *z_last,
-                     const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
-                     float *dS_in, float *dz_in, int G, int T, int D, int chunk, int block, la_feature feature,
-                     la_dtype dt, void *stream) {
+                     const float *S_res, const float *z_res, const void *dO, const float *dS_out,
+                     const float *dz_out, void *dq, void *dk, void *dv, float *dS_in, float *dz_in, int G, int T,
+                     int D, int chunk, int block, la_feature feature, la_dtype dt, void *stream) {
     const TakenEvents te;
     Sizes sz;
-    if (feature != LA_FEATURE_NONE && feature != LA_FEATURE_ELU1) return LA_ERR_INVALID;
-    la_status st = seq_checks(G, T, D, chunk, block, dt, &sz);
+    la_status st = seq_checks(G, T, D, chunk, block, dt, feature, &sz);
     if (st != LA_OK) return st;
     if (!q || !k || !v || !S_last || !z_last || !dO || !dq || !dk || !dv || !dS_in || !dz_in) return LA_ERR_INVALID;
-    if ((dS_out == nullptr) != (dz_out == nullptr)) return LA_ERR_INVALID;
-    const void *ptrs[] = {q, k, v, S_last, z_last, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in};
+    if ((dS_out == nullptr) != (dz_out == nullptr) || (S_res == nullptr) != (z_res == nullptr))
+        return LA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, S_last, z_last, S_res, z_res, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in};
     for (const void *p : ptrs)
         if (!aligned16(p)) return LA_ERR_ALIGN;
-    const Span in[] = {span(q, sz.tok),    span(k, sz.tok),     span(v, sz.tok),     span(S_last, sz.st),
-                       span(z_last, sz.z), span(dO, sz.tok),    span(dS_out, sz.st), span(dz_out, sz.z)};
+    const Span in[] = {span(q, sz.tok),     span(k, sz.tok),     span(v, sz.tok),    span(S_last, sz.st),
+                       span(z_last, sz.z),  span(S_res, sz.st),  span(z_res, sz.z),  span(dO, sz.tok),
+                       span(dS_out, sz.st), span(dz_out, sz.z)};
     const Span out[] = {span(dq, sz.tok), span(dk, sz.tok), span(dv, sz.tok), span(dS_in, sz.st),
                         span(dz_in, sz.z)};
-    st = alias_checks(in, 8, out, 5);
+    st = alias_checks(in, 10, out, 5);
     if (st != LA_OK) return st;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const hipError_t e =
-        lachunk::launch_seq_bwd_c128(q, k, v, S_last, z_last, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, G,
-                                     T / chunk, feature == LA_FEATURE_ELU1, reinterpret_cast<hipStream_t>(stream),
-                                     te.ev);
+        D == 128 ? lachunk::launch_seq_bwd_d128(q, k, v, S_last, z_last, S_res, z_res, dO, dS_out, dz_out, dq, dk,
+                                                dv, dS_in, dz_in, G, T, s, te.ev)
+                 : lachunk::launch_seq_bwd_c128(q, k, v, S_last, z_last, S_res, z_res, dO, dS_out, dz_out, dq, dk,
+                                                dv, dS_in, dz_in, G, T / chunk, feature == LA_FEATURE_ELU1, s, te.ev);
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
@@ -228,6 +242,8 @@ const char *la_kernel_name(int backward, la_dtype dt, int C, int D) {
 }
 
 const char *la_seq_kernel_name(int backward, la_dtype dt, int chunk, int D, la_feature feature) {
+    if (dt == LA_BF16 && D == 128 && chunk >= BK_TOKENS && chunk % BK_TOKENS == 0 && feature == LA_FEATURE_NONE)
+        return backward ? "la_seq_bwd_d128_kernel" : "la_fwd_kernel";  // the forward: its sequence mode
     if (dt != LA_BF16 || D != 64 || chunk != 128) return nullptr;
     if (feature == LA_FEATURE_ELU1) return backward ? "la_seq_bwd_c128w16_elu1_kernel" : "la_seq_fwd_c128_elu1_kernel";
     if (feature != LA_FEATURE_NONE) return nullptr;

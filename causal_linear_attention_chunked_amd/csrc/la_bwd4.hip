@@ -77,10 +77,13 @@ struct Bwd4Lds {
 }  // namespace
 
 // S_in, z_in: the carry before the chunk (single chunk) or after the last chunk (SEQ).
+// S_res, z_res (SEQ, may be NULL): the remainders of the final carry, whose exact value is
+// S_in + S_res, z_in + z_res.
 template <bool SEQ, bool FM>
 __device__ __forceinline__ void bwd_c128_body(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const float *__restrict__ S_in, const float *__restrict__ z_in, const bf16 *__restrict__ dO,
+    const float *__restrict__ S_in, const float *__restrict__ z_in, const float *__restrict__ S_res,
+    const float *__restrict__ z_res, const bf16 *__restrict__ dO,
     const float *__restrict__ dS_out, const float *__restrict__ dz_out,
     bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
     float *__restrict__ dS_in, float *__restrict__ dz_in, int nchunk) {
@@ -121,6 +124,8 @@ __device__ __forceinline__ void bwd_c128_body(
     const GRes zres(z_in ? (const void *)(z_in + (size_t)grp * D) : dummy, z_in ? D * 4 : 0);
     const GRes shres(dS_out ? (const void *)(dS_out + (size_t)grp * D * D) : dummy, dS_out ? D * D * 4 : 0);
     const GRes zhres(dz_out ? (const void *)(dz_out + (size_t)grp * D) : dummy, dz_out ? D * 4 : 0);
+    const GRes srres(S_res ? (const void *)(S_res + (size_t)grp * D * D) : dummy, S_res ? D * D * 4 : 0);
+    const GRes zrres(z_res ? (const void *)(z_res + (size_t)grp * D) : dummy, z_res ? D * 4 : 0);
 
     // ---- prologue: every load issued before anything waits.  Thread tid stages 16 bytes of
     // Q, K, V and dO of block tid / 512.
@@ -142,11 +147,15 @@ __device__ __forceinline__ void bwd_c128_body(
     // final carry it is recovered from (z grows with every token), so the plain fp32 differences
     // would leave errors relative to the final carry; the compensation terms keep the rounding
     // error of every subtraction (an exact two-difference), leaving the state accurate relative
-    // to itself.
+    // to itself.  They start from the final carry's remainders when those are given.
     floatx4 Scomp = zero4();
     float zcomp = 0.f;  // the four entries of z's accumulator are equal; one is carried
     {
         const uint32_t so = ((16 * pt + r) * D + 16 * ct + 4 * g) * 4;
+        if (SEQ) {
+            Scomp = gload<floatx4>(srres, so);
+            zcomp = ct == 0 ? gload<float>(zrres, (16 * pt + r) * 4) : 0.f;
+        }
         Sacc = gload<floatx4>(sres, so);
         Sh = gload<floatx4>(shres, so);
         const float a = ct == 0 ? gload<float>(zres, (16 * pt + r) * 4) : 0.f;
@@ -569,26 +578,31 @@ __global__ __launch_bounds__(W16_THREADS, 1) void la_bwd_c128w16_kernel(
     const float *__restrict__ dS_out, const float *__restrict__ dz_out,
     bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
     float *__restrict__ dS_in, float *__restrict__ dz_in) {
-    bwd_c128_body<false, false>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, 1);
+    bwd_c128_body<false, false>(q, k, v, S_in, z_in, nullptr, nullptr, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in,
+                                1);
 }
 
 __global__ __launch_bounds__(W16_THREADS, 1) void la_seq_bwd_c128w16_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const float *__restrict__ S_last, const float *__restrict__ z_last, const bf16 *__restrict__ dO,
+    const float *__restrict__ S_last, const float *__restrict__ z_last, const float *__restrict__ S_res,
+    const float *__restrict__ z_res, const bf16 *__restrict__ dO,
     const float *__restrict__ dS_out, const float *__restrict__ dz_out,
     bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
     float *__restrict__ dS_in, float *__restrict__ dz_in, int nchunk) {
-    bwd_c128_body<true, false>(q, k, v, S_last, z_last, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, nchunk);
+    bwd_c128_body<true, false>(q, k, v, S_last, z_last, S_res, z_res, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in,
+                               nchunk);
 }
 
 // the same with the feature map fused: dq and dk are the gradients of the raw inputs
 __global__ __launch_bounds__(W16_THREADS, 1) void la_seq_bwd_c128w16_elu1_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const float *__restrict__ S_last, const float *__restrict__ z_last, const bf16 *__restrict__ dO,
+    const float *__restrict__ S_last, const float *__restrict__ z_last, const float *__restrict__ S_res,
+    const float *__restrict__ z_res, const bf16 *__restrict__ dO,
     const float *__restrict__ dS_out, const float *__restrict__ dz_out,
     bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
     float *__restrict__ dS_in, float *__restrict__ dz_in, int nchunk) {
-    bwd_c128_body<true, true>(q, k, v, S_last, z_last, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, nchunk);
+    bwd_c128_body<true, true>(q, k, v, S_last, z_last, S_res, z_res, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in,
+                              nchunk);
 }
 
 hipError_t launch_bwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
@@ -601,12 +615,14 @@ hipError_t launch_bwd_c128(const void *q, const void *k, const void *v, const fl
 }
 
 hipError_t launch_seq_bwd_c128(const void *q, const void *k, const void *v, const float *S_last,
-                               const float *z_last, const void *dO, const float *dS_out, const float *dz_out,
-                               void *dq, void *dk, void *dv, float *dS_in, float *dz_in, int G, int nchunk,
-                               bool elu1, hipStream_t stream, const hipEvent_t ev[2]) {
+                               const float *z_last, const float *S_res, const float *z_res, const void *dO,
+                               const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv, float *dS_in,
+                               float *dz_in, int G, int nchunk, bool elu1, hipStream_t stream,
+                               const hipEvent_t ev[2]) {
     hipExtLaunchKernelGGL(elu1 ? la_seq_bwd_c128w16_elu1_kernel : la_seq_bwd_c128w16_kernel, dim3((unsigned)G),
-                          dim3(W16_THREADS), 0, stream, ev[0], ev[1], 0, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_last, z_last, (const bf16 *)dO,
-                          dS_out, dz_out, (bf16 *)dq, (bf16 *)dk, (bf16 *)dv, dS_in, dz_in, nchunk);
+                          dim3(W16_THREADS), 0, stream, ev[0], ev[1], 0, (const bf16 *)q, (const bf16 *)k,
+                          (const bf16 *)v, S_last, z_last, S_res, z_res, (const bf16 *)dO, dS_out, dz_out, (bf16 *)dq,
+                          (bf16 *)dk, (bf16 *)dv, dS_in, dz_in, nchunk);
     return hipGetLastError();
 }
 

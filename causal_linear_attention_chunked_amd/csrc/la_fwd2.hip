@@ -52,7 +52,8 @@ template <bool SEQ, bool FM>
 __device__ __forceinline__ void fwd_c128_body(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ S_in, const float *__restrict__ z_in,
-    bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out, int nchunk) {
+    bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out, float *__restrict__ S_res,
+    float *__restrict__ z_res, int nchunk) {
     using L = Fwd2Lds;
     constexpr int D = 64, C = 128;
     constexpr uint32_t CHUNK = C * D * 2;
@@ -89,7 +90,10 @@ __device__ __forceinline__ void fwd_c128_body(
     // it grows with every token, and the sequence backward recovers early normalisers from the
     // final one by subtraction, so z_out must be accurate to its last bit, not to the rounding
     // of thousands of additions
-    floatx4 Sacc[2];
+    // In sequence mode S is carried the same way (Sacc + Scomp): the sequence backward recovers
+    // the early states from the final carry, which must then be exact beyond its rounding
+    // (the remainder goes out as S_res, z_res).
+    floatx4 Sacc[2], Scomp[2] = {zero4(), zero4()};
     float zr[2], zc[2] = {0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -116,7 +120,7 @@ __device__ __forceinline__ void fwd_c128_body(
         auto write_state = [&](int b) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                tstore_acc(STt + b * TBYTES, nat_c, pt[i], pack4(Sacc[i]));
+                tstore_acc(STt + b * TBYTES, nat_c, pt[i], pack4(SEQ ? Sacc[i] + Scomp[i] : Sacc[i]));
                 if (ct == 0 && g == 0) {
                     bf16x2 hi, lo;
                     split_pair(zr[i] + zc[i], 0.f, hi, lo);
@@ -136,10 +140,16 @@ __device__ __forceinline__ void fwd_c128_body(
 #pragma unroll
                 for (int i = 0; i < 2; ++i) kt[kc][i] = tfrag_tr(Kt + b * TBYTES, tr_p[i], kc);
             }
+            // sequence mode: the block's K^T V in fresh accumulators, added with a two-sum
+            floatx4 P[2] = {zero4(), zero4()};
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-                for (int i = 0; i < 2; ++i) mma(Sacc[i], vt[kc], kt[kc][i]);
+                for (int i = 0; i < 2; ++i) mma(SEQ ? P[i] : Sacc[i], vt[kc], kt[kc][i]);
+            if constexpr (SEQ) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) two_sum4(Sacc[i], Scomp[i], P[i]);
+            }
             if (ct == 0) {
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
@@ -280,8 +290,25 @@ __device__ __forceinline__ void fwd_c128_body(
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int p = 16 * pt[i] + r;
-        __builtin_nontemporal_store(Sacc[i], reinterpret_cast<floatx4 *>(S_out + ((size_t)grp * D + p) * D + 16 * ct + 4 * g));
-        if (ct == 0 && g == 0) __builtin_nontemporal_store(zr[i] + zc[i], z_out + (size_t)grp * D + p);
+        const size_t so = ((size_t)grp * D + p) * D + 16 * ct + 4 * g;
+        float zs, zres;
+        fold(zr[i], zc[i], zs, zres);
+        if constexpr (SEQ) {
+            floatx4 s, res;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float a, b;
+                fold(Sacc[i][e], Scomp[i][e], a, b);
+                s[e] = a;
+                res[e] = b;
+            }
+            __builtin_nontemporal_store(s, reinterpret_cast<floatx4 *>(S_out + so));
+            if (S_res) __builtin_nontemporal_store(res, reinterpret_cast<floatx4 *>(S_res + so));
+            if (ct == 0 && g == 0 && z_res) __builtin_nontemporal_store(zres, z_res + (size_t)grp * D + p);
+        } else {
+            __builtin_nontemporal_store(Sacc[i], reinterpret_cast<floatx4 *>(S_out + so));
+        }
+        if (ct == 0 && g == 0) __builtin_nontemporal_store(zs, z_out + (size_t)grp * D + p);
     }
 }
 
@@ -289,23 +316,25 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ S_in, const float *__restrict__ z_in,
     bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out) {
-    fwd_c128_body<false, false>(q, k, v, S_in, z_in, o, S_out, z_out, 1);
+    fwd_c128_body<false, false>(q, k, v, S_in, z_in, o, S_out, z_out, nullptr, nullptr, 1);
 }
 
 // two workgroups per CU: one computes while the other waits at a barrier
 __global__ __launch_bounds__(NTHR, 2) void la_seq_fwd_c128_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ S_in, const float *__restrict__ z_in,
-    bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out, int nchunk) {
-    fwd_c128_body<true, false>(q, k, v, S_in, z_in, o, S_out, z_out, nchunk);
+    bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out, float *__restrict__ S_res,
+    float *__restrict__ z_res, int nchunk) {
+    fwd_c128_body<true, false>(q, k, v, S_in, z_in, o, S_out, z_out, S_res, z_res, nchunk);
 }
 
 // the same with the feature map fused: q and k are the raw inputs x, the op uses elu(x) + 1
 __global__ __launch_bounds__(NTHR, 2) void la_seq_fwd_c128_elu1_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ S_in, const float *__restrict__ z_in,
-    bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out, int nchunk) {
-    fwd_c128_body<true, true>(q, k, v, S_in, z_in, o, S_out, z_out, nchunk);
+    bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out, float *__restrict__ S_res,
+    float *__restrict__ z_res, int nchunk) {
+    fwd_c128_body<true, true>(q, k, v, S_in, z_in, o, S_out, z_out, S_res, z_res, nchunk);
 }
 
 hipError_t launch_fwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
@@ -316,11 +345,11 @@ hipError_t launch_fwd_c128(const void *q, const void *k, const void *v, const fl
 }
 
 hipError_t launch_seq_fwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
-                               void *o, float *S_out, float *z_out, int G, int nchunk, bool elu1, hipStream_t stream,
-                               const hipEvent_t ev[2]) {
+                               void *o, float *S_out, float *z_out, float *S_res, float *z_res, int G, int nchunk,
+                               bool elu1, hipStream_t stream, const hipEvent_t ev[2]) {
     hipExtLaunchKernelGGL(elu1 ? la_seq_fwd_c128_elu1_kernel : la_seq_fwd_c128_kernel, dim3((unsigned)G), dim3(NTHR),
                           0, stream, ev[0], ev[1], 0, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_in, z_in,
-                          (bf16 *)o, S_out, z_out, nchunk);
+                          (bf16 *)o, S_out, z_out, S_res, z_res, nchunk);
     return hipGetLastError();
 }
 

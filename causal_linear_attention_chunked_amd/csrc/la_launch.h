@@ -26,13 +26,29 @@ hipError_t launch_bwd_c128(const void *q, const void *k, const void *v, const fl
 
 // The same kernels walking a group's nchunk consecutive 128-token chunks, carry on chip
 // (backward: S_last / z_last is the state after the last chunk); elu1: q and k are raw inputs
-// and the feature map elu(x) + 1 is applied inside.
+// and the feature map elu(x) + 1 is applied inside.  The final carry is exact as the unevaluated
+// sum (S_out + S_res, z_out + z_res): the forward writes the remainders where the pointers are
+// not null, the backward starts from them (null: zero).
 hipError_t launch_seq_fwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
-                               void *o, float *S_out, float *z_out, int G, int nchunk, bool elu1, hipStream_t stream,
-                               const hipEvent_t ev[2]);
-hipError_t launch_seq_bwd_c128(const void *q, const void *k, const void *v, const float *S_last,
-                               const float *z_last, const void *dO, const float *dS_out, const float *dz_out,
-                               void *dq, void *dk, void *dv, float *dS_in, float *dz_in, int G, int nchunk,
+                               void *o, float *S_out, float *z_out, float *S_res, float *z_res, int G, int nchunk,
                                bool elu1, hipStream_t stream, const hipEvent_t ev[2]);
+hipError_t launch_seq_bwd_c128(const void *q, const void *k, const void *v, const float *S_last,
+                               const float *z_last, const float *S_res, const float *z_res, const void *dO,
+                               const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv, float *dS_in,
+                               float *dz_in, int G, int nchunk, bool elu1, hipStream_t stream,
+                               const hipEvent_t ev[2]);
+
+// bf16, D = 128: the forward over a whole sequence of T tokens per group (any T >= 1; a ragged
+// end is a masked block), S and z carried with compensation, remainders out as above.
+hipError_t launch_seq_fwd_d128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
+                               void *o, float *S_out, float *z_out, float *S_res, float *z_res, int G, int T,
+                               hipStream_t stream, const hipEvent_t ev[2]);
+
+// bf16, D = 128: the backward over a whole sequence of T tokens per group (any T >= 1, the last
+// 64-token block possibly ragged), last block first, from the carry after the last token.
+hipError_t launch_seq_bwd_d128(const void *q, const void *k, const void *v, const float *S_last,
+                               const float *z_last, const float *S_res, const float *z_res, const void *dO,
+                               const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv, float *dS_in,
+                               float *dz_in, int G, int T, hipStream_t stream, const hipEvent_t ev[2]);
 
 }  // namespace lachunk

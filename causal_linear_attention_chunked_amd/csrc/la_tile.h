@@ -77,6 +77,12 @@ __device__ __forceinline__ bf16x8 tfrag(const char *tile, const TileLanes &L, in
     const char *b = tile + rt * 16 * TROW;
     return __builtin_shufflevector(lds_b64(b + L.nat[2 * kc]), lds_b64(b + L.nat[2 * kc + 1]), 0, 1, 2, 3, 4, 5, 6, 7);
 }
+// The same for a k-chunk known only at run time.
+__device__ __forceinline__ bf16x8 tfrag_at(const char *tile, const TileLanes &L, int rt, int kc) {
+    const char *b = tile + rt * 16 * TROW;
+    return __builtin_shufflevector(lds_b64(b + L.nat_at(2 * kc)), lds_b64(b + L.nat_at(2 * kc + 1)), 0, 1, 2, 3, 4, 5,
+                                   6, 7);
+}
 // Operand fragment of tile rows 16*rt..+15 in the contiguous k order: lane (r, g) holds
 // elements 32kc + 8g..+7 of its row (one 16-byte read).  Both operands of a product must
 // use the same k order; this one pairs with cfrag_g() and crowfrag().
@@ -172,6 +178,21 @@ __device__ __forceinline__ void two_diff(float &a, float &c, float p) {
     c += err;
 }
 __device__ __forceinline__ void two_sum(float &a, float &c, float p) { two_diff(a, c, -p); }
+__device__ __forceinline__ void two_sum4(floatx4 &a, floatx4 &c, const floatx4 &p) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float ae = a[e], ce = c[e];
+        two_diff(ae, ce, -p[e]);
+        a[e] = ae;
+        c[e] = ce;
+    }
+}
+// The unevaluated sum a + c as the nearest fp32 value s and the exact remainder (a - s) + c
+// (|c| <= |a|: c is a compensation term).
+__device__ __forceinline__ void fold(float a, float c, float &s, float &res) {
+    s = a + c;
+    res = (a - s) + c;
+}
 __device__ __forceinline__ void two_diff4(floatx4 &a, floatx4 &c, const floatx4 &p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {

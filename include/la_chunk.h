@@ -50,8 +50,14 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 3
+#define LA_ABI_VERSION 4
 #define LA_BWD_MAX_C 2048
+/* Longest sequences (tokens per group) of the sequence entry points, D = 64 and D = 128:
+ * the lengths at which their results are verified to the parity tolerance against an fp64
+ * reference from a zero initial carry (the hardest case for the backward, which recovers
+ * the early states from the final carry). */
+#define LA_SEQ_D64_MAX_T 1048576
+#define LA_SEQ_D128_MAX_T 16384
 
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 
@@ -114,10 +120,10 @@ la_status la_chunk_bwd(const void *q, const void *k, const void *v,
  * Forward over a whole sequence: n = T / chunk consecutive chunks per group, in order,
  * with the carry passed from each chunk to the next on chip (the carry across
  * consecutive chunks of "Fractus-1B training optimization", section 2).  The result is
- * that of n chained la_chunk_fwd calls over the chunks (the state S bit for bit; the
- * normaliser z carries its fp32 compensation term from chunk to chunk instead of being
- * rounded at each boundary), but no carry between chunks goes through memory and the
- * whole sequence is one launch.
+ * that of n chained la_chunk_fwd calls over the chunks up to fp32 rounding (the state
+ * S and the normaliser z carry their compensation terms from chunk to chunk instead of
+ * being rounded at each boundary), but no carry between chunks goes through memory and
+ * the whole sequence is one launch.
  *   q, k, v  : [G][T][D] dt, inputs; chunk c of a group is its tokens
  *              c*chunk .. (c+1)*chunk - 1.
  *   S_in     : [G][D][D] fp32 carry before the first chunk, or NULL (zero state).
@@ -125,17 +131,30 @@ la_status la_chunk_bwd(const void *q, const void *k, const void *v,
  *   o        : [G][T][D] dt, output.
  *   S_out    : [G][D][D] fp32, state after the last chunk.
  *   z_out    : [G][D]    fp32, normaliser after the last chunk.
+ *   S_res    : [G][D][D] fp32 output, or NULL: the remainder of the final state, whose
+ *              value before rounding to fp32 is the unevaluated sum S_out + S_res
+ *              (the state is carried with a compensation term through the sequence).
+ *   z_res    : [G][D]    fp32 output, or NULL; NULL together with S_res.  Likewise.
+ *              la_seq_bwd recovers the early states from the final carry; given these
+ *              remainders it starts from the exact sum instead of its fp32 rounding,
+ *              which matters for long sequences from a small initial carry.
  *   feature  : LA_FEATURE_NONE, or LA_FEATURE_ELU1: q and k hold raw inputs x and the
  *              op runs on phi(x) = elu(x) + 1 (x + 1 for x > 0, e^x otherwise),
  *              computed in fp32 as the inputs are loaded and rounded to bf16 (the
  *              positive feature map of the workloads, fused; section 1 needs q, k > 0).
- * Supported: dt == LA_BF16, D == 64, chunk == 128, block == 64 and T a positive
- * multiple of 128 below 2^24; anything else returns LA_ERR_UNSUPPORTED (chain
- * la_chunk_fwd calls instead).  A feature outside la_feature is LA_ERR_INVALID.
+ * Supported (block == 64, dt == LA_BF16):
+ *   - D == 64: chunk == 128 and T a positive multiple of 128, T <= LA_SEQ_D64_MAX_T;
+ *   - D == 128: chunk a positive multiple of 64, 1 <= T <= LA_SEQ_D128_MAX_T (the last
+ *     chunk may be shorter than chunk, as a chain's last call may be), feature ==
+ *     LA_FEATURE_NONE.  Blocks of 64 tokens start at multiples of 64 in both forms, so
+ *     the chunk length does not change the arithmetic; a ragged end is computed as a
+ *     masked block (the chained calls take it token by token: another summation order).
+ * Anything else returns LA_ERR_UNSUPPORTED (chain la_chunk_fwd calls instead).  A
+ * feature outside la_feature is LA_ERR_INVALID.
  */
 la_status la_seq_fwd(const void *q, const void *k, const void *v,
                      const float *S_in, const float *z_in,
-                     void *o, float *S_out, float *z_out,
+                     void *o, float *S_out, float *z_out, float *S_res, float *z_res,
                      int G, int T, int D, int chunk, int block, la_feature feature, la_dtype dt, void *stream);
 
 /*
@@ -150,8 +169,17 @@ la_status la_seq_fwd(const void *q, const void *k, const void *v,
  *              by subtracting the chunk's K^T V and K^T 1 (exact products of the
  *              inputs, summed in fp32), so no per-chunk carries are kept between the
  *              passes; the results differ from a chain of la_chunk_bwd calls only by
- *              that fp32 rounding.  Passing anything but the forward's outputs gives
- *              the gradient at a different initial carry.
+ *              that fp32 rounding (and, at D == 128, by the summation order of a
+ *              ragged last block: a masked block here, token by token in the chunk
+ *              call).  Passing anything but the forward's outputs gives the gradient
+ *              at a different initial carry.
+ *   S_res    : [G][D][D] fp32, or NULL: S_res of that la_seq_fwd call.
+ *   z_res    : [G][D]    fp32, or NULL; NULL together with S_res.  With them the
+ *              recovery starts from the exact final carry; without, from its fp32
+ *              rounding, whose error reaches every earlier state (relative to the
+ *              early states it grows with T: pass them for long sequences; the
+ *              length limits hold with them).  At D == 128 the state is recovered
+ *              without a compensation term (z with one), hence its shorter limit.
  *   dO       : [G][T][D] dt, gradient of o.
  *   dS_out   : [G][D][D] fp32 gradient of S_out, or NULL.
  *   dz_out   : [G][D]    fp32 gradient of z_out, or NULL; NULL together with dS_out.
@@ -164,7 +192,7 @@ la_status la_seq_fwd(const void *q, const void *k, const void *v,
  * Supported: as la_seq_fwd.
  */
 la_status la_seq_bwd(const void *q, const void *k, const void *v,
-                     const float *S_last, const float *z_last,
+                     const float *S_last, const float *z_last, const float *S_res, const float *z_res,
                      const void *dO, const float *dS_out, const float *dz_out,
                      void *dq, void *dk, void *dv, float *dS_in, float *dz_in,
                      int G, int T, int D, int chunk, int block, la_feature feature, la_dtype dt, void *stream);

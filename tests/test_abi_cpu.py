@@ -54,8 +54,14 @@ def test_kernel_names(lib):
     assert lac.kernel_name(False, "bf16", 128, 96) is None
 
 
+def test_sequence_limits_match_the_header():
+    text = open(HEADER).read()
+    for name, value in (("LA_SEQ_D64_MAX_T", lac.SEQ_D64_MAX_T), ("LA_SEQ_D128_MAX_T", lac.SEQ_D128_MAX_T)):
+        assert int(re.search(rf"#define {name} (\d+)", text).group(1)) == value, name
+
+
 def test_version_and_status_strings(lib):
-    assert lac.abi_version() == 3
+    assert lac.abi_version() == 4
     for s in range(6):
         assert len(lac.status_str(s)) > 0
     assert lac.status_str(99) == "unknown status"
@@ -126,15 +132,18 @@ def test_fwd_chunk_beyond_32bit_offsets(lib):
     assert bwd_call(lib, G=1, C=(1 << 31) // (64 * 2), D=64) == UNSUPPORTED
 
 
+SEQ_FWD_ARGS = ["q", "k", "v", "S_in", "z_in", "o", "S_out", "z_out", "S_res", "z_res"]
+
+
 def seq_fwd_call(lib, G=4, T=512, D=64, chunk=128, block=64, feature=0, dt=1, **over):
-    args = {n: addr(i) for i, n in enumerate(["q", "k", "v", "S_in", "z_in", "o", "S_out", "z_out"])}
+    args = {n: addr(i) for i, n in enumerate(SEQ_FWD_ARGS)}
     args.update(over)
-    return lib.la_seq_fwd(args["q"], args["k"], args["v"], args["S_in"], args["z_in"], args["o"],
-                          args["S_out"], args["z_out"], G, T, D, chunk, block, feature, dt, None)
+    return lib.la_seq_fwd(*[args[n] for n in SEQ_FWD_ARGS], G, T, D, chunk, block, feature, dt, None)
 
 
 def seq_bwd_call(lib, G=4, T=512, D=64, chunk=128, block=64, feature=0, dt=1, **over):
-    names = ["q", "k", "v", "S_last", "z_last", "dO", "dS_out", "dz_out", "dq", "dk", "dv", "dS_in", "dz_in"]
+    names = ["q", "k", "v", "S_last", "z_last", "S_res", "z_res", "dO", "dS_out", "dz_out", "dq", "dk", "dv",
+             "dS_in", "dz_in"]
     args = {n: addr(i) for i, n in enumerate(names)}
     args.update(over)
     return lib.la_seq_bwd(*[args[n] for n in names], G, T, D, chunk, block, feature, dt, None)
@@ -143,25 +152,34 @@ def seq_bwd_call(lib, G=4, T=512, D=64, chunk=128, block=64, feature=0, dt=1, **
 @pytest.mark.parametrize("kw,status", [
     (dict(G=0), INVALID), (dict(T=0), INVALID), (dict(chunk=0), INVALID),
     (dict(T=500), UNSUPPORTED),                          # not whole chunks
-    (dict(chunk=64, T=512), UNSUPPORTED), (dict(D=128), UNSUPPORTED), (dict(dt=0), UNSUPPORTED),
-    (dict(block=32), UNSUPPORTED), (dict(T=1 << 24), UNSUPPORTED),
+    (dict(chunk=64, T=512), UNSUPPORTED), (dict(dt=0), UNSUPPORTED),
+    # D = 128: chunks a multiple of 64, no fused feature map, T up to the limit
+    (dict(D=128, chunk=100, T=500), UNSUPPORTED), (dict(D=128, feature=1), UNSUPPORTED),
+    (dict(D=128, T=lac.SEQ_D128_MAX_T + 1), UNSUPPORTED), (dict(D=128, T=0), INVALID),
+    (dict(block=32), UNSUPPORTED), (dict(T=lac.SEQ_D64_MAX_T + 128), UNSUPPORTED),
     (dict(q=None), INVALID), (dict(S_in=None), INVALID),
     (dict(v=ctypes.c_void_p(BASE + 2 * STEP + 8)), ALIGN),
     (dict(o=addr(1)), ALIAS), (dict(S_out=addr(3)), ALIAS),
     (dict(feature=2), INVALID), (dict(feature=-1), INVALID), (dict(feature=1, D=128), UNSUPPORTED),
+    (dict(S_res=None), INVALID), (dict(z_res=None), INVALID),   # the remainders come together
+    (dict(S_res=addr(6)), ALIAS),                        # S_res == S_out
+    (dict(z_res=ctypes.c_void_p(BASE + 9 * STEP + 8)), ALIGN),
 ])
 def test_seq_fwd_rejects(lib, kw, status):
     assert seq_fwd_call(lib, **kw) == status
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(G=0), INVALID), (dict(T=384 + 1), UNSUPPORTED), (dict(D=128), UNSUPPORTED),
+    (dict(G=0), INVALID), (dict(T=384 + 1), UNSUPPORTED), (dict(D=128, chunk=96), UNSUPPORTED),
+    (dict(D=128, T=lac.SEQ_D128_MAX_T + 64), UNSUPPORTED),
     (dict(S_last=None), INVALID), (dict(z_last=None), INVALID),   # the final carry is required
     (dict(dS_out=None), INVALID),                        # dz_out without dS_out
     (dict(dq=None), INVALID),
     (dict(dk=ctypes.c_void_p(BASE + 9 * STEP + 4)), ALIGN),
     (dict(dq=addr(5)), ALIAS), (dict(dS_in=addr(3)), ALIAS),
     (dict(feature=7), INVALID),
+    (dict(z_res=None), INVALID),                         # S_res without z_res
+    (dict(dS_in=addr(5)), ALIAS),                        # dS_in == S_res
 ])
 def test_seq_bwd_rejects(lib, kw, status):
     assert seq_bwd_call(lib, **kw) == status
@@ -176,7 +194,15 @@ def test_seq_kernel_names(lib):
     with pytest.raises(ValueError):
         lac.seq_kernel_name(True, "bf16", 128, 64, "relu")
     assert lac.seq_supported("bf16", 1024, 64, 128) and not lac.seq_supported("bf16", 1000, 64, 128)
-    assert not lac.seq_supported("float32", 1024, 64, 128) and not lac.seq_supported("bf16", 1024, 128, 128)
+    assert not lac.seq_supported("float32", 1024, 64, 128) and not lac.seq_supported("float32", 1024, 128, 128)
+    assert lac.seq_kernel_name(False, "bf16", 128, 128) == "la_fwd_kernel"
+    assert lac.seq_kernel_name(True, "bf16", 64, 128) == "la_seq_bwd_d128_kernel"
+    assert lac.seq_kernel_name(True, "bf16", 128, 128, "elu1") is None
+    assert lac.seq_kernel_name(True, "bf16", 100, 128) is None
+    assert lac.seq_supported("bf16", 8164, 128, 128) and lac.seq_supported("bf16", 1, 128, 64)
+    assert not lac.seq_supported("bf16", 8164, 128, 100) and not lac.seq_supported("bf16", 16448, 128, 128)
+    assert lac.seq_supported("bf16", 1 << 20, 64, 128) and not lac.seq_supported("bf16", (1 << 20) + 128, 64, 128)
+    assert not lac.seq_supported("bf16", 1024, 128, 128, "elu1")
 
 
 def test_time_next_launch_pairs(lib):

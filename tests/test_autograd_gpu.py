@@ -74,5 +74,11 @@ def test_autograd_sequence_entry_points(gpu):
     _case("bf16", "zero", False, G=2, T=384)
 
 
+def test_autograd_sequence_entry_points_wide_heads(gpu):
+    # bf16, D = 128, 128-token chunks and a ragged end: the sequence path
+    assert lac.seq_supported("bf16", 300, 128, 128)
+    _case("bf16", "prior", True, G=2, T=300, D=128)
+
+
 def test_autograd_fused_feature_map(gpu):
     _case("bf16", "prior", True, G=3, T=384, feature_map="elu1")

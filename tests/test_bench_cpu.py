@@ -48,13 +48,14 @@ def test_ragged_wide_head_bytes():
 
 
 def test_sequence_launch_bytes():
-    # one forward and one backward over T tokens: no carry between chunks moves; the backward
-    # reads the final carry instead of per-chunk carries
+    # one forward and one backward over T tokens: no carry between chunks moves; the forward
+    # writes the final carry and its remainders, which the backward reads instead of
+    # per-chunk carries, and writes the carry gradient
     G, T, D = 1280, 1024, 64
     tok, carry = G * T * D * 2, G * (D * D + D) * 4
     L = bench.plan_seq_launches(G, T, D, 2, carry=False)
     assert [k for k, *_ in L] == ["seqfwd", "seqbwd"]
-    assert L[0][2] == 4 * tok + carry
-    assert L[1][2] == 7 * tok + 2 * carry
+    assert L[0][2] == 4 * tok + 2 * carry
+    assert L[1][2] == 7 * tok + 3 * carry
     chained = sum(b for *_, b, _ in _bytes("g1280_8x128_d64_bf16_fwdbwd"))
     assert sum(b for *_, b, _ in L) < chained
