@@ -293,7 +293,9 @@ def main():
 
     tname = w.name + ("_seq" if args.seq else "") + (f"_{args.feature}" if args.feature else "")  # and the traffic file
     if args.seq:
-        if not lac.seq_supported(w.dtype, w.T, D, max(w.chunks)) or len(set(w.chunks)) != 1:
+        # equal chunks but for a shorter last one
+        regular = len(set(w.chunks[:-1])) <= 1 and w.chunks[-1] <= w.chunks[0]
+        if not regular or not lac.seq_supported(w.dtype, w.T, D, w.chunks[0], args.feature):
             raise SystemExit(f"{w.name}: the sequence entry points do not take this workload")
         launches = plan_seq_launches(G, w.T, D, esz, carry)
     else:
