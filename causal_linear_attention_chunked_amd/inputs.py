@@ -162,3 +162,46 @@ def chunk_bounds(chunks) -> List[tuple]:
         out.append((s, s + int(c)))
         s += int(c)
     return out
+
+
+# ---------------------------------------------------------------- cross-entropy over the tied head
+
+@dataclass(frozen=True)
+class CeWorkload:
+    """One cross-entropy workload: N tokens of width d against a V-token tied head."""
+    name: str
+    N: int
+    d: int
+    V: int
+    dtype: str = "bf16"
+    w_std: float = 0.02   # the embedding's init scale
+    seed: int = 0
+
+
+# The head of "Fractus-1B training optimization" (Bottleneck #3): 50257 tokens, width 1280
+# (its 64.3M head multiply-adds per token over the vocabulary), for the B = 4 batch of 128-token
+# chunks whose fp32 logits are the page's 103 MB (4 x 128 x 50257 x 4 bytes).
+CE_WORKLOADS = {
+    "ce_n512_d1280_v50257_bf16": CeWorkload("ce_n512_d1280_v50257_bf16", N=512, d=1280, V=50257),
+}
+
+
+def ce_workload(name: str) -> CeWorkload:
+    return CE_WORKLOADS[name]
+
+
+def make_ce_inputs(N: int, d: int, V: int, dtype: str = "bf16", w_std: float = 0.02, seed: int = 0) -> dict:
+    """Hidden states ``h`` (N, d) ~ N(0, 1), the tied embedding ``W`` (V, d) ~ N(0, w_std^2), both
+    drawn in fp32 and rounded to the dtype, and ``targets`` (N,) int32 uniform over the vocabulary;
+    drawn in that order from one seeded CPU generator."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    tdt = _torch_dtype(dtype)
+    h = torch.randn((N, d), generator=gen, dtype=torch.float32).to(tdt)
+    W = (torch.randn((V, d), generator=gen, dtype=torch.float32) * w_std).to(tdt)
+    targets = torch.randint(0, V, (N,), generator=gen, dtype=torch.int64).to(torch.int32)
+    return {"h": h, "W": W, "targets": targets}
+
+
+def ce_workload_inputs(w: CeWorkload) -> dict:
+    return make_ce_inputs(w.N, w.d, w.V, w.dtype, w.w_std, w.seed)

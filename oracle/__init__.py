@@ -13,9 +13,12 @@ no code with the GPU library and never imports it.
   for tiny shapes; writes the stored golden values.
 * :mod:`oracle.features` -- the positive feature map elu(x) + 1 in front of the op
   (raw inputs in, gradients with respect to them out), by the chain rule.
+* :mod:`oracle.ce` -- the cross-entropy over the tied output head (the pages' third
+  bottleneck and its chunked, checkpointed form), fp64.
 
 Every function cites the passage of "Fractus-1B training optimization" it
 follows.  Which pins cover which function is listed in the test suite.
 """
 from .core import build, fwd, bwd, lib_path, max_threads  # noqa: F401
 from . import features  # noqa: F401
+from . import ce  # noqa: F401
