@@ -12,6 +12,9 @@ raises.  PyTorch supplies device memory and the current stream.
     dq, dk, dv, dS_in, dz_in = seq_bwd(q, k, v, S_out, z_out, dO)   # from the final carry
     time_next_launch(start_event, stop_event)   # kernel-only timing of the next call
     o, (S_out, z_out) = linear_attention(q, k, v, S_in, z_in, chunk=128)   # differentiable (autograd)
+    loss, lse = ce_fwd(h, W, targets)                   # cross-entropy over a tied head
+    dh, dW = ce_bwd(h, W, targets, lse, dloss=None, ce_chunk=0)
+    loss = chunked_cross_entropy(h, W, targets, ce_chunk)  # differentiable (autograd)
 
 q, k, v, dO: contiguous (G, C, D) (one chunk) or (G, T, D) (a sequence) CUDA
 tensors, float32 or bfloat16 (one dtype for all); S: (G, D, D) float32 with S[p][c] (p key feature, c value feature);
@@ -24,7 +27,8 @@ import os
 import threading
 
 __all__ = ["fwd", "bwd", "seq_fwd", "seq_bwd", "seq_supported", "seq_kernel_name", "chain_fwd", "chain_bwd", "linear_attention", "chunk_attention", "ChunkFunction", "LachunkError", "lib_path", "load_library",
-           "abi_version", "status_str", "time_next_launch", "kernel_name", "BWD_MAX_C"]
+           "abi_version", "status_str", "time_next_launch", "kernel_name", "BWD_MAX_C", "ce_fwd", "ce_bwd",
+           "ce_workspace_bytes", "chunked_cross_entropy"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liblachunk.so")
@@ -74,6 +78,12 @@ def load_library():
         lib.la_seq_fwd.argtypes = [vp] * 10 + [i] * 7 + [vp]
         lib.la_seq_bwd.restype = i
         lib.la_seq_bwd.argtypes = [vp] * 15 + [i] * 7 + [vp]
+        lib.la_ce_workspace_bytes.restype = ctypes.c_size_t
+        lib.la_ce_workspace_bytes.argtypes = [i] * 4
+        lib.la_ce_fwd.restype = i
+        lib.la_ce_fwd.argtypes = [vp] * 6 + [ctypes.c_size_t] + [i] * 4 + [vp]
+        lib.la_ce_bwd.restype = i
+        lib.la_ce_bwd.argtypes = [vp] * 8 + [ctypes.c_size_t] + [i] * 5 + [vp]
         lib.la_seq_kernel_name.restype = ctypes.c_char_p
         lib.la_seq_kernel_name.argtypes = [i, i, i, i, i]
         _lib = lib
@@ -314,6 +324,78 @@ def seq_bwd(q, k, v, S_last, z_last, dO, dS_out=None, dz_out=None, chunk: int = 
     return dq, dk, dv, dS_in, dz_in
 
 
+def ce_workspace_bytes(N: int, d: int, V: int, ce_chunk: int = 0) -> int:
+    """Bytes of device workspace ce_fwd / ce_bwd need (0: shape not supported)."""
+    return int(load_library().la_ce_workspace_bytes(int(N), int(d), int(V), int(ce_chunk)))
+
+
+def _ce_check(h, W, targets):
+    import torch
+    for n, t in (("h", h), ("W", W), ("targets", targets)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous CUDA tensor")
+    if h.dim() != 2 or W.dim() != 2 or h.shape[1] != W.shape[1]:
+        raise ValueError(f"h (N, d) and W (V, d) expected, got {tuple(h.shape)} and {tuple(W.shape)}")
+    if h.dtype is not torch.bfloat16 or W.dtype is not torch.bfloat16:
+        raise ValueError("h and W must be bfloat16")
+    if targets.dtype is not torch.int32 or targets.shape != (h.shape[0],):
+        raise ValueError("targets must be int32 of shape (N,)")
+    if h.device != W.device or h.device != targets.device:
+        raise ValueError("h, W and targets must be on one device")
+    return h.shape[0], h.shape[1], W.shape[0], h.get_device()
+
+
+def _workspace(ws, nbytes, dev):
+    import torch
+    if ws is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=f"cuda:{dev}")
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes, {nbytes} needed")
+    return ws
+
+
+def ce_fwd(h, W, targets, workspace=None, out=None):
+    """Mean cross-entropy of the tied head W (V, d) over the tokens h (N, d) with int32 targets:
+    returns (loss, lse), a 0-dim float32 tensor and (N,) float32.  The logits are never stored."""
+    import torch
+    lib = _lib or load_library()
+    N, d, V, dev = _ce_check(h, W, targets)
+    nbytes = ce_workspace_bytes(N, d, V, N)
+    if nbytes == 0:
+        raise LachunkError("la_ce_fwd", 2, status_str(2))
+    ws = _workspace(workspace, nbytes, dev)
+    if out is None:
+        loss = torch.empty((), dtype=torch.float32, device=h.device)
+        lse = torch.empty((N,), dtype=torch.float32, device=h.device)
+    else:
+        loss, lse = out
+    _check("la_ce_fwd", lib.la_ce_fwd(h.data_ptr(), W.data_ptr(), targets.data_ptr(), loss.data_ptr(),
+                                      lse.data_ptr(), ws.data_ptr(), nbytes, N, d, V, LA_BF16, _stream(dev)))
+    return loss, lse
+
+
+def ce_bwd(h, W, targets, lse, dloss=None, ce_chunk: int = 0, workspace=None, out=None):
+    """Gradients of dloss * loss (dloss a float32 CUDA scalar, None = 1) with respect to h and W:
+    returns (dh bf16 (N, d), dW float32 (V, d)).  The logits are recomputed ``ce_chunk`` tokens at
+    a time (0: all at once), each chunk's softmax kept in bf16 only while its products run."""
+    import torch
+    lib = _lib or load_library()
+    N, d, V, dev = _ce_check(h, W, targets)
+    nbytes = ce_workspace_bytes(N, d, V, ce_chunk)
+    if nbytes == 0:
+        raise LachunkError("la_ce_bwd", 2, status_str(2))
+    ws = _workspace(workspace, nbytes, dev)
+    if out is None:
+        dh = torch.empty_like(h)
+        dW = torch.empty((V, d), dtype=torch.float32, device=h.device)
+    else:
+        dh, dW = out
+    _check("la_ce_bwd", lib.la_ce_bwd(h.data_ptr(), W.data_ptr(), targets.data_ptr(), lse.data_ptr(), _ptr(dloss),
+                                      dh.data_ptr(), dW.data_ptr(), ws.data_ptr(), nbytes, N, d, V, int(ce_chunk),
+                                      LA_BF16, _stream(dev)))
+    return dh, dW
+
+
 def chain_fwd(q_chunks, k_chunks, v_chunks, S_in=None, z_in=None, block: int = 64):
     """Forward over consecutive chunks (lists of (G, C_i, D) tensors), carrying (S, z).
 
@@ -344,7 +426,7 @@ def chain_bwd(q_chunks, k_chunks, v_chunks, carries, dO_chunks, dS_out=None, dz_
 
 def __getattr__(name):
     # the autograd layer imports torch; load it on first use
-    if name in ("linear_attention", "chunk_attention", "ChunkFunction"):
+    if name in ("linear_attention", "chunk_attention", "ChunkFunction", "chunked_cross_entropy"):
         from . import autograd
         return getattr(autograd, name)
     raise AttributeError(f"module {__name__!r} has no attribute {name!r}")

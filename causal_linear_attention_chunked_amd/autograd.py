@@ -136,6 +136,36 @@ def linear_attention(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int
     return o, (S, z)
 
 
+class CrossEntropyFunction(torch.autograd.Function):
+    """Mean cross-entropy over a tied head; saves h, W, the targets and lse (the checkpoint) and
+    recomputes the logits in the backward, ``ce_chunk`` tokens at a time."""
+
+    @staticmethod
+    def forward(ctx, h, W, targets, ce_chunk):
+        from . import ce_fwd as _ce_fwd
+        h, W = h.contiguous(), W.contiguous()
+        loss, lse = _ce_fwd(h, W, targets)
+        ctx.ce_chunk = ce_chunk
+        ctx.save_for_backward(h, W, targets, lse)
+        return loss
+
+    @staticmethod
+    def backward(ctx, g):
+        from . import ce_bwd as _ce_bwd
+        h, W, targets, lse = ctx.saved_tensors
+        dh, dW = _ce_bwd(h, W, targets, lse, dloss=g.float().contiguous(), ce_chunk=ctx.ce_chunk)
+        return dh, dW.to(W.dtype), None, None
+
+
+def chunked_cross_entropy(h, W, targets, ce_chunk: int = 0):
+    """The pages' chunked, checkpointed cross-entropy ("Fractus-1B training optimization",
+    section 2, Opt 3): mean over the N tokens of h (N, d) of the loss of the tied head W (V, d)
+    against int32 targets, differentiable in h and W; ``ce_chunk`` tokens per backward chunk
+    (0: all).  bf16 h and W; the gradient of W is computed in fp32 and returned in W's dtype."""
+    _check_device(h)
+    return CrossEntropyFunction.apply(h, W, targets, ce_chunk)
+
+
 def _check_device(q):
     if not q.is_cuda:
         raise ValueError("linear attention runs in the HIP library: inputs must be CUDA tensors")

@@ -219,6 +219,64 @@ la_status la_seq_bwd(const void *q, const void *k, const void *v, const float *S
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
+// Cross-entropy: the supported shapes and the workspace they need (0 when unsupported).
+static la_status ce_checks(int N, int d, int V, int ce_chunk, la_dtype dt, lachunk::CeShape *s) {
+    if (N < 1 || d < 1 || V < 2) return LA_ERR_INVALID;
+    if (dt != LA_BF16 || d % 128 != 0 || d > 8192) return LA_ERR_UNSUPPORTED;
+    *s = lachunk::ce_shape(N, d, V, ce_chunk);
+    if ((size_t)V * d >= ((size_t)1 << 30) || (size_t)s->chunk_pad * s->Vpad >= ((size_t)1 << 30) ||
+        (size_t)s->Npad * d >= ((size_t)1 << 30))
+        return LA_ERR_UNSUPPORTED;
+    return LA_OK;
+}
+
+size_t la_ce_workspace_bytes(int N, int d, int V, int ce_chunk) {
+    lachunk::CeShape s;
+    return ce_checks(N, d, V, ce_chunk, LA_BF16, &s) == LA_OK ? s.ws_bytes : 0;
+}
+
+la_status la_ce_fwd(const void *h, const void *W, const int *targets, float *loss, float *lse, void *workspace,
+                    size_t workspace_bytes, int N, int d, int V, la_dtype dt, void *stream) {
+    const TakenEvents te;
+    lachunk::CeShape s;
+    la_status st = ce_checks(N, d, V, N, dt, &s);
+    if (st != LA_OK) return st;
+    if (!h || !W || !targets || !loss || !lse || !workspace) return LA_ERR_INVALID;
+    if (workspace_bytes < s.ws_bytes) return LA_ERR_INVALID;
+    const void *ptrs[] = {h, W, targets, loss, lse, workspace};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return LA_ERR_ALIGN;
+    const Span in[] = {span(h, (size_t)N * d * 2), span(W, (size_t)V * d * 2), span(targets, (size_t)N * 4)};
+    const Span out[] = {span(loss, 4), span(lse, (size_t)N * 4), span(workspace, workspace_bytes)};
+    st = alias_checks(in, 3, out, 3);
+    if (st != LA_OK) return st;
+    const hipError_t e = lachunk::launch_ce_fwd(h, W, targets, loss, lse, workspace, N, d, V,
+                                                reinterpret_cast<hipStream_t>(stream), te.ev);
+    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
+
+la_status la_ce_bwd(const void *h, const void *W, const int *targets, const float *lse, const float *dloss, void *dh,
+                    float *dW, void *workspace, size_t workspace_bytes, int N, int d, int V, int ce_chunk,
+                    la_dtype dt, void *stream) {
+    const TakenEvents te;
+    lachunk::CeShape s;
+    la_status st = ce_checks(N, d, V, ce_chunk, dt, &s);
+    if (st != LA_OK) return st;
+    if (!h || !W || !targets || !lse || !dh || !dW || !workspace) return LA_ERR_INVALID;
+    if (workspace_bytes < s.ws_bytes) return LA_ERR_INVALID;
+    const void *ptrs[] = {h, W, targets, lse, dloss, dh, dW, workspace};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return LA_ERR_ALIGN;
+    const Span in[] = {span(h, (size_t)N * d * 2), span(W, (size_t)V * d * 2), span(targets, (size_t)N * 4),
+                       span(lse, (size_t)N * 4), span(dloss, 4)};
+    const Span out[] = {span(dh, (size_t)N * d * 2), span(dW, (size_t)V * d * 4), span(workspace, workspace_bytes)};
+    st = alias_checks(in, 5, out, 3);
+    if (st != LA_OK) return st;
+    const hipError_t e = lachunk::launch_ce_bwd(h, W, targets, lse, dloss, dh, dW, workspace, N, d, V, s.chunk,
+                                                reinterpret_cast<hipStream_t>(stream), te.ev);
+    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
+
 const char *la_status_str(la_status s) {
     switch (s) {
         case LA_OK: return "ok";

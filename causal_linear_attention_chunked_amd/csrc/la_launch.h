@@ -51,4 +51,17 @@ hipError_t launch_seq_bwd_d128(const void *q, const void *k, const void *v, cons
                                const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv, float *dS_in,
                                float *dz_in, int G, int T, hipStream_t stream, const hipEvent_t ev[2]);
 
+// Cross-entropy over a tied head (bf16 h, W; fp32 loss, lse, dW; bf16 dh).  The shape of the
+// workspace: padded sizes, the backward's chunking and the split of dh over the vocabulary.
+struct CeShape {
+    int Npad, Vpad, nvt, chunk, chunk_pad, kper, nsplit;
+    size_t fwd_bytes, p_bytes, bwd_bytes, ws_bytes;
+};
+CeShape ce_shape(int N, int d, int V, int ce_chunk);
+hipError_t launch_ce_fwd(const void *h, const void *W, const int *targets, float *loss, float *lse, void *ws, int N,
+                         int d, int V, hipStream_t stream, const hipEvent_t ev[2]);
+hipError_t launch_ce_bwd(const void *h, const void *W, const int *targets, const float *lse, const float *dloss,
+                         void *dh, float *dW, void *ws, int N, int d, int V, int ce_chunk, hipStream_t stream,
+                         const hipEvent_t ev[2]);
+
 }  // namespace lachunk

@@ -46,6 +46,8 @@
 #ifndef LA_CHUNK_H
 #define LA_CHUNK_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -196,6 +198,40 @@ la_status la_seq_bwd(const void *q, const void *k, const void *v,
                      const void *dO, const float *dS_out, const float *dz_out,
                      void *dq, void *dk, void *dv, float *dS_in, float *dz_in,
                      int G, int T, int D, int chunk, int block, la_feature feature, la_dtype dt, void *stream);
+
+/*
+ * Cross-entropy over a tied output head ("Fractus-1B training optimization", section 1,
+ * Bottleneck #3: the 50257-token head; section 2, Opt 3: chunked, checkpointed cross-entropy):
+ *     logit_iv = h_i . W_v,   lse_i = log sum_v exp(logit_iv),
+ *     loss = (1/N) sum_i (lse_i - logit_{i,t_i}),
+ * and for an upstream gradient g of the loss, with P_iv = (g/N) (softmax_iv - [v = t_i]),
+ *     dh = P W,   dW = P^T h.
+ *   h        : [N][d] bf16 hidden states (dt must be LA_BF16).
+ *   W        : [V][d] bf16, the tied embedding (class v is row v).
+ *   targets  : [N] int32 class of each token, each in [0, V) (not checked on the device: a
+ *              target outside it gives a meaningless loss, nothing worse).
+ *   loss     : fp32 scalar output (the mean over the N tokens).
+ *   lse      : [N] fp32 output of the forward, input of the backward (its checkpoint: with
+ *              it the backward forms each softmax from one recomputation of the logits).
+ *   dloss    : fp32 scalar g on the device, or NULL for g = 1.
+ *   dh       : [N][d] bf16 output;  dW : [V][d] fp32 output (overwritten).
+ *   workspace: device scratch of at least la_ce_workspace_bytes(N, d, V, ce_chunk) bytes,
+ *              16-byte aligned, owned by the caller, not read by the caller; the same
+ *              workspace serves both calls (the forward's partial sums, the backward's
+ *              P of one chunk and the partial sums of dh).
+ *   ce_chunk : tokens per backward chunk (1..N; anything else means N): the chunk's P,
+ *              ce_chunk x V bf16, is the only large transient.  The logits are never
+ *              stored by the forward.
+ * Supported: dt == LA_BF16, N >= 1, V >= 2, d a multiple of 128 up to 8192, and V * d and
+ * ceil(ce_chunk / 128) * 128 * ceil(V / 128) * 128 below 2^30 (32-bit byte offsets).  Each call
+ * launches several kernels (la_time_next_launch brackets all of them).
+ */
+size_t la_ce_workspace_bytes(int N, int d, int V, int ce_chunk);
+la_status la_ce_fwd(const void *h, const void *W, const int *targets, float *loss, float *lse,
+                    void *workspace, size_t workspace_bytes, int N, int d, int V, la_dtype dt, void *stream);
+la_status la_ce_bwd(const void *h, const void *W, const int *targets, const float *lse, const float *dloss,
+                    void *dh, float *dW, void *workspace, size_t workspace_bytes,
+                    int N, int d, int V, int ce_chunk, la_dtype dt, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *la_status_str(la_status s);

@@ -32,7 +32,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["la_abi_version", "la_chunk_bwd", "la_chunk_fwd", "la_kernel_name",
+    assert declared_functions() == ["la_abi_version", "la_ce_bwd", "la_ce_fwd", "la_ce_workspace_bytes",
+                                    "la_chunk_bwd", "la_chunk_fwd", "la_kernel_name",
                                     "la_seq_bwd", "la_seq_fwd", "la_seq_kernel_name", "la_status_str",
                                     "la_time_next_launch"]
 
@@ -203,6 +204,54 @@ def test_seq_kernel_names(lib):
     assert not lac.seq_supported("bf16", 8164, 128, 100) and not lac.seq_supported("bf16", 16448, 128, 128)
     assert lac.seq_supported("bf16", 1 << 20, 64, 128) and not lac.seq_supported("bf16", (1 << 20) + 128, 64, 128)
     assert not lac.seq_supported("bf16", 1024, 128, 128, "elu1")
+
+
+CE_WS = 1 << 30  # a fake workspace size large enough for every shape below
+
+
+def ce_fwd_call(lib, N=512, d=1280, V=50257, dt=1, ws_bytes=CE_WS, **over):
+    names = ["h", "W", "targets", "loss", "lse", "ws"]
+    args = {n: addr(i) for i, n in enumerate(names)}
+    args.update(over)
+    return lib.la_ce_fwd(*[args[n] for n in names], ws_bytes, N, d, V, dt, None)
+
+
+def ce_bwd_call(lib, N=512, d=1280, V=50257, chunk=0, dt=1, ws_bytes=CE_WS, **over):
+    names = ["h", "W", "targets", "lse", "dloss", "dh", "dW", "ws"]
+    args = {n: addr(i) for i, n in enumerate(names)}
+    args.update(over)
+    return lib.la_ce_bwd(*[args[n] for n in names], ws_bytes, N, d, V, chunk, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), INVALID), (dict(V=1), INVALID), (dict(d=0), INVALID),
+    (dict(d=1000), UNSUPPORTED), (dict(d=8192 + 128), UNSUPPORTED), (dict(dt=0), UNSUPPORTED),
+    (dict(V=1 << 20), UNSUPPORTED),                      # V d beyond 32-bit byte offsets
+    (dict(lse=None), INVALID), (dict(ws=None), INVALID),
+    (dict(ws_bytes=1000), INVALID),                      # workspace too small
+    (dict(h=ctypes.c_void_p(BASE + 8)), ALIGN),
+    (dict(loss=addr(0)), ALIAS),                         # loss inside h
+    (dict(ws=addr(1)), ALIAS),                           # workspace == W
+])
+def test_ce_fwd_rejects(lib, kw, status):
+    assert ce_fwd_call(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-1), INVALID), (dict(d=64), UNSUPPORTED), (dict(dh=None), INVALID), (dict(dW=None), INVALID),
+    (dict(ws_bytes=4096), INVALID), (dict(dW=addr(3)), ALIAS), (dict(dh=addr(5 + 1)), ALIAS),
+    (dict(dloss=ctypes.c_void_p(BASE + 4 * STEP + 4)), ALIGN),
+])
+def test_ce_bwd_rejects(lib, kw, status):
+    assert ce_bwd_call(lib, **kw) == status
+
+
+def test_ce_workspace_sizes(lib):
+    full = lac.ce_workspace_bytes(512, 1280, 50257)
+    chunked = lac.ce_workspace_bytes(512, 1280, 50257, 128)
+    # the backward's P of one chunk (bf16, padded to 128 x 128 tiles) and the dh partial sums
+    assert full >= 512 * 50304 * 2 and chunked >= 128 * 50304 * 2 and chunked < full
+    assert lac.ce_workspace_bytes(512, 100, 50257) == 0  # d not a multiple of 128
 
 
 def test_time_next_launch_pairs(lib):

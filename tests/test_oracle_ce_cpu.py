@@ -92,7 +92,7 @@ def test_c6_matches_torch_cross_entropy_float64():
     (3.0 * loss).backward()
     l, _ = ce.forward(h, W, t)
     dh, dW = ce.backward(h, W, t, dloss=3.0)
-    assert l == pytest.approx(float(loss), rel=1e-13)
+    assert l == pytest.approx(float(loss.detach()), rel=1e-13)
     assert np.allclose(dh, ht.grad.numpy(), rtol=1e-12, atol=1e-15)
     assert np.allclose(dW, Wt.grad.numpy(), rtol=1e-12, atol=1e-15)
 
