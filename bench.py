@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 METRIC = "tokens·groups/s for linear-attn fwd+bwd at G=160,C=128,D=64; % roofline"
 HEADLINE = "g160_c128_d64_bf16_fwdbwd"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -236,6 +237,133 @@ def copy_calibration(torch, mib=256, reps=5):
           flush=True)
 
 
+def timed_runs(torch, fn, K):
+    """K calls of fn() in up to five consecutive runs bracketed by device events: the per-call
+    times of the runs, sorted, and the host seconds spent enqueuing."""
+    R = min(5, K)
+    sizes = [K // R + (1 if r < K % R else 0) for r in range(R)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R)]
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    i = 0
+    for (a, b), nsteps in zip(evs, sizes):
+        a.record()
+        for _ in range(nsteps):
+            fn(i)
+            i += 1
+        b.record()
+    host_s = time.perf_counter() - h0
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) / nsteps for (a, b), nsteps in zip(evs, sizes)), host_s
+
+
+def bench_ce(args, w, torch, lac, inp):
+    """The tied head's cross-entropy (Bottleneck #3 / Opt 3 of the pages): one step is la_ce_fwd
+    and la_ce_bwd over the N tokens, inputs resident on the device.  Bound by MFMA: four products
+    of 2 N V d flops each (the forward's logits; the backward's recomputed logits, dh and dW)."""
+    N, d, V = w.N, w.d, w.V
+    I = inp.ce_workload_inputs(w)
+    ws_bytes = lac.ce_workspace_bytes(N, d, V)
+    set_bytes = V * d * 2 + V * d * 4 + 2 * N * d * 2 + ws_bytes  # W, dW, h, dh, workspace
+    nsets = max(1, math.ceil(args.footprint_mb * 1e6 / set_bytes))
+    dev = "cuda:0"
+    sets = []
+    for _ in range(nsets):
+        s = {n: I[n].to(dev).contiguous() for n in ("h", "W", "targets")}
+        s["fout"] = (torch.empty((), dtype=torch.float32, device=dev), torch.empty(N, dtype=torch.float32, device=dev))
+        s["bout"] = (torch.empty_like(s["h"]), torch.empty((V, d), dtype=torch.float32, device=dev))
+        s["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        sets.append(s)
+
+    def fwd(s):
+        lac.ce_fwd(s["h"], s["W"], s["targets"], workspace=s["ws"], out=s["fout"])
+
+    def bwd(s):
+        lac.ce_bwd(s["h"], s["W"], s["targets"], s["fout"][1], workspace=s["ws"], out=s["bout"])
+
+    def step(i):
+        fwd(sets[i % nsets])
+        bwd(sets[i % nsets])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    per_run, host_s = timed_runs(torch, step, K)
+    ms_per_step = per_run[len(per_run) // 2]
+    # per entry point: events recorded on its first and last kernel dispatch
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2)]
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        s = sets[i % nsets]
+        lac.time_next_launch(*ev[i][0])
+        fwd(s)
+        lac.time_next_launch(*ev[i][1])
+        bwd(s)
+    torch.cuda.synchronize()
+    gemm = 2.0 * N * V * d
+    entry = {}
+    for j, (name, flops, kern) in enumerate((
+            ("la_ce_fwd", gemm, "la_ce_fwd_kernel + la_ce_combine_kernel"),
+            ("la_ce_bwd", 3 * gemm, "la_ce_p_kernel + la_ce_dh_kernel + la_ce_dh_reduce_kernel + la_ce_dw_kernel"))):
+        us = sum(e[j][0].elapsed_time(e[j][1]) for e in ev) * 1e3 / K
+        tf = flops / (us * 1e-6) / 1e12
+        entry[name] = {"avg_us": us, "kernels": kern, "algorithmic_flops": flops, "TFLOP/s": tf,
+                       "frac": tf / MFMA_BF16_PEAK_TFLOPS}
+    top = "la_ce_bwd"
+    kt = entry[top]
+    out = {
+        "metric": f"tokens/s for the tied-head cross-entropy fwd+bwd, {w.name}",
+        "value": N / (ms_per_step / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "N": N, "d": d, "V": V, "ce_chunk": N, "buffer_sets": nsets,
+                   "footprint_mb": round(nsets * set_bytes / 1e6, 1), "workspace_bytes": ws_bytes,
+                   "timed_runs": len(per_run), "ms_per_step_runs": per_run, "graph_captured": False,
+                   "host_enqueue_us_per_step": host_s * 1e6 / K,
+                   "kernel_timing": "HIP events on the first and last kernel dispatch of each entry point, "
+                                    "separate timed loop"},
+        "roofline": {"bound": "mfma", "kernel": f"{top} ({kt['kernels']})", "achieved": kt["TFLOP/s"],
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": kt["frac"], "traffic": None,
+                     "algorithmic_flops": kt["algorithmic_flops"], "avg_us": kt["avg_us"]},
+        "kernels": entry,
+        "step_roofline_frac": 4 * gemm / (ms_per_step / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_ce(I, w)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_ce(I, w, min_seconds=10.0):
+    """The fp64 oracle of the cross-entropy (numpy, its BLAS on every host thread), forward and
+    backward over the full workload, repeated; and once on one BLAS thread."""
+    from oracle import ce
+    from threadpoolctl import threadpool_limits
+    h, W, t = (I[n] for n in ("h", "W", "targets"))
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        ce.forward(h, W, t)
+        ce.backward(h, W, t)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= min_seconds and len(times) >= 3:
+            break
+    times.sort()
+    med = times[len(times) // 2]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        ce.forward(h, W, t)
+        ce.backward(h, W, t)
+        t1 = time.perf_counter() - t0
+    return {"value": w.N / med, "unit": "tokens/s", "cores": os.cpu_count(), "kind": "oracle",
+            "sample": f"full {w.name} workload (N={w.N}, d={w.d}, V={w.V}), forward+backward in fp64 "
+                      f"(numpy BLAS), median of {len(times)} repeats ({sum(times):.1f} s of CPU work)",
+            "single_thread_value": w.N / t1, "single_thread_sample": "full workload, one run, one BLAS thread",
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,6 +405,8 @@ def main():
     from causal_linear_attention_chunked_amd import inputs as inp
 
     lac.load_library()
+    if args.workload in inp.CE_WORKLOADS:
+        return bench_ce(args, inp.ce_workload(args.workload), torch, lac, inp)
     w = inp.workload(args.workload)
     if not w.backward:
         raise SystemExit("bench.py times forward+backward workloads")

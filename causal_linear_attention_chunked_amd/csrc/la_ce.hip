@@ -13,8 +13,9 @@
 // ranges).  The epilogues:
 //   forward: the tile's logits never leave registers: per token, the maximum and the sum of
 //            exponentials over the tile's 128 classes (combined over the two waves in LDS) go to
-//            a partials array, and the target's logit where it falls in the tile; a single
-//            workgroup then combines the partials into lse and the mean loss, deterministically;
+//            a partials array, and the target's logit where it falls in the tile; a second kernel
+//            combines each token's partials into lse (16 threads per token), a third takes the
+//            mean loss in a fixed order (deterministic);
 //   backward: the logits are recomputed (the checkpoint) and P is written in bf16, one chunk of
 //            tokens at a time (the chunk's P is the transient of the pages' chunked form);
 //            dW = P^T h (output tiles stored, or added for the chunks after the first) and
@@ -57,8 +58,8 @@ __device__ __forceinline__ void gemm_tile(char *smem, const Operand &A, const Op
         for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
     // thread tid stages 16 bytes of storage rows tid / 8 and tid / 8 + 32 of each 64 x 64 tile
     const int srow = tid >> 3, sunit = tid & 7;
-    bf16x8 st[2][2][2];  // [operand][tile][half]
-    auto load = [&](uint32_t kk) {
+    typedef bf16x8 Stage[2][2][2];  // [operand][tile][half]
+    auto load = [&](Stage &st, uint32_t kk) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -72,7 +73,7 @@ __device__ __forceinline__ void gemm_tile(char *smem, const Operand &A, const Op
                 st[1][u][hv] = gload<bf16x8>(B.g, ob * 2);
             }
     };
-    auto store = [&](int stage) {
+    auto store = [&](const Stage &st, int stage) {
 #pragma unroll
         for (int op = 0; op < 2; ++op)
 #pragma unroll
@@ -82,15 +83,8 @@ __device__ __forceinline__ void gemm_tile(char *smem, const Operand &A, const Op
                     *reinterpret_cast<bf16x8 *>(stage_tile(smem, stage, op, u) + stage_off(tid + 256 * hv)) =
                         st[op][u][hv];
     };
-    const int nk = (int)((k1 - k0) / CK);
-    load(k0);
-    store(0);
-    lds_barrier();
-    for (int ks = 0; ks < nk; ++ks) {
-        const int cur = ks & 1;
-        const bool more = ks + 1 < nk;
-        if (more) load(k0 + (uint32_t)(ks + 1) * CK);
-        const char *At = stage_tile(smem, cur, 0, wm), *Bt = stage_tile(smem, cur, 1, wn);
+    auto compute = [&](int stage) {
+        const char *At = stage_tile(smem, stage, 0, wm), *Bt = stage_tile(smem, stage, 1, wn);
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
             bf16x8 af[4], bfr[4];
@@ -104,7 +98,21 @@ __device__ __forceinline__ void gemm_tile(char *smem, const Operand &A, const Op
 #pragma unroll
                 for (int j = 0; j < 4; ++j) mma(acc[i][j], af[i], bfr[j]);
         }
-        if (more) store(cur ^ 1);
+    };
+    // One register stage: the next k-step's loads are issued before this one's products and
+    // stored after them.  Measured and rejected: two stages a full k-step ahead (more registers,
+    // slower), A fragments read one at a time (less overlap, slower), one 16-byte read per
+    // fragment in the contiguous k order for k-contiguous operands (slower).
+    const int nk = (int)((k1 - k0) / CK);
+    Stage r0;
+    load(r0, k0);
+    store(r0, 0);
+    lds_barrier();
+    for (int ks = 0; ks < nk; ++ks) {
+        const bool more = ks + 1 < nk;
+        if (more) load(r0, k0 + (uint32_t)(ks + 1) * CK);
+        compute(ks & 1);
+        if (more) store(r0, (ks & 1) ^ 1);
         lds_barrier();
     }
 }
@@ -117,18 +125,30 @@ __device__ __forceinline__ float gmax(float x) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Workgroups are dealt to the eight XCDs in turn (workgroup b to XCD b % 8), each XCD with its own
+// L2.  The tile order is remapped so that each XCD takes one contiguous range of logical tiles:
+// tiles that share an operand are numbered consecutively, so they run on one XCD and that
+// operand is fetched into one L2 instead of several.
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t total) {
+    const uint32_t per = total / 8, rem = total % 8, x = b % 8, k = b / 8;
+    return x < rem ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
+}
+
 constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
 }  // namespace
 
-// Forward tiles: grid (vocabulary tiles, token tiles).  The A operand is W (rows = classes), B is
+// Forward tiles: one workgroup per (class tile, token tile).  The A operand is W (rows = classes), B is
 // h (rows = tokens), both k-contiguous.  part[vt][t] = (max, sum exp(logit - max)) over the tile's
 // classes, tl[t] = logit of token t's target (written by the one lane that holds it).
 __global__ __launch_bounds__(CE_THREADS, 2) void la_ce_fwd_kernel(
     const bf16 *__restrict__ h, const bf16 *__restrict__ W, const int *__restrict__ targets,
     floatx2 *__restrict__ part, float *__restrict__ tl, int N, int d, int V, int Npad) {
     __shared__ __attribute__((aligned(16))) char smem[8 * TBYTES];
-    const uint32_t v0 = blockIdx.x * CT, t0 = blockIdx.y * CT;
+    // logical tile: the token tiles of one class tile consecutively (they share its rows of W)
+    const uint32_t ntt = (uint32_t)Npad / CT;
+    const uint32_t L = xcd_tile(blockIdx.x, gridDim.x), vt = L / ntt;
+    const uint32_t v0 = vt * CT, t0 = (L % ntt) * CT;
     const Operand A{GRes(W, (uint32_t)V * d * 2), (uint32_t)d, false};
     const Operand B{GRes(h, (uint32_t)N * d * 2), (uint32_t)d, false};
     floatx4 acc[4][4];
@@ -170,29 +190,45 @@ __global__ __launch_bounds__(CE_THREADS, 2) void la_ce_fwd_kernel(
         const float m = fmaxf(a[0], b[0]);
         // a tile's classes may all lie past V only if V <= v0, which the grid excludes
         const float s = a[1] * exp_f(a[0] - m) + b[1] * exp_f(b[0] - m);
-        part[(size_t)blockIdx.x * Npad + t0 + tid] = floatx2{m, s};
+        part[(size_t)vt * Npad + t0 + tid] = floatx2{m, s};
     }
 }
 
-// One workgroup: lse_t = max_v + log(sum over tiles), loss = mean_t (lse_t - tl_t), in a fixed order.
-__global__ __launch_bounds__(1024, 1) void la_ce_combine_kernel(const floatx2 *__restrict__ part,
-                                                                const float *__restrict__ tl,
-                                                                float *__restrict__ lse, float *__restrict__ loss,
-                                                                int N, int Npad, int nvt) {
-    __shared__ float red[1024];
-    float acc = 0.f;
-    for (int t = threadIdx.x; t < N; t += 1024) {
-        float m = -INFINITY;
-        for (int vt = 0; vt < nvt; ++vt) m = fmaxf(m, part[(size_t)vt * Npad + t][0]);
-        float s = 0.f;
-        for (int vt = 0; vt < nvt; ++vt) {
+// lse_t = max + log(sum over the class tiles' partials), nll_t = lse_t - tl_t: 16 tokens per
+// workgroup, 16 threads per token each folding every 16th tile, then merged in a fixed order.
+__global__ __launch_bounds__(256) void la_ce_lse_kernel(const floatx2 *__restrict__ part, const float *__restrict__ tl,
+                                                       float *__restrict__ lse, float *__restrict__ nll, int N,
+                                                       int Npad, int nvt) {
+    const int t = blockIdx.x * 16 + (threadIdx.x >> 4), sub = threadIdx.x & 15;
+    float m = -INFINITY, s = 0.f;
+    if (t < N) {
+        for (int vt = sub; vt < nvt; vt += 16) {
             const floatx2 p = part[(size_t)vt * Npad + t];
-            s += p[1] * exp_f(p[0] - m);
+            const float mm = fmaxf(m, p[0]);
+            s = s * exp_f(m - mm) + p[1] * exp_f(p[0] - mm);
+            m = mm;
         }
+    }
+#pragma unroll
+    for (int k = 1; k < 16; k <<= 1) {  // butterfly over the 16 threads of the token
+        const float m2 = __shfl_xor(m, k), s2 = __shfl_xor(s, k);
+        const float mm = fmaxf(m, m2);
+        s = (m == -INFINITY ? 0.f : s * exp_f(m - mm)) + (m2 == -INFINITY ? 0.f : s2 * exp_f(m2 - mm));
+        m = mm;
+    }
+    if (t < N && sub == 0) {
         const float l = m + __logf(s);
         lse[t] = l;
-        acc += l - tl[t];
+        nll[t] = l - tl[t];
     }
+}
+
+// One workgroup: loss = mean of nll, summed in a fixed order.
+__global__ __launch_bounds__(1024, 1) void la_ce_mean_kernel(const float *__restrict__ nll, float *__restrict__ loss,
+                                                            int N) {
+    __shared__ float red[1024];
+    float acc = 0.f;
+    for (int t = threadIdx.x; t < N; t += 1024) acc += nll[t];
     red[threadIdx.x] = acc;
     __syncthreads();
     for (int k = 512; k > 0; k >>= 1) {
@@ -209,7 +245,9 @@ __global__ __launch_bounds__(CE_THREADS, 2) void la_ce_p_kernel(
     const float *__restrict__ lse, const float *__restrict__ dloss, bf16 *__restrict__ P, int c0, int Nc, int N,
     int d, int V, int Vpad) {
     __shared__ __attribute__((aligned(16))) char smem[8 * TBYTES];
-    const uint32_t v0 = blockIdx.x * CT, t0 = blockIdx.y * CT;
+    const uint32_t ntt = (uint32_t)(Nc + CT - 1) / CT;
+    const uint32_t L = xcd_tile(blockIdx.x, gridDim.x);
+    const uint32_t v0 = (L / ntt) * CT, t0 = (L % ntt) * CT;
     const Operand A{GRes(W, (uint32_t)V * d * 2), (uint32_t)d, false};
     const Operand B{GRes(h + (size_t)c0 * d, (uint32_t)Nc * d * 2), (uint32_t)d, false};
     floatx4 acc[4][4];
@@ -247,7 +285,10 @@ __global__ __launch_bounds__(CE_THREADS, 2) void la_ce_dw_kernel(const bf16 *__r
                                                                  int c0, int Nc, int Ncpad, int d, int V, int Vpad,
                                                                  int accumulate) {
     __shared__ __attribute__((aligned(16))) char smem[8 * TBYTES];
-    const uint32_t f0 = blockIdx.x * CT, v0 = blockIdx.y * CT;
+    // the feature tiles of one class tile consecutively (they share its columns of P)
+    const uint32_t nft = (uint32_t)d / CT;
+    const uint32_t L = xcd_tile(blockIdx.x, gridDim.x);
+    const uint32_t f0 = (L % nft) * CT, v0 = (L / nft) * CT;
     const Operand A{GRes(h + (size_t)c0 * d, (uint32_t)Nc * d * 2), (uint32_t)d, true};
     const Operand B{GRes(P, (uint32_t)Ncpad * Vpad * 2), (uint32_t)Vpad, true};
     floatx4 acc[4][4];
@@ -273,8 +314,12 @@ __global__ __launch_bounds__(CE_THREADS, 2) void la_ce_dh_kernel(const bf16 *__r
                                                                  const bf16 *__restrict__ P, float *__restrict__ part,
                                                                  int Ncpad, int d, int V, int Vpad, int kper) {
     __shared__ __attribute__((aligned(16))) char smem[8 * TBYTES];
-    const uint32_t f0 = blockIdx.x * CT, t0 = blockIdx.y * CT;
-    const uint32_t k0 = blockIdx.z * (uint32_t)kper;
+    // split slowest, then token tile, feature tile fastest: consecutive tiles share P's rows of the
+    // split, and the tiles of one split share its rows of W
+    const uint32_t nft = (uint32_t)d / CT, ntt = (uint32_t)Ncpad / CT;
+    const uint32_t L = xcd_tile(blockIdx.x, gridDim.x), z = L / (nft * ntt), rest = L % (nft * ntt);
+    const uint32_t f0 = (rest % nft) * CT, t0 = (rest / nft) * CT;
+    const uint32_t k0 = z * (uint32_t)kper;
     const uint32_t k1 = k0 + (uint32_t)kper < (uint32_t)Vpad ? k0 + (uint32_t)kper : (uint32_t)Vpad;
     const Operand A{GRes(W, (uint32_t)V * d * 2), (uint32_t)d, true};
     const Operand B{GRes(P, (uint32_t)Ncpad * Vpad * 2), (uint32_t)Vpad, false};
@@ -283,7 +328,7 @@ __global__ __launch_bounds__(CE_THREADS, 2) void la_ce_dh_kernel(const bf16 *__r
 
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 1, wn = w >> 1;
-    float *base = part + (size_t)blockIdx.z * Ncpad * d;
+    float *base = part + (size_t)z * Ncpad * d;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int t = (int)t0 + 64 * wn + 16 * j + r;
@@ -319,7 +364,7 @@ CeShape ce_shape(int N, int d, int V, int ce_chunk) {
     if (nsplit > s.Vpad / CK) nsplit = s.Vpad / CK;
     s.kper = ((s.Vpad + nsplit - 1) / nsplit + CK - 1) / CK * CK;
     s.nsplit = (s.Vpad + s.kper - 1) / s.kper;
-    s.fwd_bytes = (size_t)s.nvt * s.Npad * 8 + (size_t)s.Npad * 4;
+    s.fwd_bytes = (size_t)s.nvt * s.Npad * 8 + (size_t)s.Npad * 8;  // partials, target logits, nll
     s.p_bytes = (size_t)s.chunk_pad * s.Vpad * 2;
     s.bwd_bytes = s.p_bytes + (size_t)s.nsplit * s.chunk_pad * d * 4;
     s.ws_bytes = s.fwd_bytes > s.bwd_bytes ? s.fwd_bytes : s.bwd_bytes;
@@ -331,10 +376,13 @@ hipError_t launch_ce_fwd(const void *h, const void *W, const int *targets, float
     const CeShape s = ce_shape(N, d, V, N);
     floatx2 *part = reinterpret_cast<floatx2 *>(ws);
     float *tl = reinterpret_cast<float *>(static_cast<char *>(ws) + (size_t)s.nvt * s.Npad * 8);
-    hipExtLaunchKernelGGL(la_ce_fwd_kernel, dim3(s.nvt, s.Npad / CT), dim3(CE_THREADS), 0, stream, ev[0], nullptr, 0,
-                          (const bf16 *)h, (const bf16 *)W, targets, part, tl, N, d, V, s.Npad);
-    hipExtLaunchKernelGGL(la_ce_combine_kernel, dim3(1), dim3(1024), 0, stream, nullptr, ev[1], 0,
-                          (const floatx2 *)part, (const float *)tl, lse, loss, N, s.Npad, s.nvt);
+    float *nll = tl + s.Npad;
+    hipExtLaunchKernelGGL(la_ce_fwd_kernel, dim3(s.nvt * (s.Npad / CT)), dim3(CE_THREADS), 0, stream, ev[0], nullptr,
+                          0, (const bf16 *)h, (const bf16 *)W, targets, part, tl, N, d, V, s.Npad);
+    hipExtLaunchKernelGGL(la_ce_lse_kernel, dim3((N + 15) / 16), dim3(256), 0, stream, nullptr, nullptr, 0,
+                          (const floatx2 *)part, (const float *)tl, lse, nll, N, s.Npad, s.nvt);
+    hipExtLaunchKernelGGL(la_ce_mean_kernel, dim3(1), dim3(1024), 0, stream, nullptr, ev[1], 0, (const float *)nll,
+                          loss, N);
     return hipGetLastError();
 }
 
@@ -348,16 +396,16 @@ hipError_t launch_ce_bwd(const void *h, const void *W, const int *targets, const
         const int Nc = N - c0 < s.chunk ? N - c0 : s.chunk;
         const int Ncpad = (Nc + CT - 1) / CT * CT;
         const bool first = c0 == 0, last = c0 + s.chunk >= N;
-        hipExtLaunchKernelGGL(la_ce_p_kernel, dim3(s.nvt, Ncpad / CT), dim3(CE_THREADS), 0, stream,
+        hipExtLaunchKernelGGL(la_ce_p_kernel, dim3(s.nvt * (Ncpad / CT)), dim3(CE_THREADS), 0, stream,
                               first ? ev[0] : nullptr, nullptr, 0, (const bf16 *)h, (const bf16 *)W, targets, lse,
                               dloss, P, c0, Nc, N, d, V, s.Vpad);
-        hipExtLaunchKernelGGL(la_ce_dh_kernel, dim3(d / CT, Ncpad / CT, s.nsplit), dim3(CE_THREADS), 0, stream,
+        hipExtLaunchKernelGGL(la_ce_dh_kernel, dim3((d / CT) * (Ncpad / CT) * s.nsplit), dim3(CE_THREADS), 0, stream,
                               nullptr, nullptr, 0, (const bf16 *)W, (const bf16 *)P, part, Ncpad, d, V, s.Vpad,
                               s.kper);
         const size_t n4 = (size_t)Nc * d / 4;
         hipExtLaunchKernelGGL(la_ce_dh_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
                               nullptr, nullptr, 0, (const float *)part, (bf16 *)dh, c0, Nc, Ncpad, d, s.nsplit);
-        hipExtLaunchKernelGGL(la_ce_dw_kernel, dim3(d / CT, s.nvt), dim3(CE_THREADS), 0, stream, nullptr,
+        hipExtLaunchKernelGGL(la_ce_dw_kernel, dim3((d / CT) * s.nvt), dim3(CE_THREADS), 0, stream, nullptr,
                               last ? ev[1] : nullptr, 0, (const bf16 *)h, (const bf16 *)P, dW, c0, Nc, Ncpad, d, V,
                               s.Vpad, first ? 0 : 1);
     }
