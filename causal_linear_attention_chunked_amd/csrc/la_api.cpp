@@ -181,7 +181,7 @@ la_status la_seq_fwd(const void *q, const void *k, const void *v, const float *S
     st = alias_checks(in, 5, out, 5);
     if (st != LA_OK) return st;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    // D = 128: the general forward's sequence mode walks the whole sequence in one pass
+    // D = 128: one workgroup per group walks the whole sequence (la_seq_fwd_d128_kernel)
     const hipError_t e =
         D == 128 ? lachunk::launch_seq_fwd_d128(q, k, v, S_in, z_in, o, S_out, z_out, S_res, z_res, G, T, s, te.ev)
                  : lachunk::launch_seq_fwd_c128(q, k, v, S_in, z_in, o, S_out, z_out, S_res, z_res, G, T / chunk,
@@ -301,7 +301,7 @@ const char *la_kernel_name(int backward, la_dtype dt, int C, int D) {
 
 const char *la_seq_kernel_name(int backward, la_dtype dt, int chunk, int D, la_feature feature) {
     if (dt == LA_BF16 && D == 128 && chunk >= BK_TOKENS && chunk % BK_TOKENS == 0 && feature == LA_FEATURE_NONE)
-        return backward ? "la_seq_bwd_d128_kernel" : "la_fwd_kernel";  // the forward: its sequence mode
+        return backward ? "la_seq_bwd_d128_kernel" : "la_seq_fwd_d128_kernel";
     if (dt != LA_BF16 || D != 64 || chunk != 128) return nullptr;
     if (feature == LA_FEATURE_ELU1) return backward ? "la_seq_bwd_c128w16_elu1_kernel" : "la_seq_fwd_c128_elu1_kernel";
     if (feature != LA_FEATURE_NONE) return nullptr;

@@ -20,16 +20,7 @@
 // has no cancellation against the others).  Staging is natural row-major only:
 // transposed operands come from LDS transpose reads.  The next window's loads
 // are issued as soon as the current window is staged.
-//
-// Sequence mode (SEQ, the sequence entry point at D = 128): C is a whole sequence of
-// T tokens, walked in one pass with the state in registers.  Its ragged end is a masked
-// block (rows past the end read as zero and are not stored) instead of the token-by-token
-// tail, and S and z are carried as unevaluated sums with compensation terms (each block's
-// K^T V and K^T 1 added with a two-sum): the sequence backward recovers the early states
-// from the final carry by subtraction, so the carry goes out exact beyond its rounding, as
-// S_out + S_res and z_out + z_res.
 #include "la_common.h"
-#include "la_tile.h"
 #include "la_launch.h"
 #include <hip/hip_ext.h>
 
@@ -68,12 +59,11 @@ __device__ __forceinline__ floatx8 zrow8(const float *z, int lane) {
     return floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-template <typename T, int D, bool SEQ = false>
+template <typename T, int D>
 __global__ __launch_bounds__(NTHR, 1) void la_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ S_in, const float *__restrict__ z_in,
-    T *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out, int C,
-    float *__restrict__ S_res, float *__restrict__ z_res) {
+    T *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out, int C) {
     using L = FwdLds<T, D>;
     constexpr int WIN = L::WIN;
     constexpr int NVS = D / 64;          // value slices per group
@@ -103,8 +93,7 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_kernel(
     // waves without a block of their own (one-block windows) read nothing
     const GRes qw(q + tok0 * D, blk < WIN ? chunk_bytes : 0);
     T *og = o + tok0 * D + vs * 64;
-    // sequence mode: a ragged end is one more (masked) block
-    const int nb = SEQ ? (C + BK - 1) / BK : C / BK, tail = SEQ ? 0 : C % BK;
+    const int nb = C / BK, tail = C % BK;
     const int nwin = (nb + WIN - 1) / WIN;
 
     struct Window {
@@ -138,9 +127,6 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_kernel(
     qtail.load(tail ? qr : GRes(q, 0), (uint32_t)nb * BK * D, D, tid);
     floatx4 Sacc[NOWN];  // S[p][c], p-tile pt0 + 2i, c-tile ct: lane (c = r), element e: p = 4g + e
     floatx4 zr[NOWN];    // z[p] for the same p-tiles (every lane; kept current by the waves of c-tile 0)
-    floatx4 Scomp[NOWN], zc[NOWN];  // sequence mode: compensation terms
-#pragma unroll
-    for (int i = 0; i < NOWN; ++i) Scomp[i] = zc[i] = zero4();
 #pragma unroll
     for (int i = 0; i < NOWN; ++i)
 #pragma unroll
@@ -156,18 +142,13 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_kernel(
 #pragma unroll
         for (int i = 0; i < NOWN; ++i) {
             const int p0 = 16 * (pt0 + 2 * i) + 4 * g;
-            *reinterpret_cast<Vec4<T> *>(ST + s * L::ST_ELEMS + (16 * ct + r) * L::LDST + p0) =
-                to_vec4<T>(SEQ ? Sacc[i] + Scomp[i] : Sacc[i]);
-            if (ct == 0 && r == 0) *reinterpret_cast<floatx4 *>(zs + s * D + p0) = SEQ ? zr[i] + zc[i] : zr[i];
+            *reinterpret_cast<Vec4<T> *>(ST + s * L::ST_ELEMS + (16 * ct + r) * L::LDST + p0) = to_vec4<T>(Sacc[i]);
+            if (ct == 0 && r == 0) *reinterpret_cast<floatx4 *>(zs + s * D + p0) = zr[i];
         }
     };
     const Frag<T> ones = ones_frag<T>();
     // S += K_bi^T V_bi and z += K_bi^T 1 over one staged block
     auto update = [&](int bi) {
-        // sequence mode: the block's products in fresh accumulators, then added with a two-sum
-        floatx4 P[NOWN], Pz[NOWN];
-#pragma unroll
-        for (int i = 0; i < NOWN; ++i) P[i] = Pz[i] = zero4();
 #pragma unroll
         for (int kc2 = 0; kc2 < 2; ++kc2) {
             const int t0 = bi * BK + 32 * kc2;
@@ -175,15 +156,8 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_kernel(
 #pragma unroll
             for (int i = 0; i < NOWN; ++i) {
                 const Frag<T> kt = ldfrag_tr<T>(Ks + t0 * L::LDN + 16 * (pt0 + 2 * i), L::LDN, lane);
-                mma(SEQ ? P[i] : Sacc[i], kt, vt);
-                if (ct == 0) mma(SEQ ? Pz[i] : zr[i], kt, ones);
-            }
-        }
-        if constexpr (SEQ) {
-#pragma unroll
-            for (int i = 0; i < NOWN; ++i) {
-                two_sum4(Sacc[i], Scomp[i], P[i]);
-                if (ct == 0) two_sum4(zr[i], zc[i], Pz[i]);
+                mma(Sacc[i], kt, vt);
+                if (ct == 0) mma(zr[i], kt, ones);
             }
         }
     };
@@ -252,12 +226,9 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_kernel(
                     mma(nm[c], ldfrag<T>(STb + 16 * c * L::LDST + 32 * kc, L::LDST, lane), qc[kc]);
             }
             const float inv = __builtin_amdgcn_rcpf(dn[0]);
-            const int trow = t0 + blk * BK + 16 * tq + r;
-            T *orow = og + (size_t)trow * D + 4 * g;
-            if (!SEQ || trow < C) {  // rows of a ragged end past the sequence are not stored
+            T *orow = og + (size_t)(t0 + blk * BK + 16 * tq + r) * D + 4 * g;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) *reinterpret_cast<Vec4<T> *>(orow + 16 * c) = to_vec4<T>(nm[c] * inv);
-            }
+            for (int c = 0; c < 4; ++c) *reinterpret_cast<Vec4<T> *>(orow + 16 * c) = to_vec4<T>(nm[c] * inv);
         }
         // state after the window
         if constexpr (WIN == 2) {
@@ -271,32 +242,6 @@ __global__ __launch_bounds__(NTHR, 1) void la_fwd_kernel(
         }
     }
 
-    if constexpr (SEQ) {
-        // the carry as its nearest fp32 values and the exact remainders
-        const size_t sb = (size_t)grp * D * D + vs * 64 + 16 * ct + r;
-#pragma unroll
-        for (int i = 0; i < NOWN; ++i) {
-            floatx4 zs4, zr4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const size_t so = sb + (size_t)(16 * (pt0 + 2 * i) + 4 * g + e) * D;
-                float s, res;
-                fold(Sacc[i][e], Scomp[i][e], s, res);
-                S_out[so] = s;
-                if (S_res) S_res[so] = res;
-                float zs, zres;
-                fold(zr[i][e], zc[i][e], zs, zres);
-                zs4[e] = zs;
-                zr4[e] = zres;
-            }
-            if (vs == 0 && ct == 0 && r == 0) {
-                const size_t zo = (size_t)grp * D + 16 * (pt0 + 2 * i) + 4 * g;
-                *reinterpret_cast<floatx4 *>(z_out + zo) = zs4;
-                if (z_res) *reinterpret_cast<floatx4 *>(z_res + zo) = zr4;
-            }
-        }
-        return;
-    }
     if (tail == 0) {
         float *Sg = S_out + (size_t)grp * D * D + vs * 64 + 16 * ct + r;
 #pragma unroll
@@ -382,17 +327,7 @@ hipError_t launch_fwd(const void *q, const void *k, const void *v, const float *
                       const hipEvent_t ev[2]) {
     dim3 grid((unsigned)G * (D / 64)), block(NTHR);
     hipExtLaunchKernelGGL((la_fwd_kernel<T, D>), grid, block, 0, stream, ev[0], ev[1], 0,
-                          (const T *)q, (const T *)k, (const T *)v, S_in, z_in, (T *)o, S_out, z_out, C,
-                          (float *)nullptr, (float *)nullptr);
-    return hipGetLastError();
-}
-
-hipError_t launch_seq_fwd_d128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
-                               void *o, float *S_out, float *z_out, float *S_res, float *z_res, int G, int T,
-                               hipStream_t stream, const hipEvent_t ev[2]) {
-    hipExtLaunchKernelGGL((la_fwd_kernel<bf16, 128, true>), dim3((unsigned)G * 2), dim3(NTHR), 0, stream, ev[0],
-                          ev[1], 0, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_in, z_in, (bf16 *)o, S_out,
-                          z_out, T, S_res, z_res);
+                          (const T *)q, (const T *)k, (const T *)v, S_in, z_in, (T *)o, S_out, z_out, C);
     return hipGetLastError();
 }
 

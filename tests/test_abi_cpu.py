@@ -196,7 +196,7 @@ def test_seq_kernel_names(lib):
         lac.seq_kernel_name(True, "bf16", 128, 64, "relu")
     assert lac.seq_supported("bf16", 1024, 64, 128) and not lac.seq_supported("bf16", 1000, 64, 128)
     assert not lac.seq_supported("float32", 1024, 64, 128) and not lac.seq_supported("float32", 1024, 128, 128)
-    assert lac.seq_kernel_name(False, "bf16", 128, 128) == "la_fwd_kernel"
+    assert lac.seq_kernel_name(False, "bf16", 128, 128) == "la_seq_fwd_d128_kernel"
     assert lac.seq_kernel_name(True, "bf16", 64, 128) == "la_seq_bwd_d128_kernel"
     assert lac.seq_kernel_name(True, "bf16", 128, 128, "elu1") is None
     assert lac.seq_kernel_name(True, "bf16", 100, 128) is None
