@@ -134,13 +134,14 @@ def seq_supported(dtype, T: int, D: int, chunk: int, feature=None) -> bool:
     """Whether seq_fwd / seq_bwd take a (G, T, D) sequence in chunks of ``chunk`` tokens:
     bf16, and either D = 64 with 128-token chunks, whole chunks only (T up to SEQ_D64_MAX_T), or
     D = 128 with chunks a multiple of 64 tokens, the last one possibly shorter, T up to
-    SEQ_D128_MAX_T and no fused feature map."""
+    SEQ_D128_MAX_T; either with or without the fused feature map."""
     if _dt_code(dtype) != LA_BF16 or T < 1:
         return False
     if D == 64:
         return chunk == 128 and T % chunk == 0 and T <= SEQ_D64_MAX_T
     if D == 128:
-        return chunk >= 64 and chunk % 64 == 0 and T <= SEQ_D128_MAX_T and _feature_code(feature) == 0
+        _feature_code(feature)  # raises for an unknown feature map
+        return chunk >= 64 and chunk % 64 == 0 and T <= SEQ_D128_MAX_T
     return False
 
 

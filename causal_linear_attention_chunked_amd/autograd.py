@@ -120,7 +120,8 @@ def linear_attention(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int
     if fm is not None:
         if not seq_ok:
             raise ValueError(f"the fused feature map {feature_map!r} runs in the sequence kernels only "
-                             "(bf16, D = 64, whole 128-token chunks)")
+                             "(bf16; D = 64 in whole 128-token chunks, or D = 128 in chunks of a "
+                             "multiple of 64 tokens)")
         o, S, z = SeqFunction.apply(q, k, v, S_in, z_in, chunk, block, feature_map)
         return o, (S, z)
     if seq_ok:

@@ -65,7 +65,7 @@ la_status common_checks(int G, int C, int D, int block, la_dtype dt, Sizes *sz) 
 
 // Sequence entry points: the supported sets.  D = 64: bf16, 128-token chunks, whole chunks, T
 // up to LA_SEQ_D64_MAX_T.  D = 128: bf16, chunks a multiple of the 64-token block (the last one
-// may be ragged), T up to LA_SEQ_D128_MAX_T, no fused feature map.
+// may be ragged), T up to LA_SEQ_D128_MAX_T.  Both take the fused feature map.
 la_status seq_checks(int G, int T, int D, int chunk, int block, la_dtype dt, la_feature feature, Sizes *sz) {
     if (G < 1 || T < 1 || chunk < 1) return LA_ERR_INVALID;
     if (feature != LA_FEATURE_NONE && feature != LA_FEATURE_ELU1) return LA_ERR_INVALID;
@@ -73,8 +73,7 @@ la_status seq_checks(int G, int T, int D, int chunk, int block, la_dtype dt, la_
     if (st != LA_OK) return st;
     if (dt != LA_BF16) return LA_ERR_UNSUPPORTED;
     if (D == 64 && (chunk != 128 || T % chunk != 0 || T > LA_SEQ_D64_MAX_T)) return LA_ERR_UNSUPPORTED;
-    if (D == 128 && (chunk % BK_TOKENS != 0 || T > LA_SEQ_D128_MAX_T || feature != LA_FEATURE_NONE))
-        return LA_ERR_UNSUPPORTED;
+    if (D == 128 && (chunk % BK_TOKENS != 0 || T > LA_SEQ_D128_MAX_T)) return LA_ERR_UNSUPPORTED;
     size_t a, b;
     if (!mul_ok((size_t)G, (size_t)T, &a) || !mul_ok(a, (size_t)D * 2, &b)) return LA_ERR_INVALID;
     sz->tok = b;
@@ -183,7 +182,8 @@ la_status la_seq_fwd(const void *q, const void *k, const void *v, const float *S
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     // D = 128: one workgroup per group walks the whole sequence (la_seq_fwd_d128_kernel)
     const hipError_t e =
-        D == 128 ? lachunk::launch_seq_fwd_d128(q, k, v, S_in, z_in, o, S_out, z_out, S_res, z_res, G, T, s, te.ev)
+        D == 128 ? lachunk::launch_seq_fwd_d128(q, k, v, S_in, z_in, o, S_out, z_out, S_res, z_res, G, T,
+                                                feature == LA_FEATURE_ELU1, s, te.ev)
                  : lachunk::launch_seq_fwd_c128(q, k, v, S_in, z_in, o, S_out, z_out, S_res, z_res, G, T / chunk,
                                                 feature == LA_FEATURE_ELU1, s, te.ev);
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
@@ -213,7 +213,7 @@ la_status la_seq_bwd(const void *q, const void *k, const void *v, const float *S
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const hipError_t e =
         D == 128 ? lachunk::launch_seq_bwd_d128(q, k, v, S_last, z_last, S_res, z_res, dO, dS_out, dz_out, dq, dk,
-                                                dv, dS_in, dz_in, G, T, s, te.ev)
+                                                dv, dS_in, dz_in, G, T, feature == LA_FEATURE_ELU1, s, te.ev)
                  : lachunk::launch_seq_bwd_c128(q, k, v, S_last, z_last, S_res, z_res, dO, dS_out, dz_out, dq, dk,
                                                 dv, dS_in, dz_in, G, T / chunk, feature == LA_FEATURE_ELU1, s, te.ev);
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
@@ -300,11 +300,14 @@ const char *la_kernel_name(int backward, la_dtype dt, int C, int D) {
 }
 
 const char *la_seq_kernel_name(int backward, la_dtype dt, int chunk, int D, la_feature feature) {
-    if (dt == LA_BF16 && D == 128 && chunk >= BK_TOKENS && chunk % BK_TOKENS == 0 && feature == LA_FEATURE_NONE)
+    if (feature != LA_FEATURE_NONE && feature != LA_FEATURE_ELU1) return nullptr;
+    const bool fm = feature == LA_FEATURE_ELU1;
+    if (dt == LA_BF16 && D == 128 && chunk >= BK_TOKENS && chunk % BK_TOKENS == 0) {
+        if (fm) return backward ? "la_seq_bwd_d128_elu1_kernel" : "la_seq_fwd_d128_elu1_kernel";
         return backward ? "la_seq_bwd_d128_kernel" : "la_seq_fwd_d128_kernel";
+    }
     if (dt != LA_BF16 || D != 64 || chunk != 128) return nullptr;
-    if (feature == LA_FEATURE_ELU1) return backward ? "la_seq_bwd_c128w16_elu1_kernel" : "la_seq_fwd_c128_elu1_kernel";
-    if (feature != LA_FEATURE_NONE) return nullptr;
+    if (fm) return backward ? "la_seq_bwd_c128w16_elu1_kernel" : "la_seq_fwd_c128_elu1_kernel";
     return backward ? "la_seq_bwd_c128w16_kernel" : "la_seq_fwd_c128_kernel";
 }
 

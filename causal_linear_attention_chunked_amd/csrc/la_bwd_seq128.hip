@@ -33,6 +33,10 @@
 //   3  den, rho, inv, dden; dP (split, stored [t][j]); Sh_b split copy, zh_b
 //   4  dq; dv or dk of the wave's (key tile, column half); Sh_{b-1}, zh_{b-1}
 // Rows past the end of the sequence read as zero, get inv = 0 and are not stored.
+// FM: q and k are raw inputs, mapped by elu(x) + 1 as they are staged; dq and dk are the
+// gradients of the raw inputs, scaled at their stores by phi'(x) = min(1, phi) read back from the
+// mapped tiles.  Mapped rows past the end of the sequence are zero, as raw ones are (phi(0) = 1
+// would count the keys in the recovered z).
 #include "la_tile.h"
 #include "la_launch.h"
 #include <hip/hip_ext.h>
@@ -71,7 +75,8 @@ constexpr uint32_t key_table() {
 }
 }  // namespace
 
-__global__ __launch_bounds__(S128_THREADS, 1) void la_seq_bwd_d128_kernel(
+template <bool FM>
+__device__ __forceinline__ void bwd_seq128_body(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ S_last, const float *__restrict__ z_last, const float *__restrict__ S_res,
     const float *__restrict__ z_res, const bf16 *__restrict__ dO,
@@ -173,8 +178,9 @@ __global__ __launch_bounds__(S128_THREADS, 1) void la_seq_bwd_d128_kernel(
         {
             const int row = tid_b >> 4, f = (tid_b >> 3) & 1;
             const uint32_t so = f * TBYTES + stage_off(row * 8 + (tid_b & 7));
-            *reinterpret_cast<bf16x8 *>(smem + L::QT + so) = st[0];
-            *reinterpret_cast<bf16x8 *>(smem + L::KT + so) = st[1];
+            const bool live = row < nvalid;
+            *reinterpret_cast<bf16x8 *>(smem + L::QT + so) = FM ? (live ? elu1_8(st[0]) : bf16x8{}) : st[0];
+            *reinterpret_cast<bf16x8 *>(smem + L::KT + so) = FM ? (live ? elu1_8(st[1]) : bf16x8{}) : st[1];
             *reinterpret_cast<bf16x8 *>(smem + L::VT + so) = st[2];
             *reinterpret_cast<bf16x8 *>(smem + L::GT + so) = st[3];
         }
@@ -333,6 +339,8 @@ __global__ __launch_bounds__(S128_THREADS, 1) void la_seq_bwd_d128_kernel(
                     mma(acc, kx, tfrag(dph, TL, tq, jc));
                     mma(acc, kx, tfrag(dpl, TL, tq, jc));
                 }
+                // fused feature map: the raw query's gradient is dq phi'(x), phi' = min(1, phi)
+                if constexpr (FM) acc *= elu1_grad4(lds_b64(tq_(L::QT, pf) + tq * 16 * TROW + TL.nat_at(pl)));
                 if (valid) *reinterpret_cast<bf16x4 *>(dqrow + 16 * (2 * s + pp)) = pack4(acc);
             }
         }
@@ -396,7 +404,10 @@ __global__ __launch_bounds__(S128_THREADS, 1) void la_seq_bwd_d128_kernel(
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
                     floatx4 y = acc[x];
-                    if (p2dk) y += *reinterpret_cast<const floatx4 *>(zh + 64 * oh + 16 * x + 4 * g);
+                    if (p2dk) {
+                        y += *reinterpret_cast<const floatx4 *>(zh + 64 * oh + 16 * x + 4 * g);
+                        if constexpr (FM) y *= elu1_grad4(lds_b64(tq_(L::KT, oh) + jt2 * 16 * TROW + TL.nat[x]));
+                    }
                     *reinterpret_cast<bf16x4 *>(row + 16 * x) = pack4(y);
                 }
             }
@@ -452,11 +463,33 @@ __global__ __launch_bounds__(S128_THREADS, 1) void la_seq_bwd_d128_kernel(
     }
 }
 
+__global__ __launch_bounds__(S128_THREADS, 1) void la_seq_bwd_d128_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_last, const float *__restrict__ z_last, const float *__restrict__ S_res,
+    const float *__restrict__ z_res, const bf16 *__restrict__ dO,
+    const float *__restrict__ dS_out, const float *__restrict__ dz_out,
+    bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
+    float *__restrict__ dS_in, float *__restrict__ dz_in, int T) {
+    bwd_seq128_body<false>(q, k, v, S_last, z_last, S_res, z_res, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, T);
+}
+
+// the same with the feature map fused: dq and dk are the gradients of the raw inputs
+__global__ __launch_bounds__(S128_THREADS, 1) void la_seq_bwd_d128_elu1_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_last, const float *__restrict__ z_last, const float *__restrict__ S_res,
+    const float *__restrict__ z_res, const bf16 *__restrict__ dO,
+    const float *__restrict__ dS_out, const float *__restrict__ dz_out,
+    bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
+    float *__restrict__ dS_in, float *__restrict__ dz_in, int T) {
+    bwd_seq128_body<true>(q, k, v, S_last, z_last, S_res, z_res, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, T);
+}
+
 hipError_t launch_seq_bwd_d128(const void *q, const void *k, const void *v, const float *S_last,
                                const float *z_last, const float *S_res, const float *z_res, const void *dO,
                                const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv, float *dS_in,
-                               float *dz_in, int G, int T, hipStream_t stream, const hipEvent_t ev[2]) {
-    hipExtLaunchKernelGGL(la_seq_bwd_d128_kernel, dim3((unsigned)G), dim3(S128_THREADS), 0, stream, ev[0], ev[1], 0,
+                               float *dz_in, int G, int T, bool elu1, hipStream_t stream, const hipEvent_t ev[2]) {
+    hipExtLaunchKernelGGL(elu1 ? la_seq_bwd_d128_elu1_kernel : la_seq_bwd_d128_kernel, dim3((unsigned)G),
+                          dim3(S128_THREADS), 0, stream, ev[0], ev[1], 0,
                           (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_last, z_last, S_res, z_res,
                           (const bf16 *)dO, dS_out, dz_out, (bf16 *)dq, (bf16 *)dk, (bf16 *)dv, dS_in, dz_in, T);
     return hipGetLastError();

@@ -21,6 +21,11 @@
 // The next chunk's keys and values are loaded into the staging registers as soon as those are
 // free, and a wave's queries right after its outputs are stored.  A ragged end is a masked
 // block: rows past the sequence read as zero (buffer ranges) and are not stored.
+// FM: q and k are raw inputs and the positive feature map elu(x) + 1 is applied inside, in the
+// registers they arrive in and in the phase where the wave computes no outputs: block 0's waves
+// map the next chunk's queries and staged keys in phase C, block 1's waves their queries, this
+// chunk's second-block keys and the next chunk's first-block keys in phase B.  Mapped keys past
+// the end of the sequence are zero, as raw ones are (phi(0) = 1 would count them in z).
 #include "la_tile.h"
 #include "la_launch.h"
 #include <hip/hip_ext.h>
@@ -41,7 +46,8 @@ struct Fwd128Lds {
 };
 }  // namespace
 
-__global__ __launch_bounds__(F128_THREADS, 1) void la_seq_fwd_d128_kernel(
+template <bool FM>
+__device__ __forceinline__ void fwd_seq128_body(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ S_in, const float *__restrict__ z_in, bf16 *__restrict__ o,
     float *__restrict__ S_out, float *__restrict__ z_out, float *__restrict__ S_res, float *__restrict__ z_res,
@@ -86,6 +92,19 @@ __global__ __launch_bounds__(F128_THREADS, 1) void la_seq_fwd_d128_kernel(
         for (int kc = 0; kc < 4; ++kc) qf[kc] = ldfrag_g<bf16>(qr, (tok + 64 * blk + 16 * tq) * D + 32 * kc, D, lane);
     };
     load_q(0);
+    auto map_q = [&]() {
+        if constexpr (FM) {
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) qf[kc] = elu1_8(qf[kc]);
+        }
+    };
+    // staging registers rr of chunk cc mapped in place (rows tid / 16 + 32 (rr % 2) of block rr / 2)
+    auto map_k = [&](int rr, int cc) {
+        if constexpr (FM) {
+            const int row = 64 * (rr >> 1) + (tid >> 4) + 32 * (rr & 1);
+            kst[rr] = row < T - cc * C ? elu1_8(kst[rr]) : bf16x8{};
+        }
+    };
     floatx4 Sacc[2][4], Scomp[2][4];
     float zr[4], zc[4];
     {
@@ -107,6 +126,14 @@ __global__ __launch_bounds__(F128_THREADS, 1) void la_seq_fwd_d128_kernel(
     load_kv(2, 0);
     load_kv(3, 0);
     issue_fence();
+    // the first chunk's keys (block 0's waves also their queries and block 1's keys)
+    map_k(0, 0);
+    map_k(1, 0);
+    if (blk == 0) {
+        map_q();
+        map_k(2, 0);
+        map_k(3, 0);
+    }
     const bf16x8 ones = ones_frag<bf16>();
 
     using Blk0 = std::integral_constant<int, 0>;
@@ -240,17 +267,32 @@ __global__ __launch_bounds__(F128_THREADS, 1) void la_seq_fwd_d128_kernel(
         // ---- phase B: S_1 (copy, z_1 row); block 0's outputs; block 1's keys and values
         advance(0);
         write_state(1);
-        if (blk == 0) outputs(Blk0{});
+        if (blk == 0) {
+            outputs(Blk0{});
+        } else {
+            map_q();
+            map_k(2, c);
+            map_k(3, c);
+        }
         stage(2);
         stage(3);
         load_kv(2, cbase + CHUNK);
         load_kv(3, cbase + CHUNK);
+        if (blk == 1 && c + 1 < n) {
+            map_k(0, c + 1);
+            map_k(1, c + 1);
+        }
         lds_barrier();
 
         // ---- phase C: block 1's outputs; the state after the chunk.  No barrier follows: the next
         // chunk's phase A writes block 0's tiles, the S_0 copy and z_0 row, which phase C does not read.
         if (blk == 1) outputs(Blk1{});
         advance(1);
+        if (blk == 0 && c + 1 < n) {
+            map_q();
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) map_k(rr, c + 1);
+        }
     }
     {
         const int lane = tid & 63, r = lane & 15, g = lane >> 4;
@@ -284,10 +326,28 @@ __global__ __launch_bounds__(F128_THREADS, 1) void la_seq_fwd_d128_kernel(
     }
 }
 
+__global__ __launch_bounds__(F128_THREADS, 1) void la_seq_fwd_d128_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_in, const float *__restrict__ z_in, bf16 *__restrict__ o,
+    float *__restrict__ S_out, float *__restrict__ z_out, float *__restrict__ S_res, float *__restrict__ z_res,
+    int T) {
+    fwd_seq128_body<false>(q, k, v, S_in, z_in, o, S_out, z_out, S_res, z_res, T);
+}
+
+// the same with the feature map fused: q and k are the raw inputs x, the op uses elu(x) + 1
+__global__ __launch_bounds__(F128_THREADS, 1) void la_seq_fwd_d128_elu1_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_in, const float *__restrict__ z_in, bf16 *__restrict__ o,
+    float *__restrict__ S_out, float *__restrict__ z_out, float *__restrict__ S_res, float *__restrict__ z_res,
+    int T) {
+    fwd_seq128_body<true>(q, k, v, S_in, z_in, o, S_out, z_out, S_res, z_res, T);
+}
+
 hipError_t launch_seq_fwd_d128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
                                void *o, float *S_out, float *z_out, float *S_res, float *z_res, int G, int T,
-                               hipStream_t stream, const hipEvent_t ev[2]) {
-    hipExtLaunchKernelGGL(la_seq_fwd_d128_kernel, dim3((unsigned)G), dim3(F128_THREADS), 0, stream, ev[0], ev[1], 0,
+                               bool elu1, hipStream_t stream, const hipEvent_t ev[2]) {
+    hipExtLaunchKernelGGL(elu1 ? la_seq_fwd_d128_elu1_kernel : la_seq_fwd_d128_kernel, dim3((unsigned)G),
+                          dim3(F128_THREADS), 0, stream, ev[0], ev[1], 0,
                           (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_in, z_in, (bf16 *)o, S_out, z_out,
                           S_res, z_res, T);
     return hipGetLastError();

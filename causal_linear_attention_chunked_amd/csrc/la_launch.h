@@ -42,14 +42,14 @@ hipError_t launch_seq_bwd_c128(const void *q, const void *k, const void *v, cons
 // end is a masked block), S and z carried with compensation, remainders out as above.
 hipError_t launch_seq_fwd_d128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
                                void *o, float *S_out, float *z_out, float *S_res, float *z_res, int G, int T,
-                               hipStream_t stream, const hipEvent_t ev[2]);
+                               bool elu1, hipStream_t stream, const hipEvent_t ev[2]);
 
 // bf16, D = 128: the backward over a whole sequence of T tokens per group (any T >= 1, the last
 // 64-token block possibly ragged), last block first, from the carry after the last token.
 hipError_t launch_seq_bwd_d128(const void *q, const void *k, const void *v, const float *S_last,
                                const float *z_last, const float *S_res, const float *z_res, const void *dO,
                                const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv, float *dS_in,
-                               float *dz_in, int G, int T, hipStream_t stream, const hipEvent_t ev[2]);
+                               float *dz_in, int G, int T, bool elu1, hipStream_t stream, const hipEvent_t ev[2]);
 
 // Cross-entropy over a tied head (bf16 h, W; fp32 loss, lse, dW; bf16 dh).  The shape of the
 // workspace: padded sizes, the backward's chunking and the split of dh over the vocabulary.

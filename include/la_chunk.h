@@ -147,8 +147,8 @@ la_status la_chunk_bwd(const void *q, const void *k, const void *v,
  * Supported (block == 64, dt == LA_BF16):
  *   - D == 64: chunk == 128 and T a positive multiple of 128, T <= LA_SEQ_D64_MAX_T;
  *   - D == 128: chunk a positive multiple of 64, 1 <= T <= LA_SEQ_D128_MAX_T (the last
- *     chunk may be shorter than chunk, as a chain's last call may be), feature ==
- *     LA_FEATURE_NONE.  Blocks of 64 tokens start at multiples of 64 in both forms, so
+ *     chunk may be shorter than chunk, as a chain's last call may be).  Blocks of 64
+ *     tokens start at multiples of 64 in both forms, so
  *     the chunk length does not change the arithmetic; a ragged end is computed as a
  *     masked block (the chained calls take it token by token: another summation order).
  * Anything else returns LA_ERR_UNSUPPORTED (chain la_chunk_fwd calls instead).  A

@@ -154,14 +154,14 @@ def seq_bwd_call(lib, G=4, T=512, D=64, chunk=128, block=64, feature=0, dt=1, **
     (dict(G=0), INVALID), (dict(T=0), INVALID), (dict(chunk=0), INVALID),
     (dict(T=500), UNSUPPORTED),                          # not whole chunks
     (dict(chunk=64, T=512), UNSUPPORTED), (dict(dt=0), UNSUPPORTED),
-    # D = 128: chunks a multiple of 64, no fused feature map, T up to the limit
-    (dict(D=128, chunk=100, T=500), UNSUPPORTED), (dict(D=128, feature=1), UNSUPPORTED),
+    # D = 128: chunks a multiple of 64, T up to the limit
+    (dict(D=128, chunk=100, T=500), UNSUPPORTED), (dict(D=128, feature=1, T=500, chunk=96), UNSUPPORTED),
     (dict(D=128, T=lac.SEQ_D128_MAX_T + 1), UNSUPPORTED), (dict(D=128, T=0), INVALID),
     (dict(block=32), UNSUPPORTED), (dict(T=lac.SEQ_D64_MAX_T + 128), UNSUPPORTED),
     (dict(q=None), INVALID), (dict(S_in=None), INVALID),
     (dict(v=ctypes.c_void_p(BASE + 2 * STEP + 8)), ALIGN),
     (dict(o=addr(1)), ALIAS), (dict(S_out=addr(3)), ALIAS),
-    (dict(feature=2), INVALID), (dict(feature=-1), INVALID), (dict(feature=1, D=128), UNSUPPORTED),
+    (dict(feature=2), INVALID), (dict(feature=-1), INVALID), (dict(feature=2, D=128), INVALID),
     (dict(S_res=None), INVALID), (dict(z_res=None), INVALID),   # the remainders come together
     (dict(S_res=addr(6)), ALIAS),                        # S_res == S_out
     (dict(z_res=ctypes.c_void_p(BASE + 9 * STEP + 8)), ALIGN),
@@ -198,12 +198,14 @@ def test_seq_kernel_names(lib):
     assert not lac.seq_supported("float32", 1024, 64, 128) and not lac.seq_supported("float32", 1024, 128, 128)
     assert lac.seq_kernel_name(False, "bf16", 128, 128) == "la_seq_fwd_d128_kernel"
     assert lac.seq_kernel_name(True, "bf16", 64, 128) == "la_seq_bwd_d128_kernel"
-    assert lac.seq_kernel_name(True, "bf16", 128, 128, "elu1") is None
+    assert lac.seq_kernel_name(True, "bf16", 128, 128, "elu1") == "la_seq_bwd_d128_elu1_kernel"
+    assert lac.seq_kernel_name(False, "bf16", 192, 128, "elu1") == "la_seq_fwd_d128_elu1_kernel"
     assert lac.seq_kernel_name(True, "bf16", 100, 128) is None
     assert lac.seq_supported("bf16", 8164, 128, 128) and lac.seq_supported("bf16", 1, 128, 64)
     assert not lac.seq_supported("bf16", 8164, 128, 100) and not lac.seq_supported("bf16", 16448, 128, 128)
     assert lac.seq_supported("bf16", 1 << 20, 64, 128) and not lac.seq_supported("bf16", (1 << 20) + 128, 64, 128)
-    assert not lac.seq_supported("bf16", 1024, 128, 128, "elu1")
+    assert lac.seq_supported("bf16", 1000, 128, 128, "elu1")
+    assert not lac.seq_supported("bf16", 1000, 64, 128, "elu1")
 
 
 CE_WS = 1 << 30  # a fake workspace size large enough for every shape below

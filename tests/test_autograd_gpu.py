@@ -82,3 +82,8 @@ def test_autograd_sequence_entry_points_wide_heads(gpu):
 
 def test_autograd_fused_feature_map(gpu):
     _case("bf16", "prior", True, G=3, T=384, feature_map="elu1")
+
+
+def test_autograd_fused_feature_map_wide_heads(gpu):
+    # D = 128 with a ragged end: the mapped rows past the end must stay out of z
+    _case("bf16", "zero", True, G=2, T=230, D=128, feature_map="elu1")

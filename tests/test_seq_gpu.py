@@ -246,6 +246,42 @@ def test_seq_d128_longest_sequence(gpu):
     compare(run_seq_d128(I, dS, dz), oracle_ref(I, dS, dz))
 
 
+@pytest.mark.parametrize("G,T,carry,up", [
+    (2, 200, "zero", True),      # an 8-token ragged end: phi(0) = 1 must not enter z past it
+    (3, 64, "prior", False),     # one full block
+    (1, 1, "prior", True),       # a single token (from a zero carry its exact dq is 0: degenerate)
+    (2, 1000, "prior", True),    # 15 blocks and 40 tokens
+])
+def test_seq_d128_fused_feature_map(gpu, G, T, carry, up):
+    # raw q, k (both signs) at D = 128; the op applies elu(x)+1, gradients of the raw inputs
+    say(f"[case] seq D=128 elu1 G={G} T={T} carry={carry} upstream={up}")
+    I = inp.make_inputs(G=G, T=T, D=128, dtype="bf16", carry=carry, backward=True, seed=70 + T,
+                        features="raw")
+    dS, dz = upstream(G, 128, 71) if up else (None, None)
+    compare(run_seq(I, dS, dz, feature="elu1"), oracle_ref(I, dS, dz, feature="elu1"))
+
+
+@pytest.mark.parametrize("shift", [-4.0, 4.0])
+def test_seq_d128_fused_feature_map_branches(gpu, shift):
+    # raw inputs pushed deep into one branch of elu: e^x (small features) or x + 1
+    G, T = 2, 300
+    say(f"[case] seq D=128 elu1 raw inputs shifted by {shift}")
+    I = inp.make_inputs(G=G, T=T, D=128, dtype="bf16", carry="zero", backward=True, seed=74, features="raw")
+    for n in ("q", "k"):
+        I[n] = (I[n].float() + shift).to(torch.bfloat16)
+    compare(run_seq(I, feature="elu1"), oracle_ref(I, feature="elu1"))
+
+
+def test_seq_d128_fused_feature_map_wide_head_workload(gpu):
+    # the wide-head workload's shapes (63 x 128 + 100 tokens, 160 groups) on raw inputs
+    w = inp.workload("g160_63x128p100_d128_bf16_fwdbwd")
+    say(f"[case] seq D=128 elu1 full {w.name}")
+    I = inp.make_inputs(G=w.G, T=w.T, D=w.D, dtype=w.dtype, carry=w.carry, backward=True, seed=w.seed,
+                        features="raw")
+    groups = [0, 101, 159]
+    compare(run_seq(I, feature="elu1"), oracle_ref(I, groups=groups, feature="elu1"), groups)
+
+
 def test_seq_d128_matches_chained_calls(gpu):
     # the chunk length (a multiple of 64) does not change the arithmetic: results bit for bit;
     # against the chained calls, to fp32 rounding (compensated carry, the ragged end as a
@@ -290,4 +326,4 @@ def test_seq_rejects_unsupported(gpu):
     with pytest.raises(lac.LachunkError, match="UNSUPPORTED"):
         lac.seq_fwd(y, y, y, chunk=100)
     with pytest.raises(lac.LachunkError, match="UNSUPPORTED"):
-        lac.seq_fwd(y, y, y, feature="elu1")
+        lac.seq_fwd(y, y, y, chunk=96, feature="elu1")
