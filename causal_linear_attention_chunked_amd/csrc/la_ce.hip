@@ -4,13 +4,16 @@
 //   logit_iv = h_i . W_v,  lse_i = log sum_v exp(logit_iv),  loss = (1/N) sum_i (lse_i - logit_{i,t_i})
 //   P_iv = (g/N) (exp(logit_iv - lse_i) - [v = t_i]),  dh = P W,  dW = P^T h
 //
-// Every product is one MFMA GEMM mainloop (bf16 operands, fp32 accumulators): a 128 x 128
-// output tile per workgroup of four waves (64 x 64 each, 16 accumulator tiles), the operands
-// staged 64 k at a time into two LDS buffers of swizzled 64 x 64 tiles (csrc/la_tile.h) while
-// the next k-step's loads are in flight.  An operand is read from LDS with the natural fragment
-// read when it is stored k-contiguous and with the transposed read when it is stored k-major, so
-// no operand is ever transposed in memory.  Operand rows past the end read as zero (buffer
-// ranges).  The epilogues:
+// Every product is one MFMA GEMM mainloop (bf16 operands, fp32 accumulators): a 256 x 128
+// output tile per workgroup of eight waves (64 x 64 each, 16 accumulator tiles), the operands
+// loaded 64 k at a time straight from global memory into three LDS stages (buffer loads that
+// write LDS), two k-steps ahead of the products.  The loads fill the swizzled 64 x 64 tile layout
+// of csrc/la_tile.h: each load instruction writes 1 KB of consecutive LDS (eight tile rows), so
+// every lane fetches the 16 bytes that belong in its slot.  An operand is read from LDS with the
+// natural fragment read when it is stored k-contiguous and with the transposed read when it is
+// stored k-major, so no operand is ever transposed in memory.  Operand rows past the end of an
+// operand read as zero (buffer ranges), or, for a k-major operand whose rows end inside its
+// storage rows, as values that only reach output rows that are not stored.  The epilogues:
 //   forward: the tile's logits never leave registers: per token, the maximum and the sum of
 //            exponentials over the tile's 128 classes (combined over the two waves in LDS) go to
 //            a partials array, and the target's logit where it falls in the tile; a second kernel
@@ -27,64 +30,91 @@
 namespace lachunk {
 
 namespace {
-constexpr int CE_THREADS = 256;
-constexpr int CT = 128;  // output tile edge
-constexpr int CK = 64;   // k per stage
+constexpr int CE_THREADS = 512;  // eight waves
+constexpr int MT = 256;          // output tile rows (the A operand's)
+constexpr int NT = 128;          // output tile columns (the B operand's)
+constexpr int CK = 64;           // k per stage
+constexpr int STAGE = (MT + NT) / 64 * TBYTES;  // one stage: A tiles 0-3, then B tiles 0-1 (48 KB)
 
-// Offsets (bytes) of one stage's four tiles: A rows 0-63, 64-127, then B likewise.
-__device__ __forceinline__ char *stage_tile(char *smem, int stage, int op, int u) {
-    return smem + ((stage * 2 + op) * 2 + u) * TBYTES;
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer descriptor of `bytes` bytes at `base` as four dwords (the layout and flags of GRes):
+// reads at offsets past the range return zero and touch no memory.
+__device__ __forceinline__ int4v rsrc4(const void *base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    return int4v{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
 
 struct Operand {
-    GRes g;
+    int4v rs;      // buffer descriptor (uniform)
     uint32_t ld;   // elements between consecutive storage rows
     bool kmajor;   // stored [k][row] (row contiguous) instead of [row][k]
 };
 
-// The 128 x 128 fp32 tile C[m][n] = sum_k A[m][k] B[n][k] over k in [k0, k1) (multiples of 64),
-// m from row m0 of A, n from row n0 of B.  Wave w holds rows 64 (w & 1).. of m and 64 (w >> 1)..
+// Load into LDS: each lane's 16 bytes at voff go to LDS byte lds + 16 x lane; lds is
+// uniform (M0).  Issued as assembly, so the compiler neither counts them nor orders LDS reads
+// after them: the main loop waits for them itself (vmcnt) and a barrier publishes them.  Loads
+// the compiler does not know of can only make its own waits for its own loads stricter.
+__device__ __forceinline__ void lds_load16(const int4v &rs, const void *lds, uint32_t voff) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "{m0}"((uint32_t)(size_t)(lds_void *)lds)
+                 : "memory");
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt untouched), n < 16
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm() {
+    static_assert(n >= 0 && n < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0070 | n);
+}
+
+// The 256 x 128 fp32 tile C[m][n] = sum_k A[m][k] B[n][k] over k in [k0, k1) (multiples of 64),
+// m from row m0 of A, n from row n0 of B.  Wave w holds rows 64 (w & 3).. of m and 64 (w >> 2)..
 // of n: acc[i][j] is the 16 x 16 tile (m-tile i, n-tile j), lane (r, g) holding
-// C[m = 16 i + 4 g + e][n = 16 j + r].
+// C[m = 16 i + 4 g + e][n = 16 j + r].  s0, s1, s2: the three stages, separate LDS arrays (so
+// that the compiler can tell the stage being loaded from the one being read).
+//
+// Pipeline: stage k-step ks is loaded into s[ks % 3] two steps ahead.  Each step waits for its
+// own wave's loads of the step (vmcnt: the loads issued after them may stay in flight) and for
+// its LDS reads, then a barrier: every wave's loads of the step have landed and every wave is
+// done reading the stage the step after next is loaded into, which is issued next; then the
+// products.  The loads of the k-steps past the end are issued too, at an offset past every
+// buffer range (no memory is read), so that every step has the same loads in flight.
 template <bool AKM, bool BKM>
-__device__ __forceinline__ void gemm_tile(char *smem, const Operand &A, const Operand &B, uint32_t m0, uint32_t n0,
-                                          uint32_t k0, uint32_t k1, floatx4 (&acc)[4][4]) {
+__device__ __forceinline__ void gemm_tile(char *s0, char *s1, char *s2, const Operand &A, const Operand &B,
+                                          uint32_t m0, uint32_t n0, uint32_t k0, uint32_t k1, floatx4 (&acc)[4][4]) {
     const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 1, wn = w >> 1;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 3, wn = w >> 2;
     const TileLanes TL(lane);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
-    // thread tid stages 16 bytes of storage rows tid / 8 and tid / 8 + 32 of each 64 x 64 tile
-    const int srow = tid >> 3, sunit = tid & 7;
-    typedef bf16x8 Stage[2][2][2];  // [operand][tile][half]
-    auto load = [&](Stage &st, uint32_t kk) {
+    // Load instruction i of wave w writes rows 8w..8w+7 of tile i (A tiles 0-3, then B tiles 0-1);
+    // lane l lands in storage row y = 8w + l / 8, 16-byte slot l % 8, which holds the row's logical
+    // 16-byte unit (l % 8) ^ (swz(y) / 2).  Element offsets of the lane's units at k = 0:
+    const int y = 8 * w + (lane >> 3);
+    const int uu = (lane & 7) ^ ((y ^ (y >> 1)) & 7);
+    uint32_t offa[4], offb[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+    for (int i = 0; i < 4; ++i)
+        offa[i] = AKM ? (uint32_t)y * A.ld + m0 + 64 * i + 8 * uu : (m0 + 64 * i + (uint32_t)y) * A.ld + 8 * uu;
 #pragma unroll
-            for (int hv = 0; hv < 2; ++hv) {
-                const uint32_t row = srow + 32 * hv;
-                const uint32_t oa = AKM ? (kk + row) * A.ld + m0 + 64 * u + 8 * sunit
-                                        : (m0 + 64 * u + row) * A.ld + kk + 8 * sunit;
-                const uint32_t ob = BKM ? (kk + row) * B.ld + n0 + 64 * u + 8 * sunit
-                                        : (n0 + 64 * u + row) * B.ld + kk + 8 * sunit;
-                st[0][u][hv] = gload<bf16x8>(A.g, oa * 2);
-                st[1][u][hv] = gload<bf16x8>(B.g, ob * 2);
-            }
+    for (int i = 0; i < 2; ++i)
+        offb[i] = BKM ? (uint32_t)y * B.ld + n0 + 64 * i + 8 * uu : (n0 + 64 * i + (uint32_t)y) * B.ld + 8 * uu;
+    constexpr uint32_t PAST = 0x80000000u;  // byte offset past every operand's range (< 2^31 bytes)
+    auto issue = [&](char *st, uint32_t kk, bool live) {
+        const uint32_t ka = AKM ? kk * A.ld : kk, kb = BKM ? kk * B.ld : kk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_load16(A.rs, st + i * TBYTES + 1024 * w, live ? (offa[i] + ka) * 2 : PAST);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            lds_load16(B.rs, st + (4 + i) * TBYTES + 1024 * w, live ? (offb[i] + kb) * 2 : PAST);
     };
-    auto store = [&](const Stage &st, int stage) {
-#pragma unroll
-        for (int op = 0; op < 2; ++op)
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int hv = 0; hv < 2; ++hv)
-                    *reinterpret_cast<bf16x8 *>(stage_tile(smem, stage, op, u) + stage_off(tid + 256 * hv)) =
-                        st[op][u][hv];
-    };
-    auto compute = [&](int stage) {
-        const char *At = stage_tile(smem, stage, 0, wm), *Bt = stage_tile(smem, stage, 1, wn);
+    auto compute = [&](const char *st) {
+        const char *At = st + wm * TBYTES, *Bt = st + (4 + wn) * TBYTES;
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
             bf16x8 af[4], bfr[4];
@@ -99,22 +129,26 @@ __device__ __forceinline__ void gemm_tile(char *smem, const Operand &A, const Op
                 for (int j = 0; j < 4; ++j) mma(acc[i][j], af[i], bfr[j]);
         }
     };
-    // One register stage: the next k-step's loads are issued before this one's products and
-    // stored after them.  Measured and rejected: two stages a full k-step ahead (more registers,
-    // slower), A fragments read one at a time (less overlap, slower), one 16-byte read per
-    // fragment in the contiguous k order for k-contiguous operands (slower).
     const int nk = (int)((k1 - k0) / CK);
-    Stage r0;
-    load(r0, k0);
-    store(r0, 0);
-    lds_barrier();
-    for (int ks = 0; ks < nk; ++ks) {
-        const bool more = ks + 1 < nk;
-        if (more) load(r0, k0 + (uint32_t)(ks + 1) * CK);
-        compute(ks & 1);
-        if (more) store(r0, (ks & 1) ^ 1);
-        lds_barrier();
+    auto step = [&](char *cur, char *nxt, int ks) {
+        wait_vm_lgkm<6>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(nxt, k0 + (uint32_t)(ks + 2) * CK, ks + 2 < nk);
+        compute(cur);
+    };
+    issue(s0, k0, true);
+    issue(s1, k0 + CK, nk > 1);
+    for (int ks = 0;;) {
+        step(s0, s2, ks);
+        if (++ks == nk) break;
+        step(s1, s0, ks);
+        if (++ks == nk) break;
+        step(s2, s1, ks);
+        if (++ks == nk) break;
     }
+    wait_vm_lgkm<0>();  // the two loads past the end; the stages may be reused after a barrier
 }
 
 // max over the four lane groups (lanes l, l^16, l^32, l^48)
@@ -141,22 +175,25 @@ __device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(
 // Forward tiles: one workgroup per (class tile, token tile).  The A operand is W (rows = classes), B is
 // h (rows = tokens), both k-contiguous.  part[vt][t] = (max, sum exp(logit - max)) over the tile's
 // classes, tl[t] = logit of token t's target (written by the one lane that holds it).
-__global__ __launch_bounds__(CE_THREADS, 2) void la_ce_fwd_kernel(
+__global__ __launch_bounds__(CE_THREADS, 1) void la_ce_fwd_kernel(
     const bf16 *__restrict__ h, const bf16 *__restrict__ W, const int *__restrict__ targets,
     floatx2 *__restrict__ part, float *__restrict__ tl, int N, int d, int V, int Npad) {
-    __shared__ __attribute__((aligned(16))) char smem[8 * TBYTES];
+    __shared__ __attribute__((aligned(16))) char s0[STAGE];
+    __shared__ __attribute__((aligned(16))) char s1[STAGE];
+    __shared__ __attribute__((aligned(16))) char s2[STAGE];
     // logical tile: the token tiles of one class tile consecutively (they share its rows of W)
-    const uint32_t ntt = (uint32_t)Npad / CT;
+    const uint32_t ntt = (uint32_t)Npad / NT;
     const uint32_t L = xcd_tile(blockIdx.x, gridDim.x), vt = L / ntt;
-    const uint32_t v0 = vt * CT, t0 = (L % ntt) * CT;
-    const Operand A{GRes(W, (uint32_t)V * d * 2), (uint32_t)d, false};
-    const Operand B{GRes(h, (uint32_t)N * d * 2), (uint32_t)d, false};
+    const uint32_t v0 = vt * MT, t0 = (L % ntt) * NT;
+    const Operand A{rsrc4(W, (uint32_t)V * d * 2), (uint32_t)d, false};
+    const Operand B{rsrc4(h, (uint32_t)N * d * 2), (uint32_t)d, false};
     floatx4 acc[4][4];
-    gemm_tile<false, false>(smem, A, B, v0, t0, 0, (uint32_t)d, acc);
+    gemm_tile<false, false>(s0, s1, s2, A, B, v0, t0, 0, (uint32_t)d, acc);
+    lds_barrier();  // every wave done with the stages: s0 takes the exchange below
 
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 1, wn = w >> 1;
-    floatx2 *const xch = reinterpret_cast<floatx2 *>(smem);  // [2 wm][128 tokens]
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 3, wn = w >> 2;
+    floatx2 *const xch = reinterpret_cast<floatx2 *>(s0);  // [4 wm][128 tokens]
     const GRes tres(targets, (uint32_t)N * 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -182,14 +219,22 @@ __global__ __launch_bounds__(CE_THREADS, 2) void la_ce_fwd_kernel(
                 s += vv < V ? exp_f(acc[i][j][e] - mx) : 0.f;
             }
         s = gsum(s);
-        if (g == 0) xch[wm * CT + tloc] = floatx2{mx, s};
+        if (g == 0) xch[wm * NT + tloc] = floatx2{mx, s};
     }
     lds_barrier();
-    if (tid < CT) {
-        const floatx2 a = xch[tid], b = xch[CT + tid];
-        const float m = fmaxf(a[0], b[0]);
-        // a tile's classes may all lie past V only if V <= v0, which the grid excludes
-        const float s = a[1] * exp_f(a[0] - m) + b[1] * exp_f(b[0] - m);
+    if (tid < NT) {
+        // a wave's classes may all lie past V (then max -inf, sum 0); the first wave's never do, as
+        // the grid holds no tile with V <= v0
+        floatx2 x[4];
+        float m = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[k] = xch[k * NT + tid];
+            m = fmaxf(m, x[k][0]);
+        }
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s += x[k][1] * exp_f(x[k][0] - m);
         part[(size_t)vt * Npad + t0 + tid] = floatx2{m, s};
     }
 }
@@ -240,21 +285,23 @@ __global__ __launch_bounds__(1024, 1) void la_ce_mean_kernel(const float *__rest
 
 // Backward P tiles for the tokens [c0, c0 + Nc): the logits recomputed, P = scale (softmax - onehot)
 // in bf16 at P[t - c0][v] (pitch Vpad); classes past V and tokens past the chunk get 0.
-__global__ __launch_bounds__(CE_THREADS, 2) void la_ce_p_kernel(
+__global__ __launch_bounds__(CE_THREADS, 1) void la_ce_p_kernel(
     const bf16 *__restrict__ h, const bf16 *__restrict__ W, const int *__restrict__ targets,
     const float *__restrict__ lse, const float *__restrict__ dloss, bf16 *__restrict__ P, int c0, int Nc, int N,
     int d, int V, int Vpad) {
-    __shared__ __attribute__((aligned(16))) char smem[8 * TBYTES];
-    const uint32_t ntt = (uint32_t)(Nc + CT - 1) / CT;
+    __shared__ __attribute__((aligned(16))) char s0[STAGE];
+    __shared__ __attribute__((aligned(16))) char s1[STAGE];
+    __shared__ __attribute__((aligned(16))) char s2[STAGE];
+    const uint32_t ntt = (uint32_t)(Nc + NT - 1) / NT;
     const uint32_t L = xcd_tile(blockIdx.x, gridDim.x);
-    const uint32_t v0 = (L / ntt) * CT, t0 = (L % ntt) * CT;
-    const Operand A{GRes(W, (uint32_t)V * d * 2), (uint32_t)d, false};
-    const Operand B{GRes(h + (size_t)c0 * d, (uint32_t)Nc * d * 2), (uint32_t)d, false};
+    const uint32_t v0 = (L / ntt) * MT, t0 = (L % ntt) * NT;
+    const Operand A{rsrc4(W, (uint32_t)V * d * 2), (uint32_t)d, false};
+    const Operand B{rsrc4(h + (size_t)c0 * d, (uint32_t)Nc * d * 2), (uint32_t)d, false};
     floatx4 acc[4][4];
-    gemm_tile<false, false>(smem, A, B, v0, t0, 0, (uint32_t)d, acc);
+    gemm_tile<false, false>(s0, s1, s2, A, B, v0, t0, 0, (uint32_t)d, acc);
 
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 1, wn = w >> 1;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 3, wn = w >> 2;
     const float scale = (dloss ? *dloss : 1.f) / (float)N;
     const GRes tres(targets + c0, (uint32_t)Nc * 4), lres(lse + c0, (uint32_t)Nc * 4);
 #pragma unroll
@@ -279,23 +326,27 @@ __global__ __launch_bounds__(CE_THREADS, 2) void la_ce_p_kernel(
 }
 
 // dW tiles: C[m = feature][n = class] = sum_t h[t][m] P[t][n] over the chunk's (padded) tokens;
-// both operands k-major.  Stored as dW[n][m] (fp32), or added to it (accumulate).
-__global__ __launch_bounds__(CE_THREADS, 2) void la_ce_dw_kernel(const bf16 *__restrict__ h,
+// both operands k-major.  Stored as dW[n][m] (fp32), or added to it (accumulate).  Features past d
+// (the last feature tile when d is an odd multiple of 128) are not stored.
+__global__ __launch_bounds__(CE_THREADS, 1) void la_ce_dw_kernel(const bf16 *__restrict__ h,
                                                                  const bf16 *__restrict__ P, float *__restrict__ dW,
                                                                  int c0, int Nc, int Ncpad, int d, int V, int Vpad,
                                                                  int accumulate) {
-    __shared__ __attribute__((aligned(16))) char smem[8 * TBYTES];
+    __shared__ __attribute__((aligned(16))) char s0[STAGE];
+    __shared__ __attribute__((aligned(16))) char s1[STAGE];
+    __shared__ __attribute__((aligned(16))) char s2[STAGE];
     // the feature tiles of one class tile consecutively (they share its columns of P)
-    const uint32_t nft = (uint32_t)d / CT;
+    const uint32_t nft = (uint32_t)(d + MT - 1) / MT;
     const uint32_t L = xcd_tile(blockIdx.x, gridDim.x);
-    const uint32_t f0 = (L % nft) * CT, v0 = (L / nft) * CT;
-    const Operand A{GRes(h + (size_t)c0 * d, (uint32_t)Nc * d * 2), (uint32_t)d, true};
-    const Operand B{GRes(P, (uint32_t)Ncpad * Vpad * 2), (uint32_t)Vpad, true};
+    const uint32_t f0 = (L % nft) * MT, v0 = (L / nft) * NT;
+    const Operand A{rsrc4(h + (size_t)c0 * d, (uint32_t)Nc * d * 2), (uint32_t)d, true};
+    const Operand B{rsrc4(P, (uint32_t)Ncpad * Vpad * 2), (uint32_t)Vpad, true};
     floatx4 acc[4][4];
-    gemm_tile<true, true>(smem, A, B, f0, v0, 0, (uint32_t)Ncpad, acc);
+    gemm_tile<true, true>(s0, s1, s2, A, B, f0, v0, 0, (uint32_t)Ncpad, acc);
 
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 1, wn = w >> 1;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 3, wn = w >> 2;
+    if ((int)f0 + 64 * wm >= d) return;  // d is a multiple of 128: a wave's features lie all inside or all past
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int vv = (int)v0 + 64 * wn + 16 * j + r;
@@ -309,25 +360,28 @@ __global__ __launch_bounds__(CE_THREADS, 2) void la_ce_dw_kernel(const bf16 *__r
 }
 
 // dh partial tiles: C[m = feature][n = token] = sum_v W[v][m] P[t][v] over classes [k0, k1) of split
-// blockIdx.z; A = W k-major, B = P k-contiguous.  Stored to part[z][t][m] (fp32).
-__global__ __launch_bounds__(CE_THREADS, 2) void la_ce_dh_kernel(const bf16 *__restrict__ W,
+// z; A = W k-major, B = P k-contiguous.  Stored to part[z][t][m] (fp32), features past d excepted.
+__global__ __launch_bounds__(CE_THREADS, 1) void la_ce_dh_kernel(const bf16 *__restrict__ W,
                                                                  const bf16 *__restrict__ P, float *__restrict__ part,
                                                                  int Ncpad, int d, int V, int Vpad, int kper) {
-    __shared__ __attribute__((aligned(16))) char smem[8 * TBYTES];
+    __shared__ __attribute__((aligned(16))) char s0[STAGE];
+    __shared__ __attribute__((aligned(16))) char s1[STAGE];
+    __shared__ __attribute__((aligned(16))) char s2[STAGE];
     // split slowest, then token tile, feature tile fastest: consecutive tiles share P's rows of the
     // split, and the tiles of one split share its rows of W
-    const uint32_t nft = (uint32_t)d / CT, ntt = (uint32_t)Ncpad / CT;
+    const uint32_t nft = (uint32_t)(d + MT - 1) / MT, ntt = (uint32_t)Ncpad / NT;
     const uint32_t L = xcd_tile(blockIdx.x, gridDim.x), z = L / (nft * ntt), rest = L % (nft * ntt);
-    const uint32_t f0 = (rest % nft) * CT, t0 = (rest / nft) * CT;
+    const uint32_t f0 = (rest % nft) * MT, t0 = (rest / nft) * NT;
     const uint32_t k0 = z * (uint32_t)kper;
     const uint32_t k1 = k0 + (uint32_t)kper < (uint32_t)Vpad ? k0 + (uint32_t)kper : (uint32_t)Vpad;
-    const Operand A{GRes(W, (uint32_t)V * d * 2), (uint32_t)d, true};
-    const Operand B{GRes(P, (uint32_t)Ncpad * Vpad * 2), (uint32_t)Vpad, false};
+    const Operand A{rsrc4(W, (uint32_t)V * d * 2), (uint32_t)d, true};
+    const Operand B{rsrc4(P, (uint32_t)Ncpad * Vpad * 2), (uint32_t)Vpad, false};
     floatx4 acc[4][4];
-    gemm_tile<true, false>(smem, A, B, f0, t0, k0, k1, acc);
+    gemm_tile<true, false>(s0, s1, s2, A, B, f0, t0, k0, k1, acc);
 
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 1, wn = w >> 1;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 3, wn = w >> 2;
+    if ((int)f0 + 64 * wm >= d) return;
     float *base = part + (size_t)z * Ncpad * d;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -353,14 +407,15 @@ __global__ __launch_bounds__(256) void la_ce_dh_reduce_kernel(const float *__res
 
 CeShape ce_shape(int N, int d, int V, int ce_chunk) {
     CeShape s;
-    s.Npad = (N + CT - 1) / CT * CT;
-    s.Vpad = (V + CT - 1) / CT * CT;
-    s.nvt = s.Vpad / CT;
+    s.Npad = (N + NT - 1) / NT * NT;
+    s.Vpad = (V + MT - 1) / MT * MT;  // whole class tiles of the forward and of P
+    s.nvt = s.Vpad / MT;
     s.chunk = ce_chunk < 1 || ce_chunk > N ? N : ce_chunk;
-    s.chunk_pad = (s.chunk + CT - 1) / CT * CT;
-    // dh split over the vocabulary: enough workgroups to fill the chip, whole k-steps per split
-    const int tiles = (d / CT) * (s.chunk_pad / CT);
-    int nsplit = (512 + tiles - 1) / tiles;
+    s.chunk_pad = (s.chunk + NT - 1) / NT * NT;
+    // dh split over the vocabulary: at most one workgroup per compute unit (256), whole k-steps
+    // per split
+    const int tiles = (d + MT - 1) / MT * (s.chunk_pad / NT);
+    int nsplit = tiles >= 256 ? 1 : 256 / tiles;
     if (nsplit > s.Vpad / CK) nsplit = s.Vpad / CK;
     s.kper = ((s.Vpad + nsplit - 1) / nsplit + CK - 1) / CK * CK;
     s.nsplit = (s.Vpad + s.kper - 1) / s.kper;
@@ -377,7 +432,7 @@ hipError_t launch_ce_fwd(const void *h, const void *W, const int *targets, float
     floatx2 *part = reinterpret_cast<floatx2 *>(ws);
     float *tl = reinterpret_cast<float *>(static_cast<char *>(ws) + (size_t)s.nvt * s.Npad * 8);
     float *nll = tl + s.Npad;
-    hipExtLaunchKernelGGL(la_ce_fwd_kernel, dim3(s.nvt * (s.Npad / CT)), dim3(CE_THREADS), 0, stream, ev[0], nullptr,
+    hipExtLaunchKernelGGL(la_ce_fwd_kernel, dim3(s.nvt * (s.Npad / NT)), dim3(CE_THREADS), 0, stream, ev[0], nullptr,
                           0, (const bf16 *)h, (const bf16 *)W, targets, part, tl, N, d, V, s.Npad);
     hipExtLaunchKernelGGL(la_ce_lse_kernel, dim3((N + 15) / 16), dim3(256), 0, stream, nullptr, nullptr, 0,
                           (const floatx2 *)part, (const float *)tl, lse, nll, N, s.Npad, s.nvt);
@@ -394,18 +449,19 @@ hipError_t launch_ce_bwd(const void *h, const void *W, const int *targets, const
     float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + s.p_bytes);
     for (int c0 = 0; c0 < N; c0 += s.chunk) {
         const int Nc = N - c0 < s.chunk ? N - c0 : s.chunk;
-        const int Ncpad = (Nc + CT - 1) / CT * CT;
+        const int Ncpad = (Nc + NT - 1) / NT * NT;
+        const int nft = (d + MT - 1) / MT;
         const bool first = c0 == 0, last = c0 + s.chunk >= N;
-        hipExtLaunchKernelGGL(la_ce_p_kernel, dim3(s.nvt * (Ncpad / CT)), dim3(CE_THREADS), 0, stream,
+        hipExtLaunchKernelGGL(la_ce_p_kernel, dim3(s.nvt * (Ncpad / NT)), dim3(CE_THREADS), 0, stream,
                               first ? ev[0] : nullptr, nullptr, 0, (const bf16 *)h, (const bf16 *)W, targets, lse,
                               dloss, P, c0, Nc, N, d, V, s.Vpad);
-        hipExtLaunchKernelGGL(la_ce_dh_kernel, dim3((d / CT) * (Ncpad / CT) * s.nsplit), dim3(CE_THREADS), 0, stream,
+        hipExtLaunchKernelGGL(la_ce_dh_kernel, dim3(nft * (Ncpad / NT) * s.nsplit), dim3(CE_THREADS), 0, stream,
                               nullptr, nullptr, 0, (const bf16 *)W, (const bf16 *)P, part, Ncpad, d, V, s.Vpad,
                               s.kper);
         const size_t n4 = (size_t)Nc * d / 4;
         hipExtLaunchKernelGGL(la_ce_dh_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
                               nullptr, nullptr, 0, (const float *)part, (bf16 *)dh, c0, Nc, Ncpad, d, s.nsplit);
-        hipExtLaunchKernelGGL(la_ce_dw_kernel, dim3((d / CT) * s.nvt), dim3(CE_THREADS), 0, stream, nullptr,
+        hipExtLaunchKernelGGL(la_ce_dw_kernel, dim3(nft * (s.Vpad / NT)), dim3(CE_THREADS), 0, stream, nullptr,
                               last ? ev[1] : nullptr, 0, (const bf16 *)h, (const bf16 *)P, dW, c0, Nc, Ncpad, d, V,
                               s.Vpad, first ? 0 : 1);
     }
