@@ -308,7 +308,7 @@ def bench_ce(args, w, torch, lac, inp):
     gemm = 2.0 * N * V * d
     entry = {}
     for j, (name, flops, kern) in enumerate((
-            ("la_ce_fwd", gemm, "la_ce_fwd_kernel + la_ce_combine_kernel"),
+            ("la_ce_fwd", gemm, "la_ce_fwd_kernel + la_ce_lse_kernel + la_ce_mean_kernel"),
             ("la_ce_bwd", 3 * gemm, "la_ce_p_kernel + la_ce_dh_kernel + la_ce_dh_reduce_kernel + la_ce_dw_kernel"))):
         us = sum(e[j][0].elapsed_time(e[j][1]) for e in ev) * 1e3 / K
         tf = flops / (us * 1e-6) / 1e12
