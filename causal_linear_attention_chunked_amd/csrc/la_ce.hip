@@ -70,49 +70,101 @@ __device__ __forceinline__ void wait_vm_lgkm() {
     __builtin_amdgcn_s_waitcnt(0x0070 | n);
 }
 
-// The 256 x 128 fp32 tile C[m][n] = sum_k A[m][k] B[n][k] over k in [k0, k1) (multiples of 64),
-// m from row m0 of A, n from row n0 of B.  Wave w holds rows 64 (w & 3).. of m and 64 (w >> 2)..
-// of n: acc[i][j] is the 16 x 16 tile (m-tile i, n-tile j), lane (r, g) holding
-// C[m = 16 i + 4 g + e][n = 16 j + r].  s0, s1, s2: the three stages, separate LDS arrays (so
-// that the compiler can tell the stage being loaded from the one being read).
+// An output tile: rows m0.. of A, n0.. of B, k-steps k0 .. k0 + 64 nk.
+struct TileRange {
+    uint32_t m0, n0, k0;
+    int nk;
+};
+
+// The workgroup's logical tiles.  Workgroups are dealt to the eight XCDs in turn (workgroup b to
+// XCD b % 8, the grid a multiple of 8), each XCD with its own L2.  The T tiles are cut into eight
+// contiguous ranges, one per XCD, and the XCD's workgroups take its tiles in turn: the tiles in
+// flight on one XCD at a time are consecutive, and consecutive tiles share an operand, which is
+// then fetched into one L2 instead of several.
+struct TileWalk {
+    uint32_t first, stride, count;
+    __device__ __forceinline__ explicit TileWalk(uint32_t T) {
+        const uint32_t b = blockIdx.x, x = b % 8, k = b / 8, gx = gridDim.x / 8;
+        const uint32_t per = T / 8, rem = T % 8;
+        const uint32_t start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+        const uint32_t cnt = per + (x < rem ? 1u : 0u);
+        first = start + k;
+        stride = gx;
+        count = cnt > k ? (cnt - k + gx - 1) / gx : 0u;
+    }
+    __device__ __forceinline__ uint32_t operator[](uint32_t j) const { return first + j * stride; }
+};
+
+// Persistent GEMM over the workgroup's tiles: for each 256 x 128 tile, C[m][n] = sum_k A[m][k]
+// B[n][k], handed to epi(L, acc) when its last k-step is done.  Wave w holds rows 64 (w & 3).. of m
+// and 64 (w >> 2).. of n: acc[i][j] is the 16 x 16 tile (m-tile i, n-tile j), lane (r, g) holding
+// C[m = 16 i + 4 g + e][n = 16 j + r].  s0, s1, s2: the three stages, separate LDS arrays.
 //
-// Pipeline: stage k-step ks is loaded into s[ks % 3] two steps ahead.  Each step waits for its
-// own wave's loads of the step (vmcnt: the loads issued after them may stay in flight) and for
-// its LDS reads, then a barrier: every wave's loads of the step have landed and every wave is
+// Pipeline: the k-steps of all the workgroup's tiles form one stream; step g is loaded into
+// s[g % 3] two steps ahead, so the next tile's first loads are in flight during the current
+// tile's last products and its epilogue.  Each step waits for the wave's own loads of the step
+// (vmcnt(6): the six of the next step, always issued after them, may stay in flight; after an
+// epilogue its stores and loads are newer still, so the wait then also covers some of them) and
+// for its LDS reads, then a barrier: every wave's loads of the step have landed and every wave is
 // done reading the stage the step after next is loaded into, which is issued next; then the
-// products.  The loads of the k-steps past the end are issued too, at an offset past every
-// buffer range (no memory is read), so that every step has the same loads in flight.
-template <bool AKM, bool BKM>
-__device__ __forceinline__ void gemm_tile(char *s0, char *s1, char *s2, const Operand &A, const Operand &B,
-                                          uint32_t m0, uint32_t n0, uint32_t k0, uint32_t k1, floatx4 (&acc)[4][4]) {
+// products.  The loads past the end of the stream are issued at an offset past every buffer range
+// (no memory is read), so that every step has the same loads in flight.
+template <bool AKM, bool BKM, class TileF, class EpiF>
+__device__ __forceinline__ void gemm_tiles(char *s0, char *s1, char *s2, const Operand &A, const Operand &B,
+                                           const TileWalk &walk, TileF tile_at, EpiF epi) {
+    if (walk.count == 0) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 3, wn = w >> 2;
     const TileLanes TL(lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+    int S = 0;  // k-steps of all the workgroup's tiles
+    for (uint32_t j = 0; j < walk.count; ++j) S += tile_at(walk[j]).nk;
+
     // Load instruction i of wave w writes rows 8w..8w+7 of tile i (A tiles 0-3, then B tiles 0-1);
     // lane l lands in storage row y = 8w + l / 8, 16-byte slot l % 8, which holds the row's logical
-    // 16-byte unit (l % 8) ^ (swz(y) / 2).  Element offsets of the lane's units at k = 0:
+    // 16-byte unit (l % 8) ^ (swz(y) / 2).  Element offsets of the lane's units at k = 0 of the
+    // tile the load cursor is in:
     const int y = 8 * w + (lane >> 3);
     const int uu = (lane & 7) ^ ((y ^ (y >> 1)) & 7);
+    uint32_t ij = 0;  // load cursor: tile ij (itr), k-step is
+    int is = 0;
+    TileRange itr = tile_at(walk[0]);
     uint32_t offa[4], offb[2];
+    auto set_offsets = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        offa[i] = AKM ? (uint32_t)y * A.ld + m0 + 64 * i + 8 * uu : (m0 + 64 * i + (uint32_t)y) * A.ld + 8 * uu;
+        for (int i = 0; i < 4; ++i)
+            offa[i] = AKM ? (uint32_t)y * A.ld + itr.m0 + 64 * i + 8 * uu
+                          : (itr.m0 + 64 * i + (uint32_t)y) * A.ld + 8 * uu;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-        offb[i] = BKM ? (uint32_t)y * B.ld + n0 + 64 * i + 8 * uu : (n0 + 64 * i + (uint32_t)y) * B.ld + 8 * uu;
+        for (int i = 0; i < 2; ++i)
+            offb[i] = BKM ? (uint32_t)y * B.ld + itr.n0 + 64 * i + 8 * uu
+                          : (itr.n0 + 64 * i + (uint32_t)y) * B.ld + 8 * uu;
+    };
+    set_offsets();
     constexpr uint32_t PAST = 0x80000000u;  // byte offset past every operand's range (< 2^31 bytes)
-    auto issue = [&](char *st, uint32_t kk, bool live) {
+    auto issue_next = [&](char *st, bool live) {
+        const uint32_t kk = itr.k0 + (uint32_t)is * CK;
         const uint32_t ka = AKM ? kk * A.ld : kk, kb = BKM ? kk * B.ld : kk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) lds_load16(A.rs, st + i * TBYTES + 1024 * w, live ? (offa[i] + ka) * 2 : PAST);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             lds_load16(B.rs, st + (4 + i) * TBYTES + 1024 * w, live ? (offb[i] + kb) * 2 : PAST);
+        if (live && ++is == itr.nk) {
+            is = 0;
+            if (++ij < walk.count) {
+                itr = tile_at(walk[ij]);
+                set_offsets();
+            }
+        }
     };
+
+    floatx4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+    uint32_t cj = 0;  // product cursor: tile cj, k-step cs of its cnk
+    int cs = 0, cnk = itr.nk;
     auto compute = [&](const char *st) {
         const char *At = st + wm * TBYTES, *Bt = st + (4 + wn) * TBYTES;
 #pragma unroll
@@ -129,26 +181,34 @@ __device__ __forceinline__ void gemm_tile(char *s0, char *s1, char *s2, const Op
                 for (int j = 0; j < 4; ++j) mma(acc[i][j], af[i], bfr[j]);
         }
     };
-    const int nk = (int)((k1 - k0) / CK);
-    auto step = [&](char *cur, char *nxt, int ks) {
+    auto step = [&](char *cur, char *nxt, int g) {
         wait_vm_lgkm<6>();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue(nxt, k0 + (uint32_t)(ks + 2) * CK, ks + 2 < nk);
+        issue_next(nxt, g + 2 < S);
         compute(cur);
+        if (++cs == cnk) {
+            epi(walk[cj], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+            cs = 0;
+            if (++cj < walk.count) cnk = tile_at(walk[cj]).nk;
+        }
     };
-    issue(s0, k0, true);
-    issue(s1, k0 + CK, nk > 1);
-    for (int ks = 0;;) {
-        step(s0, s2, ks);
-        if (++ks == nk) break;
-        step(s1, s0, ks);
-        if (++ks == nk) break;
-        step(s2, s1, ks);
-        if (++ks == nk) break;
+    issue_next(s0, true);
+    issue_next(s1, S > 1);
+    for (int g = 0;;) {
+        step(s0, s2, g);
+        if (++g == S) break;
+        step(s1, s0, g);
+        if (++g == S) break;
+        step(s2, s1, g);
+        if (++g == S) break;
     }
-    wait_vm_lgkm<0>();  // the two loads past the end; the stages may be reused after a barrier
+    wait_vm_lgkm<0>();  // the loads past the end
 }
 
 // max over the four lane groups (lanes l, l^16, l^32, l^48)
@@ -159,84 +219,76 @@ __device__ __forceinline__ float gmax(float x) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Workgroups are dealt to the eight XCDs in turn (workgroup b to XCD b % 8), each XCD with its own
-// L2.  The tile order is remapped so that each XCD takes one contiguous range of logical tiles:
-// tiles that share an operand are numbered consecutively, so they run on one XCD and that
-// operand is fetched into one L2 instead of several.
-__device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t total) {
-    const uint32_t per = total / 8, rem = total % 8, x = b % 8, k = b / 8;
-    return x < rem ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
-}
-
 constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
 }  // namespace
 
-// Forward tiles: one workgroup per (class tile, token tile).  The A operand is W (rows = classes), B is
-// h (rows = tokens), both k-contiguous.  part[vt][t] = (max, sum exp(logit - max)) over the tile's
-// classes, tl[t] = logit of token t's target (written by the one lane that holds it).
+// Forward tiles (class tile vt, token tile): A = W (rows = classes), B = h (rows = tokens), both
+// k-contiguous.  part[vt][t] = (max, sum exp(logit - max)) over the tile's classes (the four waves
+// of a token half combined through LDS), tl[t] = logit of token t's target (written by the one
+// lane that holds it).
 __global__ __launch_bounds__(CE_THREADS, 1) void la_ce_fwd_kernel(
     const bf16 *__restrict__ h, const bf16 *__restrict__ W, const int *__restrict__ targets,
     floatx2 *__restrict__ part, float *__restrict__ tl, int N, int d, int V, int Npad) {
     __shared__ __attribute__((aligned(16))) char s0[STAGE];
     __shared__ __attribute__((aligned(16))) char s1[STAGE];
     __shared__ __attribute__((aligned(16))) char s2[STAGE];
+    __shared__ floatx2 xch[4 * NT];  // [4 wm][128 tokens]
     // logical tile: the token tiles of one class tile consecutively (they share its rows of W)
-    const uint32_t ntt = (uint32_t)Npad / NT;
-    const uint32_t L = xcd_tile(blockIdx.x, gridDim.x), vt = L / ntt;
-    const uint32_t v0 = vt * MT, t0 = (L % ntt) * NT;
+    const uint32_t ntt = (uint32_t)Npad / NT, nvt = (uint32_t)(V + MT - 1) / MT;
     const Operand A{rsrc4(W, (uint32_t)V * d * 2), (uint32_t)d, false};
     const Operand B{rsrc4(h, (uint32_t)N * d * 2), (uint32_t)d, false};
-    floatx4 acc[4][4];
-    gemm_tile<false, false>(s0, s1, s2, A, B, v0, t0, 0, (uint32_t)d, acc);
-    lds_barrier();  // every wave done with the stages: s0 takes the exchange below
-
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 3, wn = w >> 2;
-    floatx2 *const xch = reinterpret_cast<floatx2 *>(s0);  // [4 wm][128 tokens]
     const GRes tres(targets, (uint32_t)N * 4);
+    auto tile_at = [&](uint32_t L) { return TileRange{(L / ntt) * MT, (L % ntt) * NT, 0u, d / CK}; };
+    auto epi = [&](uint32_t L, floatx4 (&acc)[4][4]) {
+        const uint32_t vt = L / ntt, v0 = vt * MT, t0 = (L % ntt) * NT;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int tloc = 64 * wn + 16 * j + r;
-        const int t = (int)t0 + tloc;
-        const int tgt = gload<int>(tres, (uint32_t)t * 4);
-        float mx = -INFINITY;
+        for (int j = 0; j < 4; ++j) {
+            const int tloc = 64 * wn + 16 * j + r;
+            const int t = (int)t0 + tloc;
+            const int tgt = gload<int>(tres, (uint32_t)t * 4);
+            float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int vv = (int)v0 + 64 * wm + 16 * i + 4 * g + e;
-                if (vv < V) mx = fmaxf(mx, acc[i][j][e]);
-                if (vv == tgt && t < N) tl[t] = acc[i][j][e];
-            }
-        mx = gmax(mx);
-        float s = 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    const int vv = (int)v0 + 64 * wm + 16 * i + 4 * g + e;
+                    if (vv < V) mx = fmaxf(mx, acc[i][j][e]);
+                    if (vv == tgt && t < N) tl[t] = acc[i][j][e];
+                }
+            mx = gmax(mx);
+            float sum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int vv = (int)v0 + 64 * wm + 16 * i + 4 * g + e;
-                s += vv < V ? exp_f(acc[i][j][e] - mx) : 0.f;
-            }
-        s = gsum(s);
-        if (g == 0) xch[wm * NT + tloc] = floatx2{mx, s};
-    }
-    lds_barrier();
-    if (tid < NT) {
-        // a wave's classes may all lie past V (then max -inf, sum 0); the first wave's never do, as
-        // the grid holds no tile with V <= v0
-        floatx2 x[4];
-        float m = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            x[k] = xch[k * NT + tid];
-            m = fmaxf(m, x[k][0]);
+                for (int e = 0; e < 4; ++e) {
+                    const int vv = (int)v0 + 64 * wm + 16 * i + 4 * g + e;
+                    sum += vv < V ? exp_f(acc[i][j][e] - mx) : 0.f;
+                }
+            sum = gsum(sum);
+            if (g == 0) xch[wm * NT + tloc] = floatx2{mx, sum};
         }
-        float s = 0.f;
+        lds_barrier();
+        if (tid < NT) {
+            // a wave's classes may all lie past V (then max -inf, sum 0); the first wave's never do,
+            // as no tile has V <= v0
+            floatx2 x[4];
+            float m = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) s += x[k][1] * exp_f(x[k][0] - m);
-        part[(size_t)vt * Npad + t0 + tid] = floatx2{m, s};
-    }
+            for (int k = 0; k < 4; ++k) {
+                x[k] = xch[k * NT + tid];
+                m = fmaxf(m, x[k][0]);
+            }
+            float sm = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) sm += x[k][1] * exp_f(x[k][0] - m);
+            part[(size_t)vt * Npad + t0 + tid] = floatx2{m, sm};
+        }
+        lds_barrier();  // xch is rewritten by the next tile's epilogue
+    };
+    gemm_tiles<false, false>(s0, s1, s2, A, B, TileWalk(nvt * ntt), tile_at, epi);
 }
 
 // lse_t = max + log(sum over the class tiles' partials), nll_t = lse_t - tl_t: 16 tokens per
@@ -292,37 +344,37 @@ __global__ __launch_bounds__(CE_THREADS, 1) void la_ce_p_kernel(
     __shared__ __attribute__((aligned(16))) char s0[STAGE];
     __shared__ __attribute__((aligned(16))) char s1[STAGE];
     __shared__ __attribute__((aligned(16))) char s2[STAGE];
-    const uint32_t ntt = (uint32_t)(Nc + NT - 1) / NT;
-    const uint32_t L = xcd_tile(blockIdx.x, gridDim.x);
-    const uint32_t v0 = (L / ntt) * MT, t0 = (L % ntt) * NT;
+    const uint32_t ntt = (uint32_t)(Nc + NT - 1) / NT, nvt = (uint32_t)Vpad / MT;
     const Operand A{rsrc4(W, (uint32_t)V * d * 2), (uint32_t)d, false};
     const Operand B{rsrc4(h + (size_t)c0 * d, (uint32_t)Nc * d * 2), (uint32_t)d, false};
-    floatx4 acc[4][4];
-    gemm_tile<false, false>(s0, s1, s2, A, B, v0, t0, 0, (uint32_t)d, acc);
-
-    const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 3, wn = w >> 2;
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), wm = w & 3, wn = w >> 2;
     const float scale = (dloss ? *dloss : 1.f) / (float)N;
     const GRes tres(targets + c0, (uint32_t)Nc * 4), lres(lse + c0, (uint32_t)Nc * 4);
+    auto tile_at = [&](uint32_t L) { return TileRange{(L / ntt) * MT, (L % ntt) * NT, 0u, d / CK}; };
+    auto epi = [&](uint32_t L, floatx4 (&acc)[4][4]) {
+        const uint32_t v0 = (L / ntt) * MT, t0 = (L % ntt) * NT;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int tloc = (int)t0 + 64 * wn + 16 * j + r;  // token within the chunk
-        const int tgt = gload<int>(tres, (uint32_t)tloc * 4);
-        const float l = gload<float>(lres, (uint32_t)tloc * 4);
-        const bool live = tloc < Nc;
+        for (int j = 0; j < 4; ++j) {
+            const int tloc = (int)t0 + 64 * wn + 16 * j + r;  // token within the chunk
+            const int tgt = gload<int>(tres, (uint32_t)tloc * 4);
+            const float l = gload<float>(lres, (uint32_t)tloc * 4);
+            const bool live = tloc < Nc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int vb = (int)v0 + 64 * wm + 16 * i + 4 * g;
-            floatx4 p;
+            for (int i = 0; i < 4; ++i) {
+                const int vb = (int)v0 + 64 * wm + 16 * i + 4 * g;
+                floatx4 p;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int vv = vb + e;
-                const float x = exp_f(acc[i][j][e] - l) - (vv == tgt ? 1.f : 0.f);
-                p[e] = (live && vv < V) ? x * scale : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    const int vv = vb + e;
+                    const float x = exp_f(acc[i][j][e] - l) - (vv == tgt ? 1.f : 0.f);
+                    p[e] = (live && vv < V) ? x * scale : 0.f;
+                }
+                *reinterpret_cast<bf16x4 *>(P + (size_t)tloc * Vpad + vb) = pack4(p);
             }
-            *reinterpret_cast<bf16x4 *>(P + (size_t)tloc * Vpad + vb) = pack4(p);
         }
-    }
+    };
+    gemm_tiles<false, false>(s0, s1, s2, A, B, TileWalk(nvt * ntt), tile_at, epi);
 }
 
 // dW tiles: C[m = feature][n = class] = sum_t h[t][m] P[t][n] over the chunk's (padded) tokens;
@@ -336,60 +388,67 @@ __global__ __launch_bounds__(CE_THREADS, 1) void la_ce_dw_kernel(const bf16 *__r
     __shared__ __attribute__((aligned(16))) char s1[STAGE];
     __shared__ __attribute__((aligned(16))) char s2[STAGE];
     // the feature tiles of one class tile consecutively (they share its columns of P)
-    const uint32_t nft = (uint32_t)(d + MT - 1) / MT;
-    const uint32_t L = xcd_tile(blockIdx.x, gridDim.x);
-    const uint32_t f0 = (L % nft) * MT, v0 = (L / nft) * NT;
+    const uint32_t nft = (uint32_t)(d + MT - 1) / MT, nct = (uint32_t)Vpad / NT;
     const Operand A{rsrc4(h + (size_t)c0 * d, (uint32_t)Nc * d * 2), (uint32_t)d, true};
     const Operand B{rsrc4(P, (uint32_t)Ncpad * Vpad * 2), (uint32_t)Vpad, true};
-    floatx4 acc[4][4];
-    gemm_tile<true, true>(s0, s1, s2, A, B, f0, v0, 0, (uint32_t)Ncpad, acc);
-
-    const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 3, wn = w >> 2;
-    if ((int)f0 + 64 * wm >= d) return;  // d is a multiple of 128: a wave's features lie all inside or all past
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), wm = w & 3, wn = w >> 2;
+    auto tile_at = [&](uint32_t L) { return TileRange{(L % nft) * MT, (L / nft) * NT, 0u, Ncpad / CK}; };
+    auto epi = [&](uint32_t L, floatx4 (&acc)[4][4]) {
+        const uint32_t f0 = (L % nft) * MT, v0 = (L / nft) * NT;
+        // d is a multiple of 128: a wave's 64 features lie all inside or all past it
+        if ((int)f0 + 64 * wm >= d) return;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int vv = (int)v0 + 64 * wn + 16 * j + r;
-        if (vv >= V) continue;
+        for (int j = 0; j < 4; ++j) {
+            const int vv = (int)v0 + 64 * wn + 16 * j + r;
+            if (vv >= V) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            floatx4 *dst = reinterpret_cast<floatx4 *>(dW + (size_t)vv * d + f0 + 64 * wm + 16 * i + 4 * g);
-            *dst = accumulate ? *dst + acc[i][j] : acc[i][j];
+            for (int i = 0; i < 4; ++i) {
+                floatx4 *dst = reinterpret_cast<floatx4 *>(dW + (size_t)vv * d + f0 + 64 * wm + 16 * i + 4 * g);
+                *dst = accumulate ? *dst + acc[i][j] : acc[i][j];
+            }
         }
-    }
+    };
+    gemm_tiles<true, true>(s0, s1, s2, A, B, TileWalk(nft * nct), tile_at, epi);
 }
 
-// dh partial tiles: C[m = feature][n = token] = sum_v W[v][m] P[t][v] over classes [k0, k1) of split
-// z; A = W k-major, B = P k-contiguous.  Stored to part[z][t][m] (fp32), features past d excepted.
+// dh partial tiles: C[m = feature][n = token] = sum_v W[v][m] P[t][v] over the classes [k0, k1) of
+// split z; A = W k-major, B = P k-contiguous.  Stored to part[z][t][m] (fp32), features past d
+// excepted.
 __global__ __launch_bounds__(CE_THREADS, 1) void la_ce_dh_kernel(const bf16 *__restrict__ W,
                                                                  const bf16 *__restrict__ P, float *__restrict__ part,
-                                                                 int Ncpad, int d, int V, int Vpad, int kper) {
+                                                                 int Ncpad, int d, int V, int Vpad, int kper,
+                                                                 int nsplit) {
     __shared__ __attribute__((aligned(16))) char s0[STAGE];
     __shared__ __attribute__((aligned(16))) char s1[STAGE];
     __shared__ __attribute__((aligned(16))) char s2[STAGE];
     // split slowest, then token tile, feature tile fastest: consecutive tiles share P's rows of the
     // split, and the tiles of one split share its rows of W
     const uint32_t nft = (uint32_t)(d + MT - 1) / MT, ntt = (uint32_t)Ncpad / NT;
-    const uint32_t L = xcd_tile(blockIdx.x, gridDim.x), z = L / (nft * ntt), rest = L % (nft * ntt);
-    const uint32_t f0 = (rest % nft) * MT, t0 = (rest / nft) * NT;
-    const uint32_t k0 = z * (uint32_t)kper;
-    const uint32_t k1 = k0 + (uint32_t)kper < (uint32_t)Vpad ? k0 + (uint32_t)kper : (uint32_t)Vpad;
     const Operand A{rsrc4(W, (uint32_t)V * d * 2), (uint32_t)d, true};
     const Operand B{rsrc4(P, (uint32_t)Ncpad * Vpad * 2), (uint32_t)Vpad, false};
-    floatx4 acc[4][4];
-    gemm_tile<true, false>(s0, s1, s2, A, B, f0, t0, k0, k1, acc);
-
-    const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 3, wn = w >> 2;
-    if ((int)f0 + 64 * wm >= d) return;
-    float *base = part + (size_t)z * Ncpad * d;
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), wm = w & 3, wn = w >> 2;
+    auto tile_at = [&](uint32_t L) {
+        const uint32_t z = L / (nft * ntt), rest = L % (nft * ntt);
+        const uint32_t k0 = z * (uint32_t)kper;
+        const uint32_t k1 = k0 + (uint32_t)kper < (uint32_t)Vpad ? k0 + (uint32_t)kper : (uint32_t)Vpad;
+        return TileRange{(rest % nft) * MT, (rest / nft) * NT, k0, (int)((k1 - k0) / CK)};
+    };
+    auto epi = [&](uint32_t L, floatx4 (&acc)[4][4]) {
+        const uint32_t z = L / (nft * ntt), rest = L % (nft * ntt);
+        const uint32_t f0 = (rest % nft) * MT, t0 = (rest / nft) * NT;
+        if ((int)f0 + 64 * wm >= d) return;
+        float *base = part + (size_t)z * Ncpad * d;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int t = (int)t0 + 64 * wn + 16 * j + r;
+        for (int j = 0; j < 4; ++j) {
+            const int t = (int)t0 + 64 * wn + 16 * j + r;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<floatx4 *>(base + (size_t)t * d + f0 + 64 * wm + 16 * i + 4 * g) = acc[i][j];
-    }
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<floatx4 *>(base + (size_t)t * d + f0 + 64 * wm + 16 * i + 4 * g) = acc[i][j];
+        }
+    };
+    gemm_tiles<true, false>(s0, s1, s2, A, B, TileWalk(nft * ntt * (uint32_t)nsplit), tile_at, epi);
 }
 
 // dh[c0 + t][m] = sum over the splits, in order, rounded to bf16 (four features per thread).
@@ -426,14 +485,31 @@ CeShape ce_shape(int N, int d, int V, int ce_chunk) {
     return s;
 }
 
+// Workgroups of a persistent launch over T tiles: one per compute unit at most (the GEMM kernels'
+// LDS allows one), a multiple of 8 so that workgroup b runs on XCD b % 8 for every b; fewer when
+// there are fewer tiles.
+static unsigned persistent_grid(uint32_t T) {
+    static int ncu[16];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+    if (ncu[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 8;
+        ncu[dev] = n;
+    }
+    const unsigned g = (unsigned)ncu[dev] / 8 * 8, t8 = (T + 7) / 8 * 8;
+    return t8 < g ? t8 : g;
+}
+
 hipError_t launch_ce_fwd(const void *h, const void *W, const int *targets, float *loss, float *lse, void *ws, int N,
                          int d, int V, hipStream_t stream, const hipEvent_t ev[2]) {
     const CeShape s = ce_shape(N, d, V, N);
     floatx2 *part = reinterpret_cast<floatx2 *>(ws);
     float *tl = reinterpret_cast<float *>(static_cast<char *>(ws) + (size_t)s.nvt * s.Npad * 8);
     float *nll = tl + s.Npad;
-    hipExtLaunchKernelGGL(la_ce_fwd_kernel, dim3(s.nvt * (s.Npad / NT)), dim3(CE_THREADS), 0, stream, ev[0], nullptr,
-                          0, (const bf16 *)h, (const bf16 *)W, targets, part, tl, N, d, V, s.Npad);
+    hipExtLaunchKernelGGL(la_ce_fwd_kernel, dim3(persistent_grid(s.nvt * (s.Npad / NT))), dim3(CE_THREADS), 0,
+                          stream, ev[0], nullptr, 0, (const bf16 *)h, (const bf16 *)W, targets, part, tl, N, d, V,
+                          s.Npad);
     hipExtLaunchKernelGGL(la_ce_lse_kernel, dim3((N + 15) / 16), dim3(256), 0, stream, nullptr, nullptr, 0,
                           (const floatx2 *)part, (const float *)tl, lse, nll, N, s.Npad, s.nvt);
     hipExtLaunchKernelGGL(la_ce_mean_kernel, dim3(1), dim3(1024), 0, stream, nullptr, ev[1], 0, (const float *)nll,
@@ -452,16 +528,16 @@ hipError_t launch_ce_bwd(const void *h, const void *W, const int *targets, const
         const int Ncpad = (Nc + NT - 1) / NT * NT;
         const int nft = (d + MT - 1) / MT;
         const bool first = c0 == 0, last = c0 + s.chunk >= N;
-        hipExtLaunchKernelGGL(la_ce_p_kernel, dim3(s.nvt * (Ncpad / NT)), dim3(CE_THREADS), 0, stream,
+        hipExtLaunchKernelGGL(la_ce_p_kernel, dim3(persistent_grid(s.nvt * (Ncpad / NT))), dim3(CE_THREADS), 0, stream,
                               first ? ev[0] : nullptr, nullptr, 0, (const bf16 *)h, (const bf16 *)W, targets, lse,
                               dloss, P, c0, Nc, N, d, V, s.Vpad);
-        hipExtLaunchKernelGGL(la_ce_dh_kernel, dim3(nft * (Ncpad / NT) * s.nsplit), dim3(CE_THREADS), 0, stream,
-                              nullptr, nullptr, 0, (const bf16 *)W, (const bf16 *)P, part, Ncpad, d, V, s.Vpad,
-                              s.kper);
+        hipExtLaunchKernelGGL(la_ce_dh_kernel, dim3(persistent_grid(nft * (Ncpad / NT) * s.nsplit)), dim3(CE_THREADS),
+                              0, stream, nullptr, nullptr, 0, (const bf16 *)W, (const bf16 *)P, part, Ncpad, d, V,
+                              s.Vpad, s.kper, s.nsplit);
         const size_t n4 = (size_t)Nc * d / 4;
         hipExtLaunchKernelGGL(la_ce_dh_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
                               nullptr, nullptr, 0, (const float *)part, (bf16 *)dh, c0, Nc, Ncpad, d, s.nsplit);
-        hipExtLaunchKernelGGL(la_ce_dw_kernel, dim3(nft * (s.Vpad / NT)), dim3(CE_THREADS), 0, stream, nullptr,
+        hipExtLaunchKernelGGL(la_ce_dw_kernel, dim3(persistent_grid(nft * (s.Vpad / NT))), dim3(CE_THREADS), 0, stream, nullptr,
                               last ? ev[1] : nullptr, 0, (const bf16 *)h, (const bf16 *)P, dW, c0, Nc, Ncpad, d, V,
                               s.Vpad, first ? 0 : 1);
     }
