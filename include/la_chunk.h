@@ -223,7 +223,7 @@ la_status la_seq_bwd(const void *q, const void *k, const void *v,
  *              ce_chunk x V bf16, is the only large transient.  The logits are never
  *              stored by the forward.
  * Supported: dt == LA_BF16, N >= 1, V >= 2, d a multiple of 128 up to 8192, and V * d and
- * ceil(ce_chunk / 128) * 128 * ceil(V / 128) * 128 below 2^30 (32-bit byte offsets).  Each call
+ * ceil(ce_chunk / 128) * 128 * ceil(V / 256) * 256 below 2^30 (32-bit byte offsets).  Each call
  * launches several kernels (la_time_next_launch brackets all of them).
  */
 size_t la_ce_workspace_bytes(int N, int d, int V, int ce_chunk);
@@ -241,11 +241,12 @@ int la_abi_version(void);
 
 /*
  * Measurement hook for benchmarks and profilers: the next la_chunk_fwd,
- * la_chunk_bwd, la_seq_fwd or la_seq_bwd call made by the calling thread records
- * start_event and stop_event (hipEvent_t, created by the caller with timing
- * enabled) on its kernel dispatch itself, so hipEventElapsedTime(start, stop) is
- * that kernel's execution time with no marker packets in between.  Each entry
- * point launches exactly one kernel.  The request is taken by that next call
+ * la_chunk_bwd, la_seq_fwd, la_seq_bwd, la_ce_fwd or la_ce_bwd call made by the
+ * calling thread records start_event and stop_event (hipEvent_t, created by the
+ * caller with timing enabled) on its kernel dispatches themselves, so
+ * hipEventElapsedTime(start, stop) is the execution time with no marker packets in
+ * between.  The attention entry points launch exactly one kernel; the
+ * cross-entropy calls record start on their first dispatch and stop on their last.  The request is taken by that next call
  * whatever its status; (NULL, NULL) clears it.  Returns LA_ERR_INVALID if only
  * one event is given.  The events are not validated: they must be live events
  * of the device the next call runs on.
