@@ -28,7 +28,7 @@ import threading
 
 __all__ = ["fwd", "bwd", "seq_fwd", "seq_bwd", "seq_supported", "seq_kernel_name", "chain_fwd", "chain_bwd", "linear_attention", "chunk_attention", "ChunkFunction", "LachunkError", "lib_path", "load_library",
            "abi_version", "status_str", "time_next_launch", "kernel_name", "BWD_MAX_C", "ce_fwd", "ce_bwd",
-           "ce_workspace_bytes", "chunked_cross_entropy"]
+           "ce_workspace_bytes", "chunked_cross_entropy", "set_attention_impl", "get_attention_impl", "IMPLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liblachunk.so")
@@ -427,7 +427,8 @@ def chain_bwd(q_chunks, k_chunks, v_chunks, carries, dO_chunks, dS_out=None, dz_
 
 def __getattr__(name):
     # the autograd layer imports torch; load it on first use
-    if name in ("linear_attention", "chunk_attention", "ChunkFunction", "chunked_cross_entropy"):
+    if name in ("linear_attention", "chunk_attention", "ChunkFunction", "chunked_cross_entropy",
+                "set_attention_impl", "get_attention_impl", "IMPLS"):
         from . import autograd
         return getattr(autograd, name)
     raise AttributeError(f"module {__name__!r} has no attribute {name!r}")

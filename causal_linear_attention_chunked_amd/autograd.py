@@ -16,9 +16,20 @@ the carry that fed it).  Either way nothing of size (G, C, D, D) or (G, C, C) is
 kept between the passes, the memory-flat principle of the page's section 1.  Gradients flow to q, k, v and,
 when given, S_in and z_in; a loss on S_out / z_out reaches them too.
 
+The implementation is selectable, as the page's call site selects its attention form
+(section 2, Opt 2: the chunked form next to the einsum and cumsum forms it replaces).
+Here the choice is among this library's GPU paths: "seq" (the sequence entry points),
+"chunk" (one launch per chunk and direction, the carry through memory) and "auto" (seq
+where it takes the shape, else chunk).  linear_attention(impl=...) picks one per call;
+set_attention_impl() sets the default, which otherwise comes from the environment
+variable LACHUNK_ATTN_IMPL, else "auto".  The einsum and cumsum forms themselves are
+references in the oracle (test infrastructure), not product paths.
+
 The arithmetic runs in the HIP library only: CPU tensors raise.
 """
 from __future__ import annotations
+
+import os
 
 import torch
 
@@ -101,12 +112,41 @@ def chunk_attention(q, k, v, S_in=None, z_in=None, block: int = 64):
     return ChunkFunction.apply(q, k, v, S_in, z_in, block)
 
 
-def linear_attention(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int = 64, feature_map=None):
+IMPLS = ("auto", "seq", "chunk")
+IMPL_ENV = "LACHUNK_ATTN_IMPL"
+_impl = None  # set by set_attention_impl; None: the environment variable, else "auto"
+
+
+def _check_impl(name, where):
+    if name not in IMPLS:
+        raise ValueError(f"{where}: unknown attention implementation {name!r}; use one of {IMPLS}")
+    return name
+
+
+def set_attention_impl(name):
+    """Set the implementation linear_attention uses when called without ``impl``: "auto",
+    "seq" or "chunk"; None returns to the environment variable LACHUNK_ATTN_IMPL (else
+    "auto")."""
+    global _impl
+    _impl = None if name is None else _check_impl(name, "set_attention_impl")
+
+
+def get_attention_impl() -> str:
+    """The implementation linear_attention uses when called without ``impl``."""
+    if _impl is not None:
+        return _impl
+    return _check_impl(os.environ.get(IMPL_ENV, "auto"), IMPL_ENV)
+
+
+def linear_attention(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int = 64, feature_map=None,
+                     impl=None):
     """Causal linear attention over a (G, T, D) sequence in chunks of ``chunk`` tokens
     (the last one ragged), carrying (S, z) across chunks.  Returns (o, (S_out, z_out)).
     ``feature_map="elu1"``: q and k are raw inputs and elu(x) + 1 is applied inside the
     kernels (fused; the shapes of the sequence path only), gradients flowing to the raw
-    inputs."""
+    inputs.  ``impl``: "auto", "seq" or "chunk" (None: get_attention_impl()); "seq" raises
+    where the sequence entry points do not take the shape."""
+    name = get_attention_impl() if impl is None else _check_impl(impl, "linear_attention")
     _check_device(q)
     if q.dim() != 3:
         raise ValueError(f"q must be (G, T, D), got {tuple(q.shape)}")
@@ -117,14 +157,19 @@ def linear_attention(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int
         return q.new_empty(q.shape), (S_in, z_in)
     fm = None if feature_map in (None, "none") else feature_map
     seq_ok = _seq_supported(q.dtype, T, q.shape[2], chunk, fm) and block == 64
+    if name == "seq" and not seq_ok:
+        raise ValueError("impl='seq': the sequence entry points take bf16, block 64, and D = 64 in whole "
+                         "128-token chunks or D = 128 in chunks of a multiple of 64 tokens")
     if fm is not None:
+        if name == "chunk":
+            raise ValueError("impl='chunk': the fused feature map runs in the sequence kernels only")
         if not seq_ok:
             raise ValueError(f"the fused feature map {feature_map!r} runs in the sequence kernels only "
                              "(bf16; D = 64 in whole 128-token chunks, or D = 128 in chunks of a "
                              "multiple of 64 tokens)")
         o, S, z = SeqFunction.apply(q, k, v, S_in, z_in, chunk, block, feature_map)
         return o, (S, z)
-    if seq_ok:
+    if seq_ok and name != "chunk":
         o, S, z = SeqFunction.apply(q, k, v, S_in, z_in, chunk, block, None)
         return o, (S, z)
     outs = []

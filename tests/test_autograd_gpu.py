@@ -87,3 +87,47 @@ def test_autograd_fused_feature_map(gpu):
 def test_autograd_fused_feature_map_wide_heads(gpu):
     # D = 128 with a ragged end: the mapped rows past the end must stay out of z
     _case("bf16", "zero", True, G=2, T=230, D=128, feature_map="elu1")
+
+
+def _grads(I, dO, impl, D):
+    dev = "cuda:0"
+    leaf = lambda x: x.to(dev).clone().requires_grad_(True)
+    q, k, v, S_in, z_in = (leaf(I[n]) for n in ("q", "k", "v", "S_in", "z_in"))
+    o, (S_out, z_out) = lac.linear_attention(q, k, v, S_in, z_in, chunk=128, impl=impl)
+    loss = (o.float() * dO).sum() + S_out.sum() + z_out.sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    return dict(o=o, S_out=S_out, z_out=z_out, dq=q.grad, dk=k.grad, dv=v.grad, dS_in=S_in.grad, dz_in=z_in.grad)
+
+
+@pytest.mark.parametrize("T,D", [(384, 64), (300, 128)])
+def test_autograd_impls_agree(gpu, T, D):
+    # impl="seq" (one launch per direction) and impl="chunk" (one per chunk and direction, the carry
+    # through memory) compute the same op: to fp32 rounding (the sequence path keeps compensation
+    # terms across chunks and takes a ragged end as a masked block)
+    G = 2
+    print(f"[case] autograd impls seq vs chunk G={G} T={T} D={D}", flush=True)
+    I = inp.make_inputs(G=G, T=T, D=D, dtype="bf16", carry="prior", backward=True, seed=90 + D)
+    dO = I["dO"].to("cuda:0").float()
+    a, b = _grads(I, dO, "seq", D), _grads(I, dO, "chunk", D)
+    for name in a:
+        x, y = a[name].double(), b[name].double()
+        rel = float((x - y).norm() / y.norm())
+        print(f"  {name}: seq vs chunk normwise {rel:.2e}", flush=True)
+        assert rel < 2e-3, (name, rel)
+    lac.set_attention_impl("chunk")
+    try:
+        c = _grads(I, dO, None, D)  # the default from the setter
+    finally:
+        lac.set_attention_impl(None)
+    for name in c:
+        assert torch.equal(c[name], b[name]), name
+
+
+def test_autograd_impl_seq_rejects_unsupported(gpu):
+    q = torch.ones(2, 200, 64, dtype=torch.float32, device="cuda:0")
+    with pytest.raises(ValueError, match="impl='seq'"):
+        lac.linear_attention(q, q, q, impl="seq")
+    x = torch.ones(2, 256, 64, dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(ValueError, match="impl='chunk'"):
+        lac.linear_attention(x, x, x, feature_map="elu1", impl="chunk")
