@@ -9,23 +9,22 @@
 //   den_t = sum_j P[t][j] + q_t . z_b
 //   num_t = sum_j P[t][j] v_j + S_b^T q_t,   o_t = num_t / den_t
 //   S_b+1 = S_b + K_b^T V_b,   z_b+1 = z_b + K_b^T 1.
-// Wave w owns query tile tq of block w / 4 (all 128 value columns; the second block's tiles in
-// reverse, so that the two waves of a SIMD carry a long and a short causal range) and eight
-// state tiles C[c][p]: value tiles 2 cp, 2 cp + 1 and key-feature tiles 4 ph .. 4 ph + 3.  The
+// Every wave takes part in both blocks' outputs: wave w owns value half w / 4 (64 columns) of query
+// tile tq of each block (tq = w % 4 for the first half, 3 - w % 4 for the second, so that the two
+// waves of a SIMD carry a long and a short causal range), and eight state tiles C[c][p]: value
+// tiles 2 cp, 2 cp + 1 and key-feature tiles 4 ph .. 4 ph + 3.  The
 // state and z are carried as unevaluated sums with compensation terms (each block's products
 // added with a two-sum), and the final carry goes out as its nearest fp32 values and the exact
 // remainders, for the sequence backward's recovery.  Three phases per chunk, two barriers:
 //   A  stage block 0's K, V; the bf16 copy of S_0 and the split row of z_0
 //   B  S_1 (copy, z_1 row); block 0's outputs; stage block 1's K, V
-//   C  block 1's outputs; S_2 = S_1 + K_1^T V_1
+//   C  S_2 = S_1 + K_1^T V_1; block 1's outputs
 // The next chunk's keys and values are loaded into the staging registers as soon as those are
-// free, and a wave's queries right after its outputs are stored.  A ragged end is a masked
+// free, and a wave's queries of the next block right after its outputs are stored.  A ragged end is a masked
 // block: rows past the sequence read as zero (buffer ranges) and are not stored.
-// FM: q and k are raw inputs and the positive feature map elu(x) + 1 is applied inside, in the
-// registers they arrive in and in the phase where the wave computes no outputs: block 0's waves
-// map the next chunk's queries and staged keys in phase C, block 1's waves their queries, this
-// chunk's second-block keys and the next chunk's first-block keys in phase B.  Mapped keys past
-// the end of the sequence are zero, as raw ones are (phi(0) = 1 would count them in z).
+// FM: q and k are raw inputs and the positive feature map elu(x) + 1 is applied inside: keys as
+// they are staged (mapped keys past the end of the sequence are zero, as raw ones are: phi(0) = 1
+// would count them in z), queries where they are used.
 #include "la_tile.h"
 #include "la_launch.h"
 #include <hip/hip_ext.h>
@@ -63,8 +62,8 @@ __device__ __forceinline__ void fwd_seq128_body(
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int blk = w >> 2;
-    const int tq = blk ? 3 - (w & 3) : (w & 3);
+    const int half = w >> 2;
+    const int tq = half ? 3 - (w & 3) : (w & 3);
     // state tiles: value tiles 2 cp, 2 cp + 1, key-feature tiles 4 ph + i.  The waves with cp = 0 also
     // carry z; rotating cp by ph puts them on SIMDs 0 and 3.
     const int ph = w >> 2, cp = (w + ph) & 3;
@@ -85,26 +84,13 @@ __device__ __forceinline__ void fwd_seq128_body(
     };
     load_kv(0, 0);
     load_kv(1, 0);
-    bf16x8 qf[4];  // this wave's 16 queries: row t = r, k = key feature 32 kc ..
-    auto load_q = [&](uint32_t tok) {
+    bf16x8 qf[4];  // this wave's 16 queries of one block: row t = r, k = key feature 32 kc ..
+    auto load_q = [&](uint32_t tok, int b) {
         const int lane = tid & 63;
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) qf[kc] = ldfrag_g<bf16>(qr, (tok + 64 * blk + 16 * tq) * D + 32 * kc, D, lane);
+        for (int kc = 0; kc < 4; ++kc) qf[kc] = ldfrag_g<bf16>(qr, (tok + 64 * b + 16 * tq) * D + 32 * kc, D, lane);
     };
-    load_q(0);
-    auto map_q = [&]() {
-        if constexpr (FM) {
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) qf[kc] = elu1_8(qf[kc]);
-        }
-    };
-    // staging registers rr of chunk cc mapped in place (rows tid / 16 + 32 (rr % 2) of block rr / 2)
-    auto map_k = [&](int rr, int cc) {
-        if constexpr (FM) {
-            const int row = 64 * (rr >> 1) + (tid >> 4) + 32 * (rr & 1);
-            kst[rr] = row < T - cc * C ? elu1_8(kst[rr]) : bf16x8{};
-        }
-    };
+    load_q(0, 0);
     floatx4 Sacc[2][4], Scomp[2][4];
     float zr[4], zc[4];
     {
@@ -126,14 +112,6 @@ __device__ __forceinline__ void fwd_seq128_body(
     load_kv(2, 0);
     load_kv(3, 0);
     issue_fence();
-    // the first chunk's keys (block 0's waves also their queries and block 1's keys)
-    map_k(0, 0);
-    map_k(1, 0);
-    if (blk == 0) {
-        map_q();
-        map_k(2, 0);
-        map_k(3, 0);
-    }
     const bf16x8 ones = ones_frag<bf16>();
 
     using Blk0 = std::integral_constant<int, 0>;
@@ -152,7 +130,8 @@ __device__ __forceinline__ void fwd_seq128_body(
         auto stage = [&](int rr) {
             const int row = (tid_c >> 4) + 32 * (rr & 1), f = (tid_c >> 3) & 1;
             const uint32_t so = stage_off(row * 8 + (tid_c & 7));
-            *reinterpret_cast<bf16x8 *>(ktile(rr >> 1, f) + so) = kst[rr];
+            const bool live = 64 * (rr >> 1) + row < nvalid;
+            *reinterpret_cast<bf16x8 *>(ktile(rr >> 1, f) + so) = FM ? (live ? elu1_8(kst[rr]) : bf16x8{}) : kst[rr];
             *reinterpret_cast<bf16x8 *>(vtile(rr >> 1, f) + so) = vst[rr];
         };
         // bf16 copy of S_b (stored [p][c]) and the split row of z_b
@@ -205,10 +184,15 @@ __device__ __forceinline__ void fwd_seq128_body(
                 }
             }
         };
-        // this wave's outputs for its block: scores, row sums, the intra-block numerator, then the
-        // inter-block terms against the state before the block; o stored; the next chunk's queries
+        // this wave's outputs for block B (its query tile, its value half): scores, row sums, the
+        // intra-block numerator, then the inter-block terms against the state before the block; o
+        // stored
         auto outputs = [&](auto b_tag) {
             constexpr int B = decltype(b_tag)::value;
+            if constexpr (FM) {
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc) qf[kc] = elu1_8(qf[kc]);
+            }
             floatx4 sc[4];
             float dsum = 0.f;
 #pragma unroll
@@ -224,23 +208,22 @@ __device__ __forceinline__ void fwd_seq128_body(
                     dsum += (sc[jt][0] + sc[jt][1]) + (sc[jt][2] + sc[jt][3]);
                 }
             }
-            floatx4 nm[8];
+            floatx4 nm[4];  // value tiles 4 half + x
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) nm[ct] = zero4();
+            for (int x = 0; x < 4; ++x) nm[x] = zero4();
 #pragma unroll
             for (int jc = 0; jc < 2; ++jc) {
                 if (2 * jc <= tq) {
                     const Split8 pf = split_acc(sc[2 * jc], sc[2 * jc + 1]);
 #pragma unroll
-                    for (int ct = 0; ct < 8; ++ct) mma_s(nm[ct], tfrag_tr(vtile(B, ct >> 2), TL.tr[ct & 3], jc), pf);
+                    for (int x = 0; x < 4; ++x) mma_s(nm[x], tfrag_tr(vtile(B, half), TL.tr[x], jc), pf);
                 }
             }
             floatx4 dn = zero4();
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
-                for (int ct = 0; ct < 8; ++ct)
-                    mma(nm[ct], tfrag_tr(stile(B, kc >> 1, ct >> 2), TL.tr[ct & 3], kc & 1), qf[kc]);
+                for (int x = 0; x < 4; ++x) mma(nm[x], tfrag_tr(stile(B, kc >> 1, half), TL.tr[x], kc & 1), qf[kc]);
                 const char *zb = zrow + 2 * B * 256 + (kc >> 1) * 128;
                 mma(dn, rowfrag(zb, lane, kc & 1), qf[kc]);
                 mma(dn, rowfrag(zb + 256, lane, kc & 1), qf[kc]);
@@ -248,12 +231,10 @@ __device__ __forceinline__ void fwd_seq128_body(
             const float inv = __builtin_amdgcn_rcpf(gsum(dsum) + dn[0]);
             const int trow = 64 * B + 16 * tq + r;
             if (trow < nvalid) {
-                bf16 *orow = o + (gtok0 + (size_t)c * C + trow) * D + 4 * g;
+                bf16 *orow = o + (gtok0 + (size_t)c * C + trow) * D + 64 * half + 4 * g;
 #pragma unroll
-                for (int ct = 0; ct < 8; ++ct) store_bf16x4<false>(orow + 16 * ct, pack4(nm[ct] * inv));
+                for (int x = 0; x < 4; ++x) store_bf16x4<false>(orow + 16 * x, pack4(nm[x] * inv));
             }
-            // the next chunk's queries into the same registers (past the end: zeros)
-            load_q((uint32_t)(c + 1) * C);
         };
 
         // ---- phase A: block 0's keys and values; S_0 copy and z_0 row
@@ -267,32 +248,19 @@ __device__ __forceinline__ void fwd_seq128_body(
         // ---- phase B: S_1 (copy, z_1 row); block 0's outputs; block 1's keys and values
         advance(0);
         write_state(1);
-        if (blk == 0) {
-            outputs(Blk0{});
-        } else {
-            map_q();
-            map_k(2, c);
-            map_k(3, c);
-        }
         stage(2);
         stage(3);
         load_kv(2, cbase + CHUNK);
         load_kv(3, cbase + CHUNK);
-        if (blk == 1 && c + 1 < n) {
-            map_k(0, c + 1);
-            map_k(1, c + 1);
-        }
+        outputs(Blk0{});
+        load_q((uint32_t)c * C, 1);  // block 1's queries, for phase C
         lds_barrier();
 
-        // ---- phase C: block 1's outputs; the state after the chunk.  No barrier follows: the next
+        // ---- phase C: the state after the chunk; block 1's outputs.  No barrier follows: the next
         // chunk's phase A writes block 0's tiles, the S_0 copy and z_0 row, which phase C does not read.
-        if (blk == 1) outputs(Blk1{});
         advance(1);
-        if (blk == 0 && c + 1 < n) {
-            map_q();
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) map_k(rr, c + 1);
-        }
+        outputs(Blk1{});
+        load_q((uint32_t)(c + 1) * C, 0);  // the next chunk's block 0 (past the end: zeros)
     }
     {
         const int lane = tid & 63, r = lane & 15, g = lane >> 4;
