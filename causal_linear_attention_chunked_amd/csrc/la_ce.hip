@@ -4,10 +4,11 @@
 //   logit_iv = h_i . W_v,  lse_i = log sum_v exp(logit_iv),  loss = (1/N) sum_i (lse_i - logit_{i,t_i})
 //   P_iv = (g/N) (exp(logit_iv - lse_i) - [v = t_i]),  dh = P W,  dW = P^T h
 //
-// Every product is one MFMA GEMM mainloop (bf16 operands, fp32 accumulators): a 256 x 128
-// output tile per workgroup of eight waves (64 x 64 each, 16 accumulator tiles), the operands
-// loaded 64 k at a time straight from global memory into three LDS stages (buffer loads that
-// write LDS), two k-steps ahead of the products.  The loads fill the swizzled 64 x 64 tile layout
+// Every product is one MFMA GEMM mainloop (bf16 operands, fp32 accumulators): 256 x 128 output
+// tiles over eight waves (64 x 64 each, 16 accumulator tiles), persistent workgroups (one per
+// CU) each walking a run of tiles, the operands loaded 64 k at a time straight from global memory
+// into three LDS stages (buffer loads that write LDS), two k-steps ahead of the products, across
+// tile boundaries.  The loads fill the swizzled 64 x 64 tile layout
 // of csrc/la_tile.h: each load instruction writes 1 KB of consecutive LDS (eight tile rows), so
 // every lane fetches the 16 bytes that belong in its slot.  An operand is read from LDS with the
 // natural fragment read when it is stored k-contiguous and with the transposed read when it is
@@ -15,7 +16,7 @@
 // operand read as zero (buffer ranges), or, for a k-major operand whose rows end inside its
 // storage rows, as values that only reach output rows that are not stored.  The epilogues:
 //   forward: the tile's logits never leave registers: per token, the maximum and the sum of
-//            exponentials over the tile's 128 classes (combined over the two waves in LDS) go to
+//            exponentials over the tile's 256 classes (combined over the four waves in LDS) go to
 //            a partials array, and the target's logit where it falls in the tile; a second kernel
 //            combines each token's partials into lse (16 threads per token), a third takes the
 //            mean loss in a fixed order (deterministic);
