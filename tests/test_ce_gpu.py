@@ -63,6 +63,16 @@ def test_ce_head_workload_full_size(gpu):
     compare(I, run(I))
 
 
+def test_ce_persistent_walk_masked_features(gpu):
+    # d = 640 (an odd multiple of 128: the last 256-feature tile half masked) over the full
+    # vocabulary: several tiles per workgroup in the forward, dW and dh kernels, two backward
+    # chunks of 128 tokens
+    N, d, V = 256, 640, 50257
+    say(f"[case] ce N={N} d={d} V={V} chunk=128 (persistent walk, masked feature tiles)")
+    I = inp.make_ce_inputs(N, d, V, seed=17)
+    compare(I, run(I, 0.75, 128), 0.75)
+
+
 def test_ce_chunked_backward_matches_whole(gpu):
     # the pages' chunked form: the same gradients whatever the chunk (to the summation order)
     w = inp.ce_workload("ce_n512_d1280_v50257_bf16")
