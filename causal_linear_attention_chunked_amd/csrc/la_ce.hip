@@ -27,6 +27,7 @@
 #include "la_tile.h"
 #include "la_launch.h"
 #include <hip/hip_ext.h>
+#include <atomic>
 
 namespace lachunk {
 
@@ -490,15 +491,16 @@ CeShape ce_shape(int N, int d, int V, int ce_chunk) {
 // LDS allows one), a multiple of 8 so that workgroup b runs on XCD b % 8 for every b; fewer when
 // there are fewer tiles.
 static unsigned persistent_grid(uint32_t T) {
-    static int ncu[16];
+    // CU count per device, read once (threads that race on the first read store the same value)
+    static std::atomic<int> ncu[16];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
-    if (ncu[dev] == 0) {
-        int n = 0;
+    int n = ncu[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 8;
-        ncu[dev] = n;
+        ncu[dev].store(n, std::memory_order_relaxed);
     }
-    const unsigned g = (unsigned)ncu[dev] / 8 * 8, t8 = (T + 7) / 8 * 8;
+    const unsigned g = (unsigned)n / 8 * 8, t8 = (T + 7) / 8 * 8;
     return t8 < g ? t8 : g;
 }
 
