@@ -246,19 +246,20 @@ def test_seq_d128_longest_sequence(gpu):
     compare(run_seq_d128(I, dS, dz), oracle_ref(I, dS, dz))
 
 
-@pytest.mark.parametrize("G,T,carry,up", [
-    (2, 200, "zero", True),      # an 8-token ragged end: phi(0) = 1 must not enter z past it
-    (3, 64, "prior", False),     # one full block
-    (1, 1, "prior", True),       # a single token (from a zero carry its exact dq is 0: degenerate)
-    (2, 1000, "prior", True),    # 15 blocks and 40 tokens
+@pytest.mark.parametrize("G,T,carry,up,res", [
+    (2, 200, "zero", True, True),      # an 8-token ragged end: phi(0) = 1 must not enter z past it
+    (3, 64, "prior", False, True),     # one full block
+    (1, 1, "prior", True, True),       # a single token (from a zero carry its exact dq is 0: degenerate)
+    (2, 1000, "prior", True, True),    # 15 blocks and 40 tokens
+    (2, 700, "prior", True, False),    # without the remainders: the backward starts from the rounded carry
 ])
-def test_seq_d128_fused_feature_map(gpu, G, T, carry, up):
+def test_seq_d128_fused_feature_map(gpu, G, T, carry, up, res):
     # raw q, k (both signs) at D = 128; the op applies elu(x)+1, gradients of the raw inputs
-    say(f"[case] seq D=128 elu1 G={G} T={T} carry={carry} upstream={up}")
+    say(f"[case] seq D=128 elu1 G={G} T={T} carry={carry} upstream={up} remainders={res}")
     I = inp.make_inputs(G=G, T=T, D=128, dtype="bf16", carry=carry, backward=True, seed=70 + T,
                         features="raw")
     dS, dz = upstream(G, 128, 71) if up else (None, None)
-    compare(run_seq(I, dS, dz, feature="elu1"), oracle_ref(I, dS, dz, feature="elu1"))
+    compare(run_seq(I, dS, dz, feature="elu1", residual=res), oracle_ref(I, dS, dz, feature="elu1"))
 
 
 @pytest.mark.parametrize("shift", [-4.0, 4.0])
