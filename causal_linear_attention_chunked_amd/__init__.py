@@ -28,7 +28,7 @@ import threading
 
 __all__ = ["fwd", "bwd", "seq_fwd", "seq_bwd", "seq_supported", "seq_kernel_name", "chain_fwd", "chain_bwd", "linear_attention", "chunk_attention", "ChunkFunction", "LachunkError", "lib_path", "load_library",
            "abi_version", "status_str", "time_next_launch", "kernel_name", "BWD_MAX_C", "ce_fwd", "ce_bwd",
-           "ce_workspace_bytes", "chunked_cross_entropy", "set_attention_impl", "get_attention_impl", "IMPLS"]
+           "ce_workspace_bytes", "ce_fwd_workspace_bytes", "chunked_cross_entropy", "set_attention_impl", "get_attention_impl", "IMPLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liblachunk.so")
@@ -80,6 +80,8 @@ def load_library():
         lib.la_seq_bwd.argtypes = [vp] * 15 + [i] * 7 + [vp]
         lib.la_ce_workspace_bytes.restype = ctypes.c_size_t
         lib.la_ce_workspace_bytes.argtypes = [i] * 4
+        lib.la_ce_fwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.la_ce_fwd_workspace_bytes.argtypes = [i] * 3
         lib.la_ce_fwd.restype = i
         lib.la_ce_fwd.argtypes = [vp] * 6 + [ctypes.c_size_t] + [i] * 4 + [vp]
         lib.la_ce_bwd.restype = i
@@ -208,6 +210,21 @@ def _validate_state(name, t, shape, dev):
         raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shape} on cuda:{dev}")
 
 
+def _validate_outputs(names, tokens, states, ref, G, D, dev):
+    """Caller-supplied output tensors: `tokens` like `ref` (shape, dtype, device, contiguous),
+    `states` fp32 (G, D, D) then (G, D) pairs.  The library can check only alignment and
+    overlap, so a wrong buffer here would be written out of bounds."""
+    nt = len(tokens)
+    for n, t in zip(names[:nt], tokens):
+        if t is None:
+            raise ValueError(f"out: {n} is missing")
+        _validate_tokens(("the inputs", n), (ref, t))
+    for j, (n, t) in enumerate(zip(names[nt:], states)):
+        if t is None:
+            raise ValueError(f"out: {n} is missing")
+        _validate_state(n, t, (G, D, D) if j % 2 == 0 else (G, D), dev)
+
+
 def _stream(dev):
     """Raw handle of the current stream on device index ``dev``."""
     import torch
@@ -229,6 +246,7 @@ def fwd(q, k, v, S_in=None, z_in=None, block: int = 64, out=None):
         z_out = torch.empty((G, D), dtype=torch.float32, device=q.device)
     else:
         o, S_out, z_out = out
+        _validate_outputs(("o", "S_out", "z_out"), (o,), (S_out, z_out), q, G, D, dev)
     _check("la_chunk_fwd", lib.la_chunk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(S_in), _ptr(z_in),
                                             o.data_ptr(), S_out.data_ptr(), z_out.data_ptr(), G, C, D, int(block),
                                             _dtype_code(q), _stream(dev)))
@@ -252,6 +270,7 @@ def bwd(q, k, v, S_in, z_in, dO, dS_out=None, dz_out=None, block: int = 64, out=
         dz_in = torch.empty((G, D), dtype=torch.float32, device=q.device)
     else:
         dq, dk, dv, dS_in, dz_in = out
+        _validate_outputs(("dq", "dk", "dv", "dS_in", "dz_in"), (dq, dk, dv), (dS_in, dz_in), q, G, D, dev)
     _check("la_chunk_bwd", lib.la_chunk_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(S_in), _ptr(z_in),
                                             dO.data_ptr(), _ptr(dS_out), _ptr(dz_out), dq.data_ptr(),
                                             dk.data_ptr(), dv.data_ptr(), dS_in.data_ptr(), dz_in.data_ptr(),
@@ -281,6 +300,9 @@ def seq_fwd(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int = 64, ou
         z_res = torch.empty((G, D), dtype=torch.float32, device=q.device) if residual else None
     else:
         o, S_out, z_out, S_res, z_res = out if residual else (*out, None, None)
+        _validate_outputs(("o", "S_out", "z_out"), (o,), (S_out, z_out), q, G, D, dev)
+        if residual:
+            _validate_outputs(("S_res", "z_res"), (), (S_res, z_res), q, G, D, dev)
     _check("la_seq_fwd", lib.la_seq_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(S_in), _ptr(z_in),
                                         o.data_ptr(), S_out.data_ptr(), z_out.data_ptr(), _ptr(S_res), _ptr(z_res),
                                         G, T, D, int(chunk), int(block), _feature_code(feature), _dtype_code(q),
@@ -316,6 +338,7 @@ def seq_bwd(q, k, v, S_last, z_last, dO, dS_out=None, dz_out=None, chunk: int = 
         dz_in = torch.empty((G, D), dtype=torch.float32, device=q.device)
     else:
         dq, dk, dv, dS_in, dz_in = out
+        _validate_outputs(("dq", "dk", "dv", "dS_in", "dz_in"), (dq, dk, dv), (dS_in, dz_in), q, G, D, dev)
     _check("la_seq_bwd", lib.la_seq_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), S_last.data_ptr(),
                                         z_last.data_ptr(), _ptr(S_res), _ptr(z_res), dO.data_ptr(), _ptr(dS_out),
                                         _ptr(dz_out),
@@ -326,8 +349,15 @@ def seq_bwd(q, k, v, S_last, z_last, dO, dS_out=None, dz_out=None, chunk: int = 
 
 
 def ce_workspace_bytes(N: int, d: int, V: int, ce_chunk: int = 0) -> int:
-    """Bytes of device workspace ce_fwd / ce_bwd need (0: shape not supported)."""
+    """Bytes of device workspace ce_bwd needs at this chunk, enough for ce_fwd too, so one
+    buffer serves both (0: shape not supported)."""
     return int(load_library().la_ce_workspace_bytes(int(N), int(d), int(V), int(ce_chunk)))
+
+
+def ce_fwd_workspace_bytes(N: int, d: int, V: int) -> int:
+    """Bytes of device workspace ce_fwd needs: its per-tile partial sums, no logits (0: shape not
+    supported)."""
+    return int(load_library().la_ce_fwd_workspace_bytes(int(N), int(d), int(V)))
 
 
 def _ce_check(h, W, targets):
@@ -350,9 +380,21 @@ def _workspace(ws, nbytes, dev):
     import torch
     if ws is None:
         return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=f"cuda:{dev}")
+    if ws.get_device() != dev or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on cuda:{dev}")
     if ws.numel() * ws.element_size() < nbytes:
         raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes, {nbytes} needed")
     return ws
+
+
+def _ce_f32(name, t, shape, dev):
+    """A float32 tensor of `shape` on cuda:dev, contiguous (a scalar may be 0-dim or one element)."""
+    import torch
+    ok = (t is not None and t.dtype is torch.float32 and t.get_device() == dev and t.is_contiguous()
+          and (tuple(t.shape) == shape or (shape == () and t.numel() == 1)))
+    if not ok:
+        what = "scalar" if shape == () else f"tensor of shape {shape}"
+        raise ValueError(f"{name} must be a contiguous float32 {what} on cuda:{dev}")
 
 
 def ce_fwd(h, W, targets, workspace=None, out=None):
@@ -361,7 +403,7 @@ def ce_fwd(h, W, targets, workspace=None, out=None):
     import torch
     lib = _lib or load_library()
     N, d, V, dev = _ce_check(h, W, targets)
-    nbytes = ce_workspace_bytes(N, d, V, N)
+    nbytes = ce_fwd_workspace_bytes(N, d, V)
     if nbytes == 0:
         raise LachunkError("la_ce_fwd", 2, status_str(2))
     ws = _workspace(workspace, nbytes, dev)
@@ -370,6 +412,8 @@ def ce_fwd(h, W, targets, workspace=None, out=None):
         lse = torch.empty((N,), dtype=torch.float32, device=h.device)
     else:
         loss, lse = out
+        _ce_f32("loss", loss, (), dev)
+        _ce_f32("lse", lse, (N,), dev)
     _check("la_ce_fwd", lib.la_ce_fwd(h.data_ptr(), W.data_ptr(), targets.data_ptr(), loss.data_ptr(),
                                       lse.data_ptr(), ws.data_ptr(), nbytes, N, d, V, LA_BF16, _stream(dev)))
     return loss, lse
@@ -382,6 +426,9 @@ def ce_bwd(h, W, targets, lse, dloss=None, ce_chunk: int = 0, workspace=None, ou
     import torch
     lib = _lib or load_library()
     N, d, V, dev = _ce_check(h, W, targets)
+    _ce_f32("lse", lse, (N,), dev)
+    if dloss is not None:
+        _ce_f32("dloss", dloss, (), dev)
     nbytes = ce_workspace_bytes(N, d, V, ce_chunk)
     if nbytes == 0:
         raise LachunkError("la_ce_bwd", 2, status_str(2))
@@ -391,6 +438,10 @@ def ce_bwd(h, W, targets, lse, dloss=None, ce_chunk: int = 0, workspace=None, ou
         dW = torch.empty((V, d), dtype=torch.float32, device=h.device)
     else:
         dh, dW = out
+        if (dh is None or dh.dtype is not torch.bfloat16 or dh.shape != h.shape or dh.get_device() != dev
+                or not dh.is_contiguous()):
+            raise ValueError(f"out: dh must be a contiguous bfloat16 tensor of shape {tuple(h.shape)} on cuda:{dev}")
+        _ce_f32("dW", dW, (V, d), dev)
     _check("la_ce_bwd", lib.la_ce_bwd(h.data_ptr(), W.data_ptr(), targets.data_ptr(), lse.data_ptr(), _ptr(dloss),
                                       dh.data_ptr(), dW.data_ptr(), ws.data_ptr(), nbytes, N, d, V, int(ce_chunk),
                                       LA_BF16, _stream(dev)))

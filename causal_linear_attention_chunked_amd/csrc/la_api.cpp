@@ -219,30 +219,44 @@ la_status la_seq_bwd(const void *q, const void *k, const void *v, const float *S
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
-// Cross-entropy: the supported shapes and the workspace they need (0 when unsupported).
-static la_status ce_checks(int N, int d, int V, int ce_chunk, la_dtype dt, lachunk::CeShape *s) {
+// Cross-entropy: the shapes the forward supports (its kernels address h and W with 32-bit byte
+// offsets; the partials are indexed in 64 bits).  The forward's workspace is s->fwd_bytes.
+static la_status ce_fwd_checks(int N, int d, int V, la_dtype dt, lachunk::CeShape *s) {
     if (N < 1 || d < 1 || V < 2) return LA_ERR_INVALID;
     if (dt != LA_BF16 || d % 128 != 0 || d > 8192) return LA_ERR_UNSUPPORTED;
+    *s = lachunk::ce_shape(N, d, V, N);
+    if ((size_t)V * d >= ((size_t)1 << 30) || (size_t)s->Npad * d >= ((size_t)1 << 30)) return LA_ERR_UNSUPPORTED;
+    return LA_OK;
+}
+
+// The backward's, at this chunk: P of one chunk is also addressed with 32-bit byte offsets.  Its
+// workspace is s->bwd_bytes.
+static la_status ce_bwd_checks(int N, int d, int V, int ce_chunk, la_dtype dt, lachunk::CeShape *s) {
+    la_status st = ce_fwd_checks(N, d, V, dt, s);
+    if (st != LA_OK) return st;
     *s = lachunk::ce_shape(N, d, V, ce_chunk);
-    if ((size_t)V * d >= ((size_t)1 << 30) || (size_t)s->chunk_pad * s->Vpad >= ((size_t)1 << 30) ||
-        (size_t)s->Npad * d >= ((size_t)1 << 30))
-        return LA_ERR_UNSUPPORTED;
+    if ((size_t)s->chunk_pad * s->Vpad >= ((size_t)1 << 30)) return LA_ERR_UNSUPPORTED;
     return LA_OK;
 }
 
 size_t la_ce_workspace_bytes(int N, int d, int V, int ce_chunk) {
     lachunk::CeShape s;
-    return ce_checks(N, d, V, ce_chunk, LA_BF16, &s) == LA_OK ? s.ws_bytes : 0;
+    return ce_bwd_checks(N, d, V, ce_chunk, LA_BF16, &s) == LA_OK ? s.ws_bytes : 0;
+}
+
+size_t la_ce_fwd_workspace_bytes(int N, int d, int V) {
+    lachunk::CeShape s;
+    return ce_fwd_checks(N, d, V, LA_BF16, &s) == LA_OK ? s.fwd_bytes : 0;
 }
 
 la_status la_ce_fwd(const void *h, const void *W, const int *targets, float *loss, float *lse, void *workspace,
                     size_t workspace_bytes, int N, int d, int V, la_dtype dt, void *stream) {
     const TakenEvents te;
     lachunk::CeShape s;
-    la_status st = ce_checks(N, d, V, N, dt, &s);
+    la_status st = ce_fwd_checks(N, d, V, dt, &s);
     if (st != LA_OK) return st;
     if (!h || !W || !targets || !loss || !lse || !workspace) return LA_ERR_INVALID;
-    if (workspace_bytes < s.ws_bytes) return LA_ERR_INVALID;
+    if (workspace_bytes < s.fwd_bytes) return LA_ERR_INVALID;
     const void *ptrs[] = {h, W, targets, loss, lse, workspace};
     for (const void *p : ptrs)
         if (!aligned16(p)) return LA_ERR_ALIGN;
@@ -260,10 +274,10 @@ la_status la_ce_bwd(const void *h, const void *W, const int *targets, const floa
                     la_dtype dt, void *stream) {
     const TakenEvents te;
     lachunk::CeShape s;
-    la_status st = ce_checks(N, d, V, ce_chunk, dt, &s);
+    la_status st = ce_bwd_checks(N, d, V, ce_chunk, dt, &s);
     if (st != LA_OK) return st;
     if (!h || !W || !targets || !lse || !dh || !dW || !workspace) return LA_ERR_INVALID;
-    if (workspace_bytes < s.ws_bytes) return LA_ERR_INVALID;
+    if (workspace_bytes < s.bwd_bytes) return LA_ERR_INVALID;
     const void *ptrs[] = {h, W, targets, lse, dloss, dh, dW, workspace};
     for (const void *p : ptrs)
         if (!aligned16(p)) return LA_ERR_ALIGN;

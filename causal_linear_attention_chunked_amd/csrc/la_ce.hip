@@ -33,9 +33,9 @@ namespace lachunk {
 
 namespace {
 constexpr int CE_THREADS = 512;  // eight waves
-constexpr int MT = 256;          // output tile rows (the A operand's)
-constexpr int NT = 128;          // output tile columns (the B operand's)
-constexpr int CK = 64;           // k per stage
+constexpr int MT = CE_MT;        // output tile rows (the A operand's)
+constexpr int NT = CE_NT;        // output tile columns (the B operand's)
+constexpr int CK = CE_CK;        // k per stage
 constexpr int STAGE = (MT + NT) / 64 * TBYTES;  // one stage: A tiles 0-3, then B tiles 0-1 (48 KB)
 
 typedef int int4v __attribute__((ext_vector_type(4)));
@@ -465,27 +465,6 @@ __global__ __launch_bounds__(256) void la_ce_dh_reduce_kernel(const float *__res
 }
 
 // ---------------------------------------------------------------- host side
-
-CeShape ce_shape(int N, int d, int V, int ce_chunk) {
-    CeShape s;
-    s.Npad = (N + NT - 1) / NT * NT;
-    s.Vpad = (V + MT - 1) / MT * MT;  // whole class tiles of the forward and of P
-    s.nvt = s.Vpad / MT;
-    s.chunk = ce_chunk < 1 || ce_chunk > N ? N : ce_chunk;
-    s.chunk_pad = (s.chunk + NT - 1) / NT * NT;
-    // dh split over the vocabulary: at most one workgroup per compute unit (256), whole k-steps
-    // per split
-    const int tiles = (d + MT - 1) / MT * (s.chunk_pad / NT);
-    int nsplit = tiles >= 256 ? 1 : 256 / tiles;
-    if (nsplit > s.Vpad / CK) nsplit = s.Vpad / CK;
-    s.kper = ((s.Vpad + nsplit - 1) / nsplit + CK - 1) / CK * CK;
-    s.nsplit = (s.Vpad + s.kper - 1) / s.kper;
-    s.fwd_bytes = (size_t)s.nvt * s.Npad * 8 + (size_t)s.Npad * 8;  // partials, target logits, nll
-    s.p_bytes = (size_t)s.chunk_pad * s.Vpad * 2;
-    s.bwd_bytes = s.p_bytes + (size_t)s.nsplit * s.chunk_pad * d * 4;
-    s.ws_bytes = s.fwd_bytes > s.bwd_bytes ? s.fwd_bytes : s.bwd_bytes;
-    return s;
-}
 
 // Workgroups of a persistent launch over T tiles: one per compute unit at most (the GEMM kernels'
 // LDS allows one), a multiple of 8 so that workgroup b runs on XCD b % 8 for every b; fewer when

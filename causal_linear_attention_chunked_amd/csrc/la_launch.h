@@ -51,13 +51,35 @@ hipError_t launch_seq_bwd_d128(const void *q, const void *k, const void *v, cons
                                const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv, float *dS_in,
                                float *dz_in, int G, int T, bool elu1, hipStream_t stream, const hipEvent_t ev[2]);
 
-// Cross-entropy over a tied head (bf16 h, W; fp32 loss, lse, dW; bf16 dh).  The shape of the
-// workspace: padded sizes, the backward's chunking and the split of dh over the vocabulary.
+// Cross-entropy over a tied head (bf16 h, W; fp32 loss, lse, dW; bf16 dh).  The GEMM tiles
+// (CE_MT class rows x CE_NT tokens, CE_CK k per stage) and the shape of the workspace: padded
+// sizes, the backward's chunking and the split of dh over the vocabulary.  Host arithmetic
+// only (the argument checks use it too).
+constexpr int CE_MT = 256, CE_NT = 128, CE_CK = 64;
 struct CeShape {
     int Npad, Vpad, nvt, chunk, chunk_pad, kper, nsplit;
     size_t fwd_bytes, p_bytes, bwd_bytes, ws_bytes;
 };
-CeShape ce_shape(int N, int d, int V, int ce_chunk);
+inline CeShape ce_shape(int N, int d, int V, int ce_chunk) {
+    CeShape s;
+    s.Npad = (N + CE_NT - 1) / CE_NT * CE_NT;
+    s.Vpad = (V + CE_MT - 1) / CE_MT * CE_MT;  // whole class tiles of the forward and of P
+    s.nvt = s.Vpad / CE_MT;
+    s.chunk = ce_chunk < 1 || ce_chunk > N ? N : ce_chunk;
+    s.chunk_pad = (s.chunk + CE_NT - 1) / CE_NT * CE_NT;
+    // dh split over the vocabulary: at most one workgroup per compute unit (256), whole k-steps
+    // per split
+    const int tiles = (d + CE_MT - 1) / CE_MT * (s.chunk_pad / CE_NT);
+    int nsplit = tiles >= 256 ? 1 : 256 / tiles;
+    if (nsplit > s.Vpad / CE_CK) nsplit = s.Vpad / CE_CK;
+    s.kper = ((s.Vpad + nsplit - 1) / nsplit + CE_CK - 1) / CE_CK * CE_CK;
+    s.nsplit = (s.Vpad + s.kper - 1) / s.kper;
+    s.fwd_bytes = (size_t)s.nvt * s.Npad * 8 + (size_t)s.Npad * 8;  // partials, target logits, nll
+    s.p_bytes = (size_t)s.chunk_pad * s.Vpad * 2;
+    s.bwd_bytes = s.p_bytes + (size_t)s.nsplit * s.chunk_pad * d * 4;
+    s.ws_bytes = s.fwd_bytes > s.bwd_bytes ? s.fwd_bytes : s.bwd_bytes;
+    return s;
+}
 hipError_t launch_ce_fwd(const void *h, const void *W, const int *targets, float *loss, float *lse, void *ws, int N,
                          int d, int V, hipStream_t stream, const hipEvent_t ev[2]);
 hipError_t launch_ce_bwd(const void *h, const void *W, const int *targets, const float *lse, const float *dloss,

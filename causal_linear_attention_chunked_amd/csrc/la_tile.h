@@ -189,11 +189,13 @@ __device__ __forceinline__ void two_sum4(floatx4 &a, floatx4 &c, const floatx4 &
         c[e] = ce;
     }
 }
-// The unevaluated sum a + c as the nearest fp32 value s and the exact remainder (a - s) + c
-// (|c| <= |a|: c is a compensation term).
-__device__ __forceinline__ void fold(float a, float c, float &s, float &res) {
+// The unevaluated sum a + c as its fp32 rounding s and the exact remainder res = (a + c) - s,
+// for any magnitudes of a and c (Knuth's branch-free two-sum: a compensation term may outgrow
+// a running sum whose terms cancel).  Host-callable, so that a CPU test can check it.
+__host__ __device__ __forceinline__ void fold(float a, float c, float &s, float &res) {
     s = a + c;
-    res = (a - s) + c;
+    const float cc = s - a;
+    res = (a - (s - cc)) + (c - cc);
 }
 __device__ __forceinline__ void two_diff4(floatx4 &a, floatx4 &c, const floatx4 &p) {
 #pragma unroll

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 4
+#define LA_ABI_VERSION 5
 #define LA_BWD_MAX_C 2048
 /* Longest sequences (tokens per group) of the sequence entry points, D = 64 and D = 128:
  * the lengths at which their results are verified to the parity tolerance against an fp64
@@ -215,18 +215,23 @@ la_status la_seq_bwd(const void *q, const void *k, const void *v,
  *              it the backward forms each softmax from one recomputation of the logits).
  *   dloss    : fp32 scalar g on the device, or NULL for g = 1.
  *   dh       : [N][d] bf16 output;  dW : [V][d] fp32 output (overwritten).
- *   workspace: device scratch of at least la_ce_workspace_bytes(N, d, V, ce_chunk) bytes,
- *              16-byte aligned, owned by the caller, not read by the caller; the same
- *              workspace serves both calls (the forward's partial sums, the backward's
- *              P of one chunk and the partial sums of dh).
+ *   workspace: device scratch owned by the caller, 16-byte aligned, not read by the caller:
+ *              at least la_ce_fwd_workspace_bytes(N, d, V) bytes for the forward (its
+ *              per-tile partial sums: about 8 * N * V / 256 bytes, no logits) and
+ *              la_ce_workspace_bytes(N, d, V, ce_chunk) for the backward, which is also
+ *              enough for the forward, so one buffer of that size serves both calls (the
+ *              backward's P of one chunk and the partial sums of dh).
  *   ce_chunk : tokens per backward chunk (1..N; anything else means N): the chunk's P,
- *              ce_chunk x V bf16, is the only large transient.  The logits are never
- *              stored by the forward.
- * Supported: dt == LA_BF16, N >= 1, V >= 2, d a multiple of 128 up to 8192, and V * d and
- * ceil(ce_chunk / 128) * 128 * ceil(V / 256) * 256 below 2^30 (32-bit byte offsets).  Each call
- * launches several kernels (la_time_next_launch brackets all of them).
+ *              ce_chunk x V bf16, is the backward's only large transient.  The logits are
+ *              never stored.
+ * Supported: dt == LA_BF16, N >= 1, V >= 2, d a multiple of 128 up to 8192, V * d and
+ * ceil(N / 128) * 128 * d below 2^30, and for the backward also
+ * ceil(ce_chunk / 128) * 128 * ceil(V / 256) * 256 below 2^30 (32-bit byte offsets); the
+ * workspace-size calls return 0 outside that set.  Each call launches several kernels
+ * (la_time_next_launch brackets all of them).
  */
 size_t la_ce_workspace_bytes(int N, int d, int V, int ce_chunk);
+size_t la_ce_fwd_workspace_bytes(int N, int d, int V);
 la_status la_ce_fwd(const void *h, const void *W, const int *targets, float *loss, float *lse,
                     void *workspace, size_t workspace_bytes, int N, int d, int V, la_dtype dt, void *stream);
 la_status la_ce_bwd(const void *h, const void *W, const int *targets, const float *lse, const float *dloss,

@@ -109,15 +109,3 @@ def bwd(q, k, v, S_in, z_in, dO, dS_out=None, dz_out=None, nthreads: int = 0):
         raise ValueError(f"oracle: la_oracle_bwd returned {rc}")
     return dq, dk, dv, dS_in, dz_in
 
-
-def fwd_chunked_calls(q, k, v, S_in, z_in, chunks, nthreads: int = 0):
-    """Run ``fwd`` chunk by chunk, carrying (S, z); returns (o, [(S_out, z_out) per chunk])."""
-    q, k, v, S_in, z_in = map(_f64, (q, k, v, S_in, z_in))
-    outs, carries, s = [], [], 0
-    S, z = S_in, z_in
-    for c in chunks:
-        o, S, z = fwd(q[:, s:s + c], k[:, s:s + c], v[:, s:s + c], S, z, nthreads)
-        outs.append(o)
-        carries.append((S, z))
-        s += c
-    return np.concatenate(outs, axis=1), carries

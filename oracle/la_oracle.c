@@ -13,9 +13,9 @@
  *     z_t = z_in + sum_{j<=t} k_j
  *     o_t = (S_t^T q_t) / (q_t . z_t)
  *
- * and S_out = S_T, z_out = z_T.  The backward is the reverse scan that the same
- * section names ("the derivative of a cumsum is a reverse cumsum"), written out
- * for the loss  L = sum_t <dO_t, o_t> + <dS_out, S_out> + dz_out . z_out:
+ * and S_out = S_T, z_out = z_T.  The backward is the reverse scan of the same
+ * section (the gradient of a prefix sum is a suffix sum), written out for the
+ * loss  L = sum_t <dO_t, o_t> + <dS_out, S_out> + dz_out . z_out:
  *
  *     den_t  = q_t . z_t,   dn_t = dO_t / den_t,   dden_t = -(dO_t . o_t) / den_t
  *     dq_t   = S_t dn_t + dden_t z_t

@@ -1,0 +1,148 @@
+// Drives every entry point of include/la_chunk.h through its host-side validation, built with
+// AddressSanitizer against stand-in launchers (stub_launchers.cpp): accepted calls must reach
+// the launcher the dispatch rules name, rejected ones must return their status and launch
+// nothing.  Device pointers are fake, aligned, non-overlapping addresses: the validation only
+// compares and offsets them, it never dereferences them.  Exit status 0 when every case holds.
+#include <stdint.h>
+#include <stdio.h>
+
+#include "la_chunk.h"
+
+extern int g_last_launch;
+enum {
+    L_NONE = 0, L_FWD, L_BWD, L_FWD_C128, L_BWD_C128, L_SEQ_FWD_C128, L_SEQ_BWD_C128, L_SEQ_FWD_D128,
+    L_SEQ_BWD_D128, L_CE_FWD, L_CE_BWD, L_CE_FWD_NOALLOC
+};
+
+static int failures = 0;
+
+static void *A(int i) { return reinterpret_cast<void *>((uintptr_t)1 << 40 | (uintptr_t)i << 32); }
+static float *F(int i) { return static_cast<float *>(A(i)); }
+
+static void expect(const char *what, la_status got, la_status want, int launch_want) {
+    const int launched = g_last_launch;
+    g_last_launch = L_NONE;
+    if (got != want || launched != (want == LA_OK ? launch_want : L_NONE)) {
+        printf("FAIL %s: status %d (want %d), launcher %d (want %d)\n", what, (int)got, (int)want, launched,
+               want == LA_OK ? launch_want : L_NONE);
+        ++failures;
+    }
+}
+
+int main() {
+    // ---- la_chunk_fwd
+    expect("fwd headline", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 160, 128, 64, 64, LA_BF16, 0),
+           LA_OK, L_FWD_C128);
+    expect("fwd ragged", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 4, 100, 64, 64, LA_BF16, 0),
+           LA_OK, L_FWD);
+    expect("fwd fp32 d128 no carry",
+           la_chunk_fwd(A(0), A(1), A(2), nullptr, nullptr, A(5), F(6), F(7), 1, 37, 128, 64, LA_F32, 0), LA_OK, L_FWD);
+    expect("fwd G=0", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 0, 128, 64, 64, LA_BF16, 0),
+           LA_ERR_INVALID, 0);
+    expect("fwd D=96", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 4, 128, 96, 64, LA_BF16, 0),
+           LA_ERR_UNSUPPORTED, 0);
+    expect("fwd half carry", la_chunk_fwd(A(0), A(1), A(2), nullptr, F(4), A(5), F(6), F(7), 4, 128, 64, 64, LA_BF16, 0),
+           LA_ERR_INVALID, 0);
+    expect("fwd misaligned",
+           la_chunk_fwd((char *)A(0) + 8, A(1), A(2), F(3), F(4), A(5), F(6), F(7), 4, 128, 64, 64, LA_BF16, 0),
+           LA_ERR_ALIGN, 0);
+    expect("fwd S_out == S_in", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(3), F(7), 4, 128, 64, 64, LA_BF16, 0),
+           LA_ERR_ALIAS, 0);
+    expect("fwd overflow",
+           la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 0x7fffffff, 0x7fffffff, 128, 64, LA_BF16, 0),
+           LA_ERR_INVALID, 0);
+
+    // ---- la_chunk_bwd
+    expect("bwd headline",
+           la_chunk_bwd(A(0), A(1), A(2), F(3), F(4), A(5), nullptr, nullptr, A(8), A(9), A(10), F(11), F(12), 160, 128,
+                        64, 64, LA_BF16, 0),
+           LA_OK, L_BWD_C128);
+    expect("bwd d128 upstream",
+           la_chunk_bwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), A(8), A(9), A(10), F(11), F(12), 160, 100, 128,
+                        64, LA_BF16, 0),
+           LA_OK, L_BWD);
+    expect("bwd C > max",
+           la_chunk_bwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), A(8), A(9), A(10), F(11), F(12), 4,
+                        LA_BWD_MAX_C + 1, 64, 64, LA_BF16, 0),
+           LA_ERR_UNSUPPORTED, 0);
+    expect("bwd dq == dO",
+           la_chunk_bwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), A(5), A(9), A(10), F(11), F(12), 4, 128, 64, 64,
+                        LA_BF16, 0),
+           LA_ERR_ALIAS, 0);
+    expect("bwd half upstream",
+           la_chunk_bwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), nullptr, A(8), A(9), A(10), F(11), F(12), 4, 128, 64,
+                        64, LA_BF16, 0),
+           LA_ERR_INVALID, 0);
+
+    // ---- sequence calls
+    expect("seq fwd d64",
+           la_seq_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), F(8), F(9), 1280, 1024, 64, 128, 64,
+                      LA_FEATURE_NONE, LA_BF16, 0),
+           LA_OK, L_SEQ_FWD_C128);
+    expect("seq fwd d128 ragged elu1",
+           la_seq_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), nullptr, nullptr, 160, 8164, 128, 128, 64,
+                      LA_FEATURE_ELU1, LA_BF16, 0),
+           LA_OK, L_SEQ_FWD_D128);
+    expect("seq fwd d64 partial chunk",
+           la_seq_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), F(8), F(9), 4, 500, 64, 128, 64, LA_FEATURE_NONE,
+                      LA_BF16, 0),
+           LA_ERR_UNSUPPORTED, 0);
+    expect("seq fwd bad feature",
+           la_seq_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), F(8), F(9), 4, 512, 64, 128, 64, (la_feature)5,
+                      LA_BF16, 0),
+           LA_ERR_INVALID, 0);
+    expect("seq bwd d64",
+           la_seq_bwd(A(0), A(1), A(2), F(3), F(4), F(5), F(6), A(7), nullptr, nullptr, A(10), A(11), A(12), F(13),
+                      F(14), 1280, 1024, 64, 128, 64, LA_FEATURE_NONE, LA_BF16, 0),
+           LA_OK, L_SEQ_BWD_C128);
+    expect("seq bwd d128",
+           la_seq_bwd(A(0), A(1), A(2), F(3), F(4), nullptr, nullptr, A(7), F(8), F(9), A(10), A(11), A(12), F(13),
+                      F(14), 160, 8164, 128, 128, 64, LA_FEATURE_NONE, LA_BF16, 0),
+           LA_OK, L_SEQ_BWD_D128);
+    expect("seq bwd no final carry",
+           la_seq_bwd(A(0), A(1), A(2), nullptr, F(4), nullptr, nullptr, A(7), nullptr, nullptr, A(10), A(11), A(12),
+                      F(13), F(14), 4, 512, 64, 128, 64, LA_FEATURE_NONE, LA_BF16, 0),
+           LA_ERR_INVALID, 0);
+
+    // ---- cross-entropy
+    const size_t fws = la_ce_fwd_workspace_bytes(512, 1280, 50257);
+    const size_t bws = la_ce_workspace_bytes(512, 1280, 50257, 128);
+    if (fws == 0 || bws < fws) {
+        printf("FAIL workspace sizes %zu %zu\n", fws, bws);
+        ++failures;
+    }
+    expect("ce fwd", la_ce_fwd(A(0), A(1), (const int *)A(2), F(3), F(4), A(5), fws, 512, 1280, 50257, LA_BF16, 0),
+           LA_OK, L_CE_FWD);
+    expect("ce fwd small ws",
+           la_ce_fwd(A(0), A(1), (const int *)A(2), F(3), F(4), A(5), fws - 1, 512, 1280, 50257, LA_BF16, 0),
+           LA_ERR_INVALID, 0);
+    expect("ce bwd chunked",
+           la_ce_bwd(A(0), A(1), (const int *)A(2), F(3), nullptr, A(5), F(6), A(7), bws, 512, 1280, 50257, 128,
+                     LA_BF16, 0),
+           LA_OK, L_CE_BWD);
+    expect("ce bwd d=100",
+           la_ce_bwd(A(0), A(1), (const int *)A(2), F(3), nullptr, A(5), F(6), A(7), bws, 512, 100, 50257, 128,
+                     LA_BF16, 0),
+           LA_ERR_UNSUPPORTED, 0);
+
+    // ---- the rest of the boundary
+    for (int s = -1; s <= 6; ++s)
+        if (la_status_str((la_status)s) == nullptr) {
+            printf("FAIL la_status_str(%d) is NULL\n", s);
+            ++failures;
+        }
+    if (la_abi_version() != LA_ABI_VERSION) {
+        printf("FAIL la_abi_version\n");
+        ++failures;
+    }
+    if (la_time_next_launch(A(0), nullptr) != LA_ERR_INVALID || la_time_next_launch(nullptr, nullptr) != LA_OK) {
+        printf("FAIL la_time_next_launch\n");
+        ++failures;
+    }
+    if (!la_kernel_name(1, LA_BF16, 128, 64) || la_kernel_name(1, LA_F32, 128, 96) ||
+        !la_seq_kernel_name(0, LA_BF16, 128, 128, LA_FEATURE_ELU1))
+        ++failures;
+
+    printf("%s: %d failures\n", failures ? "FAILED" : "ok", failures);
+    return failures ? 1 : 0;
+}

@@ -32,7 +32,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["la_abi_version", "la_ce_bwd", "la_ce_fwd", "la_ce_workspace_bytes",
+    assert declared_functions() == ["la_abi_version", "la_ce_bwd", "la_ce_fwd", "la_ce_fwd_workspace_bytes",
+                                    "la_ce_workspace_bytes",
                                     "la_chunk_bwd", "la_chunk_fwd", "la_kernel_name",
                                     "la_seq_bwd", "la_seq_fwd", "la_seq_kernel_name", "la_status_str",
                                     "la_time_next_launch"]
@@ -62,7 +63,7 @@ def test_sequence_limits_match_the_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lac.abi_version() == 4
+    assert lac.abi_version() == 5
     for s in range(6):
         assert len(lac.status_str(s)) > 0
     assert lac.status_str(99) == "unknown status"
@@ -254,6 +255,26 @@ def test_ce_workspace_sizes(lib):
     # the backward's P of one chunk (bf16, padded to 128 x 128 tiles) and the dh partial sums
     assert full >= 512 * 50304 * 2 and chunked >= 128 * 50304 * 2 and chunked < full
     assert lac.ce_workspace_bytes(512, 100, 50257) == 0  # d not a multiple of 128
+    # the forward needs its partial sums only: (V / 256 class tiles + 1) x N_pad x 8 bytes, the
+    # same whatever the backward's chunk
+    assert lac.ce_fwd_workspace_bytes(512, 1280, 50257) == (197 + 1) * 512 * 8
+    assert lac.ce_fwd_workspace_bytes(512, 1280, 50257) < chunked
+
+
+def test_ce_fwd_takes_shapes_whose_whole_p_would_not_fit(lib):
+    # N x V_pad >= 2^30: the backward must chunk (a whole-N P is beyond 32-bit offsets), the
+    # forward never forms P and takes the shape with its own small workspace
+    N, d, V = 30000, 128, 50257
+    fwd_ws = lac.ce_fwd_workspace_bytes(N, d, V)
+    assert fwd_ws == (197 + 1) * 30080 * 8
+    assert lac.ce_workspace_bytes(N, d, V) == 0
+    assert lac.ce_workspace_bytes(N, d, V, 1024) > fwd_ws
+    assert ce_fwd_call(lib, N=N, d=d, V=V, ws_bytes=fwd_ws - 1) == INVALID
+    # with enough workspace every check before the overlap check passes (the workspace here
+    # is placed on W, so the call stops there, before any launch)
+    assert ce_fwd_call(lib, N=N, d=d, V=V, ws_bytes=fwd_ws, ws=addr(1)) == ALIAS
+    assert ce_bwd_call(lib, N=N, d=d, V=V, chunk=0, ws_bytes=CE_WS) == UNSUPPORTED
+    assert ce_bwd_call(lib, N=N, d=d, V=V, chunk=1024, ws_bytes=CE_WS, ws=addr(1)) == ALIAS
 
 
 def test_time_next_launch_pairs(lib):
