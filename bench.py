@@ -10,8 +10,12 @@ forward and one backward launch; `--workload` names the chained ones.  Steps
 rotate over enough buffer sets (>= 640 MB) that the 256 MB last-level cache
 cannot serve the traffic.  Two timed regions, each bracketed by device
 synchronisation:
-  1. K plain steps in five consecutive runs: the median run's time per step gives `value`
-     and `ms_per_step`;
+  1. K steps in up to five consecutive runs of at least 40 steps, each run replayed from one
+     HIP graph of its steps (kernel nodes only; `--no-graph` to skip): the median run's time
+     per step gives `value` and `ms_per_step`.  The same K steps as plain
+     library calls from Python are timed too (`config.plain_loop_*`): there the host's launch
+     rate, not the device, can set the pace.  Before timing, replays of one set's graph are
+     checked bit for bit against an eager step (`config.graph_replays_match_eager`);
   2. K more steps in which every launch carries a pair of HIP events recorded
      on its kernel dispatch (la_time_next_launch): the per-kernel durations
      behind the roofline.  Those events cost host time per launch, which is why
@@ -20,6 +24,8 @@ Then, for context only: K steps on a single buffer set (its inputs warm in the c
 `config.warm_single_set_ms_per_step`) and a 1 GiB device copy (`roofline.copy_GBs_measured`,
 the practical ceiling beside the 8 TB/s peak).  Prints one JSON line.
 
+    python bench.py --floors             # launch floors: empty and streaming kernels (no arithmetic)
+                                         # of the headline launches' sizes, timed the same ways
     python bench.py --copy-calibration   # one plain device copy of known size, for counter scaling
     python bench.py --counters-summary DIR
         # HBM bytes per launch of each kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
@@ -89,7 +95,7 @@ def kernel_source_hash():
     import glob
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "causal_linear_attention_chunked_amd", "csrc", "*"))):
-        if os.path.basename(f) == "la_ce.hip":
+        if os.path.basename(f) in ("la_ce.hip", "la_floor.hip"):
             continue
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
@@ -243,21 +249,84 @@ def copy_calibration(torch, mib=256, reps=5):
 def timed_runs(torch, fn, K):
     """K calls of fn() in up to five consecutive runs bracketed by device events: the per-call
     times of the runs, sorted, and the host seconds spent enqueuing."""
-    R = min(5, K)
-    sizes = [K // R + (1 if r < K % R else 0) for r in range(R)]
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R)]
+    per_run, host_s, _ = timed_block_runs(torch, lambda i0, n: [fn(i) for i in range(i0, i0 + n)], K)
+    return per_run, host_s
+
+
+def run_sizes(K, runs=5, min_steps=0):
+    """Steps of each of up to `runs` consecutive timed runs (at least `min_steps` each where K allows)."""
+    R = max(1, min(runs, K, K // min_steps if min_steps else K))
+    return [K // R + (1 if r < K % R else 0) for r in range(R)]
+
+
+def timed_block_runs(torch, run, K, sizes=None):
+    """K steps in consecutive runs of `sizes` steps (default: up to five) bracketed by device
+    events (synchronised before and after), `run(i0, n)` enqueuing steps i0 .. i0 + n - 1: the
+    per-step times of the runs in ms, sorted, the host seconds spent enqueuing, and the total
+    device ms."""
+    sizes = sizes or run_sizes(K)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sizes]
     torch.cuda.synchronize()
     h0 = time.perf_counter()
     i = 0
     for (a, b), nsteps in zip(evs, sizes):
         a.record()
-        for _ in range(nsteps):
-            fn(i)
-            i += 1
+        run(i, nsteps)
+        i += nsteps
         b.record()
     host_s = time.perf_counter() - h0
     torch.cuda.synchronize()
-    return sorted(a.elapsed_time(b) / nsteps for (a, b), nsteps in zip(evs, sizes)), host_s
+    total = sum(a.elapsed_time(b) for a, b in evs)
+    return sorted(a.elapsed_time(b) / nsteps for (a, b), nsteps in zip(evs, sizes)), host_s, total
+
+
+GRAPH_MIN_STEPS = 40  # steps per captured run: one replay's launch cost spread over at least these
+
+
+def graph_matches_eager(torch, step, sets, outputs_of, replays=3):
+    """Whether replays of a graph of one step on the first set give the bits of an eager step: the
+    outputs are poisoned with NaN (eager work) before every replay and compared after it."""
+    s = sets[0]
+    step(s)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outputs_of(s)]
+    g = RunGraphs(torch, lambda j: step(sets[j]), len(sets), [1])
+    for _ in range(replays):
+        for t in outputs_of(s):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.run(0, 1)
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(ref, outputs_of(s))):
+            return False
+    return True
+
+
+class RunGraphs:
+    """The timed runs of a benchmark captured in HIP graphs, one graph per run (kernel nodes only:
+    the library's calls record no memset or copy), so that each run is one host call and the
+    device, not the host's launch rate, sets the pace.  Run r's graph holds its steps i0 .. i0 +
+    n - 1 on the buffer sets i mod nsets, the order of the plain loop.  One graph per run because a
+    replay has a fixed cost of its own (over 10 us on this platform, measured): replaying a graph
+    per step would add it to every step."""
+
+    def __init__(self, torch, step_on_set, nsets, sizes):
+        self.graphs = {}
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        i0 = 0
+        for n in sizes:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(i0, i0 + n):
+                    step_on_set(i % nsets)
+            self.graphs[(i0, n)] = g
+            i0 += n
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+
+    def run(self, i0, n):
+        self.graphs[(i0, n)].replay()
 
 
 def bench_ce(args, w, torch, lac, inp):
@@ -338,6 +407,55 @@ def bench_ce(args, w, torch, lac, inp):
     print(json.dumps(out), flush=True)
 
 
+def bench_floors(args, torch, lac, nwg=160):
+    """Launch floors at the headline launches' sizes: an empty kernel, and streaming kernels (no
+    arithmetic, every load issued up front) moving the forward's and the backward's bytes in
+    `nwg` workgroups, on buffers rotated over the same footprint as the benchmark.  Each is timed
+    as the attention kernels are: back to back from Python, replayed from HIP graphs, and one
+    launch at a time between dispatch-bound events; and the two streaming kernels back to back
+    as a step, the floor of a step of the two attention launches."""
+    ib, ob = 81920 * nwg, 65536 * nwg  # the larger (backward) shape's bytes; the forward uses less
+    nsets = max(2, math.ceil(args.footprint_mb * 1e6 / (ib + ob)))
+    dev = "cuda:0"
+    sets = [(torch.empty(ib, dtype=torch.uint8, device=dev).fill_(1), torch.empty(ob, dtype=torch.uint8, device=dev))
+            for _ in range(nsets)]
+    algo = {"empty": 0, "fwd": (65536 + 32768) * nwg, "bwd": (81920 + 65536) * nwg}
+    K = args.steps
+    out = {"floors": {}, "nwg": nwg, "threads": 512, "buffer_sets": nsets,
+           "footprint_mb": round(nsets * (ib + ob) / 1e6, 1), "steps": K,
+           "kernels": {k: lac.FLOOR_NAMES[lac.FLOOR_KINDS[k]] for k in lac.FLOOR_KINDS}}
+    cases = [("empty", ["empty"]), ("fwd", ["fwd"]), ("bwd", ["bwd"]), ("fwd+bwd step", ["fwd", "bwd"])]
+    for label, kinds in cases:
+        def step_on(j, kinds=kinds):
+            for kd in kinds:
+                lac.floor_launch(kd, nwg, sets[j][0], sets[j][1])
+        for i in range(args.warmup):
+            step_on(i % nsets)
+        plain, _, _ = timed_block_runs(torch, lambda i0, n: [step_on(i % nsets) for i in range(i0, i0 + n)], K)
+        sizes = run_sizes(K, min_steps=GRAPH_MIN_STEPS)
+        graphs = RunGraphs(torch, step_on, nsets, sizes)
+        for i0, n in graphs.graphs:  # first replays (graph upload) untimed
+            graphs.run(i0, n)
+        graph, _, _ = timed_block_runs(torch, graphs.run, K, sizes)
+        r = {"plain_us": plain[len(plain) // 2] * 1e3, "graph_us": graph[len(graph) // 2] * 1e3}
+        if len(kinds) == 1:
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+            torch.cuda.synchronize()
+            for i, (a, b) in enumerate(ev):
+                lac.time_next_launch(a, b)
+                step_on(i % nsets)
+            torch.cuda.synchronize()
+            d = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+            r.update({"dispatch_events_avg_us": sum(d) / K, "dispatch_events_median_us": d[K // 2],
+                      "bytes": algo[kinds[0]]})
+        else:
+            r["bytes"] = algo["fwd"] + algo["bwd"]
+        if r["bytes"]:
+            r["graph_frac_of_8TBs"] = r["bytes"] / (r["graph_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
+        out["floors"][label] = r
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline_ce(I, w, min_seconds=10.0):
     """The fp64 oracle of the cross-entropy (numpy, its BLAS on every host thread), forward and
     backward over the full workload, repeated; and once on one BLAS thread."""
@@ -379,6 +497,10 @@ def main():
     ap.add_argument("--feature", choices=["elu1"], default=None,
                     help="with --seq: raw q, k in, the feature map elu(x)+1 fused into the kernels")
     ap.add_argument("--footprint-mb", type=float, default=640.0)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the plain loop of library calls only (no HIP graph capture)")
+    ap.add_argument("--floors", action="store_true",
+                    help="time the launch-floor kernels (no arithmetic) of the headline launches' sizes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only plain 256 MiB device-to-device copies (HBM counter calibration)")
     ap.add_argument("--counters-summary", metavar="DIR",
@@ -408,6 +530,8 @@ def main():
     from causal_linear_attention_chunked_amd import inputs as inp
 
     lac.load_library()
+    if args.floors:
+        return bench_floors(args, torch, lac)
     if args.workload in inp.CE_WORKLOADS:
         return bench_ce(args, inp.ce_workload(args.workload), torch, lac, inp)
     w = inp.workload(args.workload)
@@ -493,30 +617,38 @@ def main():
         for kind, _, _, i in launches:
             launch(s, kind, i)
 
+    def outputs_of(s):
+        if args.seq:
+            return [t for t in (*s["seq"]["fout"], *s["seq"]["bout"]) if t is not None]
+        return [t for c in s["chunks"] for t in (*c["fout"], *c["bout"])]
+
     for i in range(args.warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
 
     K = args.steps
-    # region 1: plain steps, K in all, timed in up to five consecutive runs (the median run's
-    # per-step time is the result; the mean over all K is reported beside it)
-    R = min(5, K)
-    sizes = [K // R + (1 if r < K % R else 0) for r in range(R)]
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R)]
-    torch.cuda.synchronize()
-    h0 = time.perf_counter()
-    i = 0
-    for (a, b), nsteps in zip(evs, sizes):
-        a.record()
-        for _ in range(nsteps):
-            step(sets[i % nsets])
-            i += 1
-        b.record()
-    host_s = time.perf_counter() - h0
-    torch.cuda.synchronize()
-    per_run = sorted(a.elapsed_time(b) / nsteps for (a, b), nsteps in zip(evs, sizes))
+    # region 1: K steps in up to five consecutive runs (the median run's per-step time is the
+    # result; the mean over all K is reported beside it), replayed from HIP graphs so that the
+    # device, not the host's launch rate, sets the pace; the same K steps as plain library calls
+    # from Python are timed beside them
+    plain_runs, plain_host_s, plain_total = timed_block_runs(
+        torch, lambda i0, nst: [step(sets[i % nsets]) for i in range(i0, i0 + nst)], K)
+    graphs, graph_error, graph_check = None, None, None
+    sizes = run_sizes(K, min_steps=GRAPH_MIN_STEPS)
+    if not args.no_graph:
+        try:
+            graph_check = graph_matches_eager(torch, step, sets, outputs_of)
+            graphs = RunGraphs(torch, lambda j: step(sets[j]), nsets, sizes)
+            for i0, nst in graphs.graphs:  # first replays (graph upload) untimed
+                graphs.run(i0, nst)
+        except Exception as e:  # reported; the plain loop then gives the result
+            graphs, graph_error = None, repr(e)
+    if graphs is not None:
+        per_run, host_s, total_ms = timed_block_runs(torch, graphs.run, K, sizes)
+    else:
+        per_run, host_s, total_ms = plain_runs, plain_host_s, plain_total
     ms_per_step = per_run[len(per_run) // 2]
-    ms_per_step_mean = sum(a.elapsed_time(b) for a, b in evs) / K
+    ms_per_step_mean = total_ms / K
     value = G * w.T / (ms_per_step / 1e3)
 
     # region 2: the same steps with dispatch-bound events on every launch
@@ -572,10 +704,15 @@ def main():
                    "block": w.block, "carry": w.carry, "launches_per_step": len(launches),
                    "buffer_sets": nsets, "footprint_mb": round(nsets * set_bytes / 1e6, 1),
                    "entry_points": "la_seq_fwd/la_seq_bwd" if args.seq else "la_chunk_fwd/la_chunk_bwd",
-                   "timed_runs": R, "ms_per_step_runs": per_run, "ms_per_step_mean": ms_per_step_mean,
+                   "timed_runs": len(per_run), "ms_per_step_runs": per_run, "ms_per_step_mean": ms_per_step_mean,
                    "warm_single_set_ms_per_step": warm_ms,
                    "feature_map": args.feature or "applied by the caller",
-                   "graph_captured": False, "host_enqueue_us_per_step": host_s * 1e6 / K,
+                   "graph_captured": graphs is not None, "graph_error": graph_error,
+                   "graph_replays_match_eager": graph_check,
+                   "host_enqueue_us_per_step": host_s * 1e6 / K,
+                   "plain_loop_ms_per_step": plain_runs[len(plain_runs) // 2],
+                   "plain_loop_ms_per_step_runs": plain_runs,
+                   "plain_loop_host_enqueue_us_per_step": plain_host_s * 1e6 / K,
                    "kernel_timing": "HIP events recorded on each kernel dispatch, separate timed loop"},
         "roofline": {"bound": "hbm", "kernel": top, "achieved": kt["GB/s"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kt["frac"], "traffic": kt["traffic"],

@@ -88,6 +88,8 @@ def load_library():
         lib.la_ce_bwd.argtypes = [vp] * 8 + [ctypes.c_size_t] + [i] * 5 + [vp]
         lib.la_seq_kernel_name.restype = ctypes.c_char_p
         lib.la_seq_kernel_name.argtypes = [i, i, i, i, i]
+        lib.la_floor_launch.restype = i
+        lib.la_floor_launch.argtypes = [i, i, vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
         _lib = lib
         return lib
 
@@ -446,6 +448,24 @@ def ce_bwd(h, W, targets, lse, dloss=None, ce_chunk: int = 0, workspace=None, ou
                                       dh.data_ptr(), dW.data_ptr(), ws.data_ptr(), nbytes, N, d, V, int(ce_chunk),
                                       LA_BF16, _stream(dev)))
     return dh, dW
+
+
+FLOOR_KINDS = {"empty": 0, "fwd": 1, "bwd": 2}
+FLOOR_NAMES = {0: "la_floor_empty_kernel", 1: "la_floor_stream_kernel<8, 4>", 2: "la_floor_stream_kernel<10, 8>"}
+
+
+def floor_launch(kind: str, nwg: int, inp, out):
+    """Measurement aid: one launch-floor kernel (no arithmetic) of ``nwg`` workgroups on the
+    current stream.  kind "empty", or "fwd" / "bwd": every workgroup reads 65536 / 81920 bytes of
+    ``inp`` and writes 32768 / 65536 bytes of ``out`` (contiguous CUDA tensors, any dtype)."""
+    lib = _lib or load_library()
+    if kind not in FLOOR_KINDS:
+        raise ValueError(f"unknown floor kind {kind!r}; use one of {sorted(FLOOR_KINDS)}")
+    if not out.is_cuda or not out.is_contiguous() or (inp is not None and (not inp.is_cuda or not inp.is_contiguous())):
+        raise ValueError("floor buffers must be contiguous CUDA tensors")
+    nb = lambda t: 0 if t is None else t.numel() * t.element_size()
+    _check("la_floor_launch", lib.la_floor_launch(FLOOR_KINDS[kind], int(nwg), _ptr(inp), nb(inp), out.data_ptr(),
+                                                  nb(out), _stream(out.get_device())))
 
 
 def chain_fwd(q_chunks, k_chunks, v_chunks, S_in=None, z_in=None, block: int = 64):

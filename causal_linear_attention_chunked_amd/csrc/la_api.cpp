@@ -325,6 +325,22 @@ const char *la_seq_kernel_name(int backward, la_dtype dt, int chunk, int D, la_f
     return backward ? "la_seq_bwd_c128w16_kernel" : "la_seq_fwd_c128_kernel";
 }
 
+la_status la_floor_launch(int kind, int nwg, const void *in, size_t in_bytes, void *out, size_t out_bytes,
+                          void *stream) {
+    const TakenEvents te;
+    if (kind < 0 || kind > 2 || nwg < 1) return LA_ERR_INVALID;
+    int nin, nout;
+    lachunk::floor_shape(kind, &nin, &nout);
+    const size_t per_in = (size_t)nin * lachunk::FLOOR_THREADS * 16, per_out = (size_t)nout * lachunk::FLOOR_THREADS * 16;
+    // the empty kernel's only pointer is never written, but must be a device buffer of 4 bytes per thread
+    const size_t need_out = kind == 0 ? (size_t)lachunk::FLOOR_THREADS * 4 : (size_t)nwg * per_out;
+    if (!out || out_bytes < need_out || (kind != 0 && (!in || in_bytes < (size_t)nwg * per_in))) return LA_ERR_INVALID;
+    if (!aligned16(in) || !aligned16(out)) return LA_ERR_ALIGN;
+    if (kind != 0 && overlap(span(in, (size_t)nwg * per_in), span(out, need_out))) return LA_ERR_ALIAS;
+    const hipError_t e = lachunk::launch_floor(kind, nwg, in, out, reinterpret_cast<hipStream_t>(stream), te.ev);
+    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
+
 la_status la_time_next_launch(void *start_event, void *stop_event) {
     if ((start_event == nullptr) != (stop_event == nullptr)) return LA_ERR_INVALID;
     pending_ev[0] = reinterpret_cast<hipEvent_t>(start_event);

@@ -270,6 +270,23 @@ const char *la_kernel_name(int backward, la_dtype dt, int C, int D);
 /* The same for la_seq_fwd (backward = 0) and la_seq_bwd (backward = 1) at this chunk length. */
 const char *la_seq_kernel_name(int backward, la_dtype dt, int chunk, int D, la_feature feature);
 
+/*
+ * Measurement aid: launch floors, kernels that do no arithmetic, for measuring what one launch
+ * of a given size costs apart from any computation (nothing else in the library calls them).
+ *   kind 0: an empty kernel of nwg workgroups; out must hold 512 * 4 bytes (never written),
+ *           in is ignored;
+ *   kind 1: nwg workgroups of 512 threads, each reading 65536 bytes of `in` (8 loads of 16 bytes
+ *           per thread, all issued before the first is used) and writing 32768 bytes of `out`
+ *           (non-temporal stores): at nwg = 160 the forward's bytes at the headline shape
+ *           (160 groups, one 128-token chunk, D = 64, bf16: 10.5 MB read, 5.3 MB written);
+ *   kind 2: the same with 81920 bytes read and 65536 written per workgroup: the backward's
+ *           (13.2 MB read, 10.5 MB written at nwg = 160).
+ * in_bytes, out_bytes: the sizes of the device buffers, which must hold those counts times nwg
+ * (LA_ERR_INVALID otherwise); 16-byte aligned; not overlapping.  la_time_next_launch applies.
+ */
+la_status la_floor_launch(int kind, int nwg, const void *in, size_t in_bytes, void *out, size_t out_bytes,
+                          void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,7 +11,7 @@
 extern int g_last_launch;
 enum {
     L_NONE = 0, L_FWD, L_BWD, L_FWD_C128, L_BWD_C128, L_SEQ_FWD_C128, L_SEQ_BWD_C128, L_SEQ_FWD_D128,
-    L_SEQ_BWD_D128, L_CE_FWD, L_CE_BWD, L_CE_FWD_NOALLOC
+    L_SEQ_BWD_D128, L_CE_FWD, L_CE_BWD, L_CE_FWD_NOALLOC, L_FLOOR
 };
 
 static int failures = 0;
@@ -124,6 +124,15 @@ int main() {
            la_ce_bwd(A(0), A(1), (const int *)A(2), F(3), nullptr, A(5), F(6), A(7), bws, 512, 100, 50257, 128,
                      LA_BF16, 0),
            LA_ERR_UNSUPPORTED, 0);
+
+    // ---- launch floors
+    expect("floor empty", la_floor_launch(0, 160, nullptr, 0, A(1), 2048, 0), LA_OK, L_FLOOR);
+    expect("floor fwd", la_floor_launch(1, 160, A(0), 160 * 65536, A(1), 160 * 32768, 0), LA_OK, L_FLOOR);
+    expect("floor bwd small out", la_floor_launch(2, 160, A(0), 160 * 81920, A(1), 160 * 65536 - 1, 0),
+           LA_ERR_INVALID, 0);
+    expect("floor bad kind", la_floor_launch(3, 160, A(0), 1 << 30, A(1), 1 << 30, 0), LA_ERR_INVALID, 0);
+    expect("floor overlap", la_floor_launch(1, 160, A(0), 160 * 65536, (char *)A(0) + 4096, 160 * 32768, 0),
+           LA_ERR_ALIAS, 0);
 
     // ---- the rest of the boundary
     for (int s = -1; s <= 6; ++s)

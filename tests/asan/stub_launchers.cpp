@@ -12,7 +12,7 @@ namespace lachunk {
 
 enum : int {
     L_FWD = 1, L_BWD, L_FWD_C128, L_BWD_C128, L_SEQ_FWD_C128, L_SEQ_BWD_C128, L_SEQ_FWD_D128, L_SEQ_BWD_D128,
-    L_CE_FWD, L_CE_BWD, L_CE_FWD_NOALLOC
+    L_CE_FWD, L_CE_BWD, L_CE_FWD_NOALLOC, L_FLOOR
 };
 
 static hipError_t hit(int id) {
@@ -87,5 +87,7 @@ hipError_t launch_ce_bwd(const void *, const void *, const int *, const float *,
                          void *, int, int, int, int, hipStream_t, const hipEvent_t *) {
     return hit(L_CE_BWD);
 }
+
+hipError_t launch_floor(int, int, const void *, void *, hipStream_t, const hipEvent_t *) { return hit(L_FLOOR); }
 
 }  // namespace lachunk

@@ -34,7 +34,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["la_abi_version", "la_ce_bwd", "la_ce_fwd", "la_ce_fwd_workspace_bytes",
                                     "la_ce_workspace_bytes",
-                                    "la_chunk_bwd", "la_chunk_fwd", "la_kernel_name",
+                                    "la_chunk_bwd", "la_chunk_fwd", "la_floor_launch", "la_kernel_name",
                                     "la_seq_bwd", "la_seq_fwd", "la_seq_kernel_name", "la_status_str",
                                     "la_time_next_launch"]
 
