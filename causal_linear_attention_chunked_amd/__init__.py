@@ -88,6 +88,8 @@ def load_library():
         lib.la_ce_bwd.argtypes = [vp] * 8 + [ctypes.c_size_t] + [i] * 5 + [vp]
         lib.la_seq_kernel_name.restype = ctypes.c_char_p
         lib.la_seq_kernel_name.argtypes = [i, i, i, i, i]
+        lib.la_ce_fwd_noalloc.restype = i
+        lib.la_ce_fwd_noalloc.argtypes = [vp] * 5 + [i] * 4 + [vp]
         lib.la_floor_launch.restype = i
         lib.la_floor_launch.argtypes = [i, i, vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
         _lib = lib
@@ -418,6 +420,29 @@ def ce_fwd(h, W, targets, workspace=None, out=None):
         _ce_f32("lse", lse, (N,), dev)
     _check("la_ce_fwd", lib.la_ce_fwd(h.data_ptr(), W.data_ptr(), targets.data_ptr(), loss.data_ptr(),
                                       lse.data_ptr(), ws.data_ptr(), nbytes, N, d, V, LA_BF16, _stream(dev)))
+    return loss, lse
+
+
+CE_NOALLOC_SCRATCH_BYTES = 8 << 20  # LA_CE_NOALLOC_SCRATCH_BYTES
+
+
+def ce_fwd_noalloc(h, W, targets, out):
+    """ce_fwd for callers that cannot allocate: the library's own static per-device scratch is the
+    workspace, and the caller passes the outputs ``out = (loss, lse)``; nothing is allocated.
+    Calls that overlap on one device race on that scratch.  Shapes whose forward workspace
+    exceeds CE_NOALLOC_SCRATCH_BYTES raise (LA_ERR_UNSUPPORTED)."""
+    lib = _lib or load_library()
+    N, d, V, dev = _ce_check(h, W, targets)
+    loss, lse = out
+    _ce_f32("loss", loss, (), dev)
+    _ce_f32("lse", lse, (N,), dev)
+    st = lib.la_ce_fwd_noalloc(h.data_ptr(), W.data_ptr(), targets.data_ptr(), loss.data_ptr(), lse.data_ptr(),
+                               N, d, V, LA_BF16, _stream(dev))
+    if st == 2 and ce_fwd_workspace_bytes(N, d, V) > CE_NOALLOC_SCRATCH_BYTES:
+        raise LachunkError("la_ce_fwd_noalloc", st,
+                           f"{status_str(st)}: its workspace of {ce_fwd_workspace_bytes(N, d, V)} bytes exceeds the "
+                           f"library's scratch of {CE_NOALLOC_SCRATCH_BYTES}")
+    _check("la_ce_fwd_noalloc", st)
     return loss, lse
 
 

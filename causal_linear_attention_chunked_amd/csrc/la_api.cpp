@@ -9,6 +9,8 @@
 #include "../../include/la_chunk.h"
 #include "la_launch.h"
 
+static_assert(LA_CE_NOALLOC_SCRATCH_BYTES == lachunk::CE_SCRATCH_BYTES, "the header states the scratch size");
+
 namespace {
 
 struct Span {
@@ -266,6 +268,26 @@ la_status la_ce_fwd(const void *h, const void *W, const int *targets, float *los
     if (st != LA_OK) return st;
     const hipError_t e = lachunk::launch_ce_fwd(h, W, targets, loss, lse, workspace, N, d, V,
                                                 reinterpret_cast<hipStream_t>(stream), te.ev);
+    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
+
+la_status la_ce_fwd_noalloc(const void *h, const void *W, const int *targets, float *loss, float *lse, int N, int d,
+                            int V, la_dtype dt, void *stream) {
+    const TakenEvents te;
+    lachunk::CeShape s;
+    la_status st = ce_fwd_checks(N, d, V, dt, &s);
+    if (st != LA_OK) return st;
+    if (s.fwd_bytes > LA_CE_NOALLOC_SCRATCH_BYTES) return LA_ERR_UNSUPPORTED;
+    if (!h || !W || !targets || !loss || !lse) return LA_ERR_INVALID;
+    const void *ptrs[] = {h, W, targets, loss, lse};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return LA_ERR_ALIGN;
+    const Span in[] = {span(h, (size_t)N * d * 2), span(W, (size_t)V * d * 2), span(targets, (size_t)N * 4)};
+    const Span out[] = {span(loss, 4), span(lse, (size_t)N * 4)};
+    st = alias_checks(in, 3, out, 2);
+    if (st != LA_OK) return st;
+    const hipError_t e = lachunk::launch_ce_fwd_noalloc(h, W, targets, loss, lse, N, d, V,
+                                                        reinterpret_cast<hipStream_t>(stream), te.ev);
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 

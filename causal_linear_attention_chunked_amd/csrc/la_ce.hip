@@ -499,6 +499,32 @@ hipError_t launch_ce_fwd(const void *h, const void *W, const int *targets, float
     return hipGetLastError();
 }
 
+// The forward's workspace for callers that cannot allocate one: one copy of this array per
+// device the library runs on, held until the process ends, shared by every such call on that
+// device (calls that overlap on one device race on it).  Its name in host code is a host-side
+// stand-in, not a device address: the host uses only the address hipGetSymbolAddress gives for
+// the current device, looked up once per device and kept.  The forward overwrites every byte of
+// the workspace it reads, so nothing needs clearing between calls.
+static __device__ __align__(256) char scratch[CE_SCRATCH_BYTES];
+constexpr int SCRATCH_MAX_DEVICES = 64;
+static std::atomic<void *> scratch_ptr[SCRATCH_MAX_DEVICES];
+
+hipError_t launch_ce_fwd_noalloc(const void *h, const void *W, const int *targets, float *loss, float *lse, int N,
+                                 int d, int V, hipStream_t stream, const hipEvent_t ev[2]) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+    void *p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {  // first call on this device (threads that race here store the same address)
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return launch_ce_fwd(h, W, targets, loss, lse, p, N, d, V, stream, ev);
+}
+
 hipError_t launch_ce_bwd(const void *h, const void *W, const int *targets, const float *lse, const float *dloss,
                          void *dh, float *dW, void *ws, int N, int d, int V, int ce_chunk, hipStream_t stream,
                          const hipEvent_t ev[2]) {

@@ -82,6 +82,11 @@ inline CeShape ce_shape(int N, int d, int V, int ce_chunk) {
 }
 hipError_t launch_ce_fwd(const void *h, const void *W, const int *targets, float *loss, float *lse, void *ws, int N,
                          int d, int V, hipStream_t stream, const hipEvent_t ev[2]);
+// The same forward with the library's own per-device scratch array (CE_SCRATCH_BYTES, a static
+// device array) as its workspace: nothing is allocated by the library or the caller.
+constexpr size_t CE_SCRATCH_BYTES = (size_t)8 << 20;
+hipError_t launch_ce_fwd_noalloc(const void *h, const void *W, const int *targets, float *loss, float *lse, int N,
+                                 int d, int V, hipStream_t stream, const hipEvent_t ev[2]);
 hipError_t launch_ce_bwd(const void *h, const void *W, const int *targets, const float *lse, const float *dloss,
                          void *dh, float *dW, void *ws, int N, int d, int V, int ce_chunk, hipStream_t stream,
                          const hipEvent_t ev[2]);

@@ -238,6 +238,26 @@ la_status la_ce_bwd(const void *h, const void *W, const int *targets, const floa
                     void *dh, float *dW, void *workspace, size_t workspace_bytes,
                     int N, int d, int V, int ce_chunk, la_dtype dt, void *stream);
 
+/*
+ * la_ce_fwd for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same forward, same kernels and results,
+ * but the workspace is the library's own static device array of LA_CE_NOALLOC_SCRATCH_BYTES,
+ * one per GPU the library runs on, held until the process ends.  The caller passes only the
+ * inputs and outputs (h, W, targets, loss, lse as for la_ce_fwd); nothing is allocated by the
+ * call, the library or the caller.
+ *   - Sizes whose forward workspace (la_ce_fwd_workspace_bytes) exceeds
+ *     LA_CE_NOALLOC_SCRATCH_BYTES return LA_ERR_UNSUPPORTED (with V = 50257, up to 5248 tokens);
+ *     otherwise the checks and statuses of la_ce_fwd apply.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's contents (the
+ *     forward overwrites all it reads, so nothing needs clearing).  Calls that overlap on one
+ *     GPU (concurrent streams, or other host threads) race on it: serialise them.
+ *   - The first call on a device looks up that device's copy of the array (hipGetSymbolAddress)
+ *     and keeps its address; a failed lookup returns LA_ERR_LAUNCH.
+ */
+#define LA_CE_NOALLOC_SCRATCH_BYTES 8388608
+la_status la_ce_fwd_noalloc(const void *h, const void *W, const int *targets, float *loss, float *lse,
+                            int N, int d, int V, la_dtype dt, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *la_status_str(la_status s);
 

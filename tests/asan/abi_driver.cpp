@@ -125,6 +125,12 @@ int main() {
                      LA_BF16, 0),
            LA_ERR_UNSUPPORTED, 0);
 
+    expect("ce fwd noalloc", la_ce_fwd_noalloc(A(0), A(1), (const int *)A(2), F(3), F(4), 512, 1280, 50257, LA_BF16, 0),
+           LA_OK, L_CE_FWD_NOALLOC);
+    expect("ce fwd noalloc beyond scratch",
+           la_ce_fwd_noalloc(A(0), A(1), (const int *)A(2), F(3), F(4), 6000, 128, 50257, LA_BF16, 0),
+           LA_ERR_UNSUPPORTED, 0);
+
     // ---- launch floors
     expect("floor empty", la_floor_launch(0, 160, nullptr, 0, A(1), 2048, 0), LA_OK, L_FLOOR);
     expect("floor fwd", la_floor_launch(1, 160, A(0), 160 * 65536, A(1), 160 * 32768, 0), LA_OK, L_FLOOR);

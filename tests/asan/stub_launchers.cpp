@@ -83,6 +83,10 @@ hipError_t launch_ce_fwd(const void *, const void *, const int *, float *, float
                          hipStream_t, const hipEvent_t *) {
     return hit(L_CE_FWD);
 }
+hipError_t launch_ce_fwd_noalloc(const void *, const void *, const int *, float *, float *, int, int, int, hipStream_t,
+                                 const hipEvent_t *) {
+    return hit(L_CE_FWD_NOALLOC);
+}
 hipError_t launch_ce_bwd(const void *, const void *, const int *, const float *, const float *, void *, float *,
                          void *, int, int, int, int, hipStream_t, const hipEvent_t *) {
     return hit(L_CE_BWD);

@@ -32,7 +32,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["la_abi_version", "la_ce_bwd", "la_ce_fwd", "la_ce_fwd_workspace_bytes",
+    assert declared_functions() == ["la_abi_version", "la_ce_bwd", "la_ce_fwd", "la_ce_fwd_noalloc",
+                                    "la_ce_fwd_workspace_bytes",
                                     "la_ce_workspace_bytes",
                                     "la_chunk_bwd", "la_chunk_fwd", "la_floor_launch", "la_kernel_name",
                                     "la_seq_bwd", "la_seq_fwd", "la_seq_kernel_name", "la_status_str",
@@ -275,6 +276,20 @@ def test_ce_fwd_takes_shapes_whose_whole_p_would_not_fit(lib):
     assert ce_fwd_call(lib, N=N, d=d, V=V, ws_bytes=fwd_ws, ws=addr(1)) == ALIAS
     assert ce_bwd_call(lib, N=N, d=d, V=V, chunk=0, ws_bytes=CE_WS) == UNSUPPORTED
     assert ce_bwd_call(lib, N=N, d=d, V=V, chunk=1024, ws_bytes=CE_WS, ws=addr(1)) == ALIAS
+
+
+def test_ce_fwd_noalloc_limits(lib):
+    names = ["h", "W", "targets", "loss", "lse"]
+    call = lambda N, d=128, V=50257, **over: lib.la_ce_fwd_noalloc(
+        *[over.get(n, addr(i)) for i, n in enumerate(names)], N, d, V, 1, None)
+    limit = lac.CE_NOALLOC_SCRATCH_BYTES
+    # the largest token count whose forward workspace fits the library's scratch at V = 50257
+    fits = max(n for n in range(128, 8192, 128) if lac.ce_fwd_workspace_bytes(n, 128, 50257) <= limit)
+    assert fits == 5248
+    assert call(fits + 1) == UNSUPPORTED                   # beyond the scratch: refused before launch
+    assert call(fits, lse=None) == INVALID
+    assert call(fits, loss=addr(0)) == ALIAS               # checks pass up to the overlap check
+    assert call(0) == INVALID and call(16, d=100) == UNSUPPORTED
 
 
 def test_time_next_launch_pairs(lib):
