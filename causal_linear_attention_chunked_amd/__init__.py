@@ -63,9 +63,9 @@ def load_library():
         lib = ctypes.CDLL(_LIB_PATH)
         vp, i = ctypes.c_void_p, ctypes.c_int
         lib.la_chunk_fwd.restype = i
-        lib.la_chunk_fwd.argtypes = [vp] * 8 + [i] * 5 + [vp]
+        lib.la_chunk_fwd.argtypes = [vp] * 8 + [i] * 6 + [vp]
         lib.la_chunk_bwd.restype = i
-        lib.la_chunk_bwd.argtypes = [vp] * 13 + [i] * 5 + [vp]
+        lib.la_chunk_bwd.argtypes = [vp] * 13 + [i] * 6 + [vp]
         lib.la_status_str.restype = ctypes.c_char_p
         lib.la_status_str.argtypes = [i]
         lib.la_abi_version.restype = i
@@ -73,7 +73,7 @@ def load_library():
         lib.la_time_next_launch.restype = i
         lib.la_time_next_launch.argtypes = [vp, vp]
         lib.la_kernel_name.restype = ctypes.c_char_p
-        lib.la_kernel_name.argtypes = [i, i, i, i]
+        lib.la_kernel_name.argtypes = [i] * 6
         lib.la_seq_fwd.restype = i
         lib.la_seq_fwd.argtypes = [vp] * 10 + [i] * 7 + [vp]
         lib.la_seq_bwd.restype = i
@@ -108,13 +108,6 @@ def _dt_code(dtype):
     return LA_BF16 if str(dtype).replace("torch.", "") in ("bf16", "bfloat16") else LA_F32
 
 
-def kernel_name(backward: bool, dtype, C: int, D: int):
-    """Name of the kernel a fwd (backward=False) or bwd call launches for this element type
-    ("bf16"/"float32" or a torch dtype), chunk length and head dimension; None if unsupported."""
-    name = load_library().la_kernel_name(int(bool(backward)), _dt_code(dtype), int(C), int(D))
-    return None if name is None else name.decode()
-
-
 FEATURES = {None: 0, "none": 0, "elu1": 1}
 
 
@@ -122,6 +115,15 @@ def _feature_code(feature):
     if feature not in FEATURES:
         raise ValueError(f"unknown feature map {feature!r}; use None or 'elu1'")
     return FEATURES[feature]
+
+
+def kernel_name(backward: bool, dtype, C: int, D: int, block: int = 64, feature=None):
+    """Name of the kernel a fwd (backward=False) or bwd call launches for this element type
+    ("bf16"/"float32" or a torch dtype), chunk length, head dimension, block (64: the blocked
+    form, 1: the cumsum form) and feature map; None if unsupported."""
+    name = load_library().la_kernel_name(int(bool(backward)), _dt_code(dtype), int(C), int(D), int(block),
+                                         _feature_code(feature))
+    return None if name is None else name.decode()
 
 
 def seq_kernel_name(backward: bool, dtype, chunk: int, D: int, feature=None):
@@ -235,8 +237,10 @@ def _stream(dev):
     return torch._C._cuda_getCurrentRawStream(dev)
 
 
-def fwd(q, k, v, S_in=None, z_in=None, block: int = 64, out=None):
-    """Forward over one chunk: returns (o, S_out, z_out).  ``out`` may supply them."""
+def fwd(q, k, v, S_in=None, z_in=None, block: int = 64, out=None, feature=None):
+    """Forward over one chunk: returns (o, S_out, z_out).  ``out`` may supply them.  ``block``:
+    64, the blocked (chunked) form; 1, the cumsum form (the per-token recurrence).
+    ``feature="elu1"``: q, k are raw inputs and elu(x) + 1 is applied inside."""
     lib = _lib or load_library()
     G, C, D, dev = _validate_tokens(("q", "k", "v"), (q, k, v))
     if (S_in is None) != (z_in is None):
@@ -253,12 +257,13 @@ def fwd(q, k, v, S_in=None, z_in=None, block: int = 64, out=None):
         _validate_outputs(("o", "S_out", "z_out"), (o,), (S_out, z_out), q, G, D, dev)
     _check("la_chunk_fwd", lib.la_chunk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(S_in), _ptr(z_in),
                                             o.data_ptr(), S_out.data_ptr(), z_out.data_ptr(), G, C, D, int(block),
-                                            _dtype_code(q), _stream(dev)))
+                                            _feature_code(feature), _dtype_code(q), _stream(dev)))
     return o, S_out, z_out
 
 
-def bwd(q, k, v, S_in, z_in, dO, dS_out=None, dz_out=None, block: int = 64, out=None):
-    """Backward over one chunk: returns (dq, dk, dv, dS_in, dz_in)."""
+def bwd(q, k, v, S_in, z_in, dO, dS_out=None, dz_out=None, block: int = 64, out=None, feature=None):
+    """Backward over one chunk: returns (dq, dk, dv, dS_in, dz_in); ``block`` and ``feature`` as
+    in ``fwd`` (with the map, dq and dk are the gradients of the raw inputs)."""
     lib = _lib or load_library()
     G, C, D, dev = _validate_tokens(("q", "k", "v", "dO"), (q, k, v, dO))
     if (S_in is None) != (z_in is None) or (dS_out is None) != (dz_out is None):
@@ -278,7 +283,8 @@ def bwd(q, k, v, S_in, z_in, dO, dS_out=None, dz_out=None, block: int = 64, out=
     _check("la_chunk_bwd", lib.la_chunk_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(S_in), _ptr(z_in),
                                             dO.data_ptr(), _ptr(dS_out), _ptr(dz_out), dq.data_ptr(),
                                             dk.data_ptr(), dv.data_ptr(), dS_in.data_ptr(), dz_in.data_ptr(),
-                                            G, C, D, int(block), _dtype_code(q), _stream(dev)))
+                                            G, C, D, int(block), _feature_code(feature), _dtype_code(q),
+                                            _stream(dev)))
     return dq, dk, dv, dS_in, dz_in
 
 

@@ -17,13 +17,15 @@ kept between the passes, the memory-flat principle of the page's section 1.  Gra
 when given, S_in and z_in; a loss on S_out / z_out reaches them too.
 
 The implementation is selectable, as the page's call site selects its attention form
-(section 2, Opt 2: the chunked form next to the einsum and cumsum forms it replaces).
-Here the choice is among this library's GPU paths: "seq" (the sequence entry points),
-"chunk" (one launch per chunk and direction, the carry through memory) and "auto" (seq
-where it takes the shape, else chunk).  linear_attention(impl=...) picks one per call;
-set_attention_impl() sets the default, which otherwise comes from the environment
-variable LACHUNK_ATTN_IMPL, else "auto".  The einsum and cumsum forms themselves are
-references in the oracle (test infrastructure), not product paths.
+(section 2, Opt 1 and Opt 2: the chunked form next to the einsum and cumsum forms it
+replaces).  Here the choice is among this library's GPU paths: "seq" (the sequence entry
+points), "chunk" (the chunked form, one launch per chunk and direction, the carry through
+memory), "cumsum" (the cumsum form: the per-token recurrence, block = 1 in the chunk entry
+points, chunk by chunk with the carry) and "auto" (seq where it takes the shape, else
+chunk).  linear_attention(impl=...) picks one per call; set_attention_impl() sets the
+default, which otherwise comes from the environment variable LACHUNK_ATTN_IMPL, else
+"auto".  The masked-einsum form, O(C^2 D^2) per chunk, is a reference in the oracle (test
+infrastructure), not a product path.
 
 The arithmetic runs in the HIP library only: CPU tensors raise.
 """
@@ -41,13 +43,14 @@ from . import seq_supported as _seq_supported
 
 
 class ChunkFunction(torch.autograd.Function):
-    """One chunk: (q, k, v, S_in, z_in) -> (o, S_out, z_out), backward by recomputation."""
+    """One chunk: (q, k, v, S_in, z_in) -> (o, S_out, z_out), backward by recomputation; block 64
+    (the chunked form) or 1 (the cumsum form); feature "elu1" maps raw q, k inside."""
 
     @staticmethod
-    def forward(ctx, q, k, v, S_in, z_in, block):
+    def forward(ctx, q, k, v, S_in, z_in, block, feature=None):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o, S_out, z_out = _fwd(q, k, v, S_in, z_in, block)
-        ctx.block = block
+        o, S_out, z_out = _fwd(q, k, v, S_in, z_in, block, feature=feature)
+        ctx.block, ctx.feature = block, feature
         ctx.has_carry = S_in is not None
         ctx.save_for_backward(q, k, v, S_in, z_in)
         return o, S_out, z_out
@@ -66,10 +69,10 @@ class ChunkFunction(torch.autograd.Function):
         dS_out = None if dS_out is None else dS_out.float().contiguous()
         dz_out = None if dz_out is None else dz_out.float().contiguous()
         dq, dk, dv, dS_in, dz_in = _bwd(q, k, v, S_in, z_in, do.to(q.dtype).contiguous(), dS_out, dz_out,
-                                        ctx.block)
+                                        ctx.block, feature=ctx.feature)
         if not ctx.has_carry:
             dS_in = dz_in = None
-        return dq, dk, dv, dS_in, dz_in, None
+        return dq, dk, dv, dS_in, dz_in, None, None
 
 
 class SeqFunction(torch.autograd.Function):
@@ -106,13 +109,13 @@ class SeqFunction(torch.autograd.Function):
         return dq, dk, dv, dS_in, dz_in, None, None, None
 
 
-def chunk_attention(q, k, v, S_in=None, z_in=None, block: int = 64):
+def chunk_attention(q, k, v, S_in=None, z_in=None, block: int = 64, feature_map=None):
     """Differentiable single-chunk op: returns (o, S_out, z_out)."""
     _check_device(q)
-    return ChunkFunction.apply(q, k, v, S_in, z_in, block)
+    return ChunkFunction.apply(q, k, v, S_in, z_in, block, _fm(feature_map))
 
 
-IMPLS = ("auto", "seq", "chunk")
+IMPLS = ("auto", "seq", "chunk", "cumsum")
 IMPL_ENV = "LACHUNK_ATTN_IMPL"
 _impl = None  # set by set_attention_impl; None: the environment variable, else "auto"
 
@@ -125,8 +128,8 @@ def _check_impl(name, where):
 
 def set_attention_impl(name):
     """Set the implementation linear_attention uses when called without ``impl``: "auto",
-    "seq" or "chunk"; None returns to the environment variable LACHUNK_ATTN_IMPL (else
-    "auto")."""
+    "seq", "chunk" or "cumsum"; None returns to the environment variable LACHUNK_ATTN_IMPL
+    (else "auto")."""
     global _impl
     _impl = None if name is None else _check_impl(name, "set_attention_impl")
 
@@ -143,9 +146,9 @@ def linear_attention(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int
     """Causal linear attention over a (G, T, D) sequence in chunks of ``chunk`` tokens
     (the last one ragged), carrying (S, z) across chunks.  Returns (o, (S_out, z_out)).
     ``feature_map="elu1"``: q and k are raw inputs and elu(x) + 1 is applied inside the
-    kernels (fused; the shapes of the sequence path only), gradients flowing to the raw
-    inputs.  ``impl``: "auto", "seq" or "chunk" (None: get_attention_impl()); "seq" raises
-    where the sequence entry points do not take the shape."""
+    kernels (fused, on every path), gradients flowing to the raw inputs.  ``impl``: "auto",
+    "seq", "chunk" or "cumsum" (None: get_attention_impl()); "seq" raises where the sequence
+    entry points do not take the shape; "cumsum" runs the per-token form chunk by chunk."""
     name = get_attention_impl() if impl is None else _check_impl(impl, "linear_attention")
     _check_device(q)
     if q.dim() != 3:
@@ -155,28 +158,20 @@ def linear_attention(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int
     T = q.shape[1]
     if T == 0:
         return q.new_empty(q.shape), (S_in, z_in)
-    fm = None if feature_map in (None, "none") else feature_map
+    fm = _fm(feature_map)
     seq_ok = _seq_supported(q.dtype, T, q.shape[2], chunk, fm) and block == 64
     if name == "seq" and not seq_ok:
         raise ValueError("impl='seq': the sequence entry points take bf16, block 64, and D = 64 in whole "
                          "128-token chunks or D = 128 in chunks of a multiple of 64 tokens")
-    if fm is not None:
-        if name == "chunk":
-            raise ValueError("impl='chunk': the fused feature map runs in the sequence kernels only")
-        if not seq_ok:
-            raise ValueError(f"the fused feature map {feature_map!r} runs in the sequence kernels only "
-                             "(bf16; D = 64 in whole 128-token chunks, or D = 128 in chunks of a "
-                             "multiple of 64 tokens)")
-        o, S, z = SeqFunction.apply(q, k, v, S_in, z_in, chunk, block, feature_map)
+    if seq_ok and name in ("seq", "auto"):
+        o, S, z = SeqFunction.apply(q, k, v, S_in, z_in, chunk, block, fm)
         return o, (S, z)
-    if seq_ok and name != "chunk":
-        o, S, z = SeqFunction.apply(q, k, v, S_in, z_in, chunk, block, None)
-        return o, (S, z)
+    blk = 1 if name == "cumsum" else block
     outs = []
     S, z = S_in, z_in
     for t0 in range(0, T, chunk):
         t1 = min(T, t0 + chunk)
-        o, S, z = ChunkFunction.apply(q[:, t0:t1], k[:, t0:t1], v[:, t0:t1], S, z, block)
+        o, S, z = ChunkFunction.apply(q[:, t0:t1], k[:, t0:t1], v[:, t0:t1], S, z, blk, fm)
         outs.append(o)
     o = outs[0] if len(outs) == 1 else torch.cat(outs, dim=1)
     return o, (S, z)
@@ -210,6 +205,14 @@ def chunked_cross_entropy(h, W, targets, ce_chunk: int = 0):
     (0: all).  bf16 h and W; the gradient of W is computed in fp32 and returned in W's dtype."""
     _check_device(h)
     return CrossEntropyFunction.apply(h, W, targets, ce_chunk)
+
+
+def _fm(feature_map):
+    if feature_map in (None, "none"):
+        return None
+    if feature_map != "elu1":
+        raise ValueError(f"unknown feature map {feature_map!r}; use None or 'elu1'")
+    return feature_map
 
 
 def _check_device(q):

@@ -12,6 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblachunk.so")
 SOURCES = ["la_api.cpp", "la_fwd.hip", "la_fwd2.hip", "la_bwd.hip", "la_bwd4.hip", "la_bwd_seq128.hip", "la_ce.hip", "la_fwd_seq128.hip",
+           "la_cumsum.hip",
            "la_floor.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -52,7 +52,7 @@ la_status common_checks(int G, int C, int D, int block, la_dtype dt, Sizes *sz) 
     if (G < 1 || C < 1) return LA_ERR_INVALID;
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_UNSUPPORTED;
     if (D != 64 && D != 128) return LA_ERR_UNSUPPORTED;
-    if (block != 64) return LA_ERR_UNSUPPORTED;
+    if (block != 64 && block != 1) return LA_ERR_UNSUPPORTED;
     const size_t esz = dt == LA_F32 ? 4 : 2;
     size_t a, b;
     if (!mul_ok((size_t)G, (size_t)C, &a) || !mul_ok(a, (size_t)D, &b) || !mul_ok(b, esz, &sz->tok))
@@ -73,13 +73,24 @@ la_status seq_checks(int G, int T, int D, int chunk, int block, la_dtype dt, la_
     if (feature != LA_FEATURE_NONE && feature != LA_FEATURE_ELU1) return LA_ERR_INVALID;
     la_status st = common_checks(G, chunk, D, block, dt, sz);
     if (st != LA_OK) return st;
-    if (dt != LA_BF16) return LA_ERR_UNSUPPORTED;
+    if (dt != LA_BF16 || block != BK_TOKENS) return LA_ERR_UNSUPPORTED;
     if (D == 64 && (chunk != 128 || T % chunk != 0 || T > LA_SEQ_D64_MAX_T)) return LA_ERR_UNSUPPORTED;
     if (D == 128 && (chunk % BK_TOKENS != 0 || T > LA_SEQ_D128_MAX_T)) return LA_ERR_UNSUPPORTED;
     size_t a, b;
     if (!mul_ok((size_t)G, (size_t)T, &a) || !mul_ok(a, (size_t)D * 2, &b)) return LA_ERR_INVALID;
     sz->tok = b;
     return LA_OK;
+}
+
+// Which kernel family a chunk call runs: the 128-token kernels (bf16, D = 64, C = 128, block 64),
+// the per-token cumsum kernels (block 1; the fused feature map on any other shape; the fp32
+// backward at D = 128, whose blocked fp32 tiles exceed the LDS), or the general blocked kernels.
+enum class Path { C128, CUMSUM, GENERAL };
+Path chunk_path(bool backward, la_dtype dt, int C, int D, int block, la_feature feature) {
+    const bool c128 = dt == LA_BF16 && D == 64 && C == 128 && block == BK_TOKENS;
+    if (c128) return Path::C128;
+    if (block == 1 || feature == LA_FEATURE_ELU1 || (backward && dt == LA_F32 && D == 128)) return Path::CUMSUM;
+    return Path::GENERAL;
 }
 
 // every output span against every input span and every other output span
@@ -98,10 +109,11 @@ la_status alias_checks(const Span *in, int nin, const Span *out, int nout) {
 extern "C" {
 
 la_status la_chunk_fwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
-                       void *o, float *S_out, float *z_out, int G, int C, int D, int block, la_dtype dt,
-                       void *stream) {
+                       void *o, float *S_out, float *z_out, int G, int C, int D, int block, la_feature feature,
+                       la_dtype dt, void *stream) {
     const TakenEvents te;
     Sizes sz;
+    if (feature != LA_FEATURE_NONE && feature != LA_FEATURE_ELU1) return LA_ERR_INVALID;
     la_status st = common_checks(G, C, D, block, dt, &sz);
     if (st != LA_OK) return st;
     if (!q || !k || !v || !o || !S_out || !z_out) return LA_ERR_INVALID;
@@ -115,9 +127,19 @@ la_status la_chunk_fwd(const void *q, const void *k, const void *v, const float 
     if (st != LA_OK) return st;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const bool fm = feature == LA_FEATURE_ELU1;
     hipError_t e;
-    if (dt == LA_BF16 && D == 64 && C == 128)
-        e = lachunk::launch_fwd_c128(q, k, v, S_in, z_in, o, S_out, z_out, G, s, te.ev);
+    const Path path = chunk_path(false, dt, C, D, block, feature);
+    if (path == Path::C128)
+        e = lachunk::launch_fwd_c128(q, k, v, S_in, z_in, o, S_out, z_out, G, fm, s, te.ev);
+    else if (path == Path::CUMSUM)
+        e = dt == LA_BF16
+                ? (D == 64 ? lachunk::launch_cumsum_fwd<__bf16, 64>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, fm, s, te.ev)
+                           : lachunk::launch_cumsum_fwd<__bf16, 128>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, fm, s,
+                                                                     te.ev))
+                : (D == 64 ? lachunk::launch_cumsum_fwd<float, 64>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, fm, s, te.ev)
+                           : lachunk::launch_cumsum_fwd<float, 128>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, fm, s,
+                                                                    te.ev));
     else if (dt == LA_BF16)
         e = D == 64 ? lachunk::launch_fwd<__bf16, 64>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s, te.ev)
                     : lachunk::launch_fwd<__bf16, 128>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, s, te.ev);
@@ -129,13 +151,14 @@ la_status la_chunk_fwd(const void *q, const void *k, const void *v, const float 
 
 la_status la_chunk_bwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
                        const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
-                       float *dS_in, float *dz_in, int G, int C, int D, int block, la_dtype dt, void *stream) {
+                       float *dS_in, float *dz_in, int G, int C, int D, int block, la_feature feature, la_dtype dt,
+                       void *stream) {
     const TakenEvents te;
     Sizes sz;
+    if (feature != LA_FEATURE_NONE && feature != LA_FEATURE_ELU1) return LA_ERR_INVALID;
     la_status st = common_checks(G, C, D, block, dt, &sz);
     if (st != LA_OK) return st;
     if (C > LA_BWD_MAX_C) return LA_ERR_UNSUPPORTED;
-    if (dt == LA_F32 && D == 128) return LA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !dO || !dq || !dk || !dv || !dS_in || !dz_in) return LA_ERR_INVALID;
     if ((S_in == nullptr) != (z_in == nullptr)) return LA_ERR_INVALID;
     if ((dS_out == nullptr) != (dz_out == nullptr)) return LA_ERR_INVALID;
@@ -150,9 +173,22 @@ la_status la_chunk_bwd(const void *q, const void *k, const void *v, const float 
     if (st != LA_OK) return st;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const bool fm = feature == LA_FEATURE_ELU1;
     hipError_t e;
-    if (dt == LA_BF16 && D == 64 && C == 128)
-        e = lachunk::launch_bwd_c128(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, G, s, te.ev);
+    const Path path = chunk_path(true, dt, C, D, block, feature);
+    if (path == Path::C128)
+        e = lachunk::launch_bwd_c128(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, G, fm, s,
+                                     te.ev);
+    else if (path == Path::CUMSUM)
+        e = dt == LA_BF16
+                ? (D == 64 ? lachunk::launch_cumsum_bwd<__bf16, 64>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv,
+                                                                    dS_in, dz_in, G, C, fm, s, te.ev)
+                           : lachunk::launch_cumsum_bwd<__bf16, 128>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk,
+                                                                     dv, dS_in, dz_in, G, C, fm, s, te.ev))
+                : (D == 64 ? lachunk::launch_cumsum_bwd<float, 64>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv,
+                                                                   dS_in, dz_in, G, C, fm, s, te.ev)
+                           : lachunk::launch_cumsum_bwd<float, 128>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv,
+                                                                    dS_in, dz_in, G, C, fm, s, te.ev));
     else if (dt == LA_BF16)
         e = D == 64 ? lachunk::launch_bwd<__bf16, 64>(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in,
                                                      dz_in, G, C, s, te.ev)
@@ -327,12 +363,19 @@ const char *la_status_str(la_status s) {
 
 int la_abi_version(void) { return LA_ABI_VERSION; }
 
-const char *la_kernel_name(int backward, la_dtype dt, int C, int D) {
-    if ((dt != LA_F32 && dt != LA_BF16) || (D != 64 && D != 128) || C < 1) return nullptr;
-    const bool c128 = dt == LA_BF16 && D == 64 && C == 128;  // the dispatch rule of the entry points
-    if (!backward) return c128 ? "la_fwd_c128_kernel" : "la_fwd_kernel";
-    if (C > LA_BWD_MAX_C || (dt == LA_F32 && D == 128)) return nullptr;
-    return c128 ? "la_bwd_c128w16_kernel" : "la_bwd_kernel";
+const char *la_kernel_name(int backward, la_dtype dt, int C, int D, int block, la_feature feature) {
+    if ((dt != LA_F32 && dt != LA_BF16) || (D != 64 && D != 128) || C < 1 || (block != 64 && block != 1)) return nullptr;
+    if (feature != LA_FEATURE_NONE && feature != LA_FEATURE_ELU1) return nullptr;
+    if (backward && C > LA_BWD_MAX_C) return nullptr;
+    const bool fm = feature == LA_FEATURE_ELU1;
+    switch (chunk_path(backward != 0, dt, C, D, block, feature)) {
+        case Path::C128:
+            if (backward) return fm ? "la_bwd_c128w16_elu1_kernel" : "la_bwd_c128w16_kernel";
+            return fm ? "la_fwd_c128_elu1_kernel" : "la_fwd_c128_kernel";
+        case Path::CUMSUM: return backward ? "la_cumsum_bwd_kernel" : "la_cumsum_fwd_kernel";
+        case Path::GENERAL: break;
+    }
+    return backward ? "la_bwd_kernel" : "la_fwd_kernel";
 }
 
 const char *la_seq_kernel_name(int backward, la_dtype dt, int chunk, int D, la_feature feature) {

@@ -605,12 +605,24 @@ __global__ __launch_bounds__(W16_THREADS, 1) void la_seq_bwd_c128w16_elu1_kernel
                               nchunk);
 }
 
+// the one-chunk backward with the feature map fused: dq and dk are the gradients of the raw inputs
+__global__ __launch_bounds__(W16_THREADS, 1) void la_bwd_c128w16_elu1_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_in, const float *__restrict__ z_in, const bf16 *__restrict__ dO,
+    const float *__restrict__ dS_out, const float *__restrict__ dz_out,
+    bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
+    float *__restrict__ dS_in, float *__restrict__ dz_in) {
+    bwd_c128_body<false, true>(q, k, v, S_in, z_in, nullptr, nullptr, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in,
+                               1);
+}
+
 hipError_t launch_bwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
                            const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
-                           float *dS_in, float *dz_in, int G, hipStream_t stream, const hipEvent_t ev[2]) {
-    hipExtLaunchKernelGGL(la_bwd_c128w16_kernel, dim3((unsigned)G), dim3(W16_THREADS), 0, stream, ev[0], ev[1], 0,
-                          (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_in, z_in, (const bf16 *)dO, dS_out,
-                          dz_out, (bf16 *)dq, (bf16 *)dk, (bf16 *)dv, dS_in, dz_in);
+                           float *dS_in, float *dz_in, int G, bool elu1, hipStream_t stream, const hipEvent_t ev[2]) {
+    hipExtLaunchKernelGGL(elu1 ? la_bwd_c128w16_elu1_kernel : la_bwd_c128w16_kernel, dim3((unsigned)G),
+                          dim3(W16_THREADS), 0, stream, ev[0], ev[1], 0, (const bf16 *)q, (const bf16 *)k,
+                          (const bf16 *)v, S_in, z_in, (const bf16 *)dO, dS_out, dz_out, (bf16 *)dq, (bf16 *)dk,
+                          (bf16 *)dv, dS_in, dz_in);
     return hipGetLastError();
 }
 

@@ -337,10 +337,20 @@ __global__ __launch_bounds__(NTHR, 2) void la_seq_fwd_c128_elu1_kernel(
     fwd_c128_body<true, true>(q, k, v, S_in, z_in, o, S_out, z_out, S_res, z_res, nchunk);
 }
 
+// the one-chunk forward with the feature map fused: q and k are the raw inputs x
+__global__ __launch_bounds__(NTHR, 1) void la_fwd_c128_elu1_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_in, const float *__restrict__ z_in,
+    bf16 *__restrict__ o, float *__restrict__ S_out, float *__restrict__ z_out) {
+    fwd_c128_body<false, true>(q, k, v, S_in, z_in, o, S_out, z_out, nullptr, nullptr, 1);
+}
+
 hipError_t launch_fwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
-                           void *o, float *S_out, float *z_out, int G, hipStream_t stream, const hipEvent_t ev[2]) {
-    hipExtLaunchKernelGGL(la_fwd_c128_kernel, dim3((unsigned)G), dim3(NTHR), 0, stream, ev[0], ev[1], 0,
-                          (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_in, z_in, (bf16 *)o, S_out, z_out);
+                           void *o, float *S_out, float *z_out, int G, bool elu1, hipStream_t stream,
+                           const hipEvent_t ev[2]) {
+    hipExtLaunchKernelGGL(elu1 ? la_fwd_c128_elu1_kernel : la_fwd_c128_kernel, dim3((unsigned)G), dim3(NTHR), 0,
+                          stream, ev[0], ev[1], 0, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, S_in, z_in,
+                          (bf16 *)o, S_out, z_out);
     return hipGetLastError();
 }
 

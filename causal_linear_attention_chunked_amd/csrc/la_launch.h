@@ -17,12 +17,26 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const float *
                       float *dS_in, float *dz_in, int G, int C, hipStream_t stream,
                       const hipEvent_t ev[2]);
 
-// bf16, D = 64, exactly two blocks (C = 128): both blocks of the chunk worked on side by side.
+// bf16, D = 64, exactly two blocks (C = 128): both blocks of the chunk worked on side by side;
+// elu1: q and k are raw inputs and the feature map elu(x) + 1 is applied inside.
 hipError_t launch_fwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
-                           void *o, float *S_out, float *z_out, int G, hipStream_t stream, const hipEvent_t ev[2]);
+                           void *o, float *S_out, float *z_out, int G, bool elu1, hipStream_t stream,
+                           const hipEvent_t ev[2]);
 hipError_t launch_bwd_c128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
                            const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
-                           float *dS_in, float *dz_in, int G, hipStream_t stream, const hipEvent_t ev[2]);
+                           float *dS_in, float *dz_in, int G, bool elu1, hipStream_t stream, const hipEvent_t ev[2]);
+
+// The cumsum form: the per-token recurrence over one chunk of any length (backward: C up to
+// LA_BWD_MAX_C), fp32 arithmetic, any supported element type and D; elu1 as above.
+template <typename T, int D>
+hipError_t launch_cumsum_fwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
+                             void *o, float *S_out, float *z_out, int G, int C, bool elu1, hipStream_t stream,
+                             const hipEvent_t ev[2]);
+template <typename T, int D>
+hipError_t launch_cumsum_bwd(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
+                             const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
+                             float *dS_in, float *dz_in, int G, int C, bool elu1, hipStream_t stream,
+                             const hipEvent_t ev[2]);
 
 // The same kernels walking a group's nchunk consecutive 128-token chunks, carry on chip
 // (backward: S_last / z_last is the state after the last chunk); elu1: q and k are raw inputs

@@ -151,14 +151,14 @@ __device__ __forceinline__ void store_bf16x4(bf16 *p, const bf16x4 &x) {
 // inputs mapped in fp32 (e^x as 2^(x log2 e) on the transcendental unit) and rounded to bf16.
 // Since e^x >= x + 1 everywhere, phi(x) = max(x + 1, min(e^x, 1)): the min is the exp's output
 // clamp to [0, 1], and no compare and select is needed.
+__device__ __forceinline__ float elu1_f(float f) {
+    const float e = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(f * 1.4426950408889634f), 0.f, 1.f);
+    return __builtin_fmaxf(f + 1.f, e);
+}
 __device__ __forceinline__ bf16x8 elu1_8(const bf16x8 &x) {
     bf16x8 y;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float f = (float)x[i];
-        const float e = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(f * 1.4426950408889634f), 0.f, 1.f);
-        y[i] = (bf16)__builtin_fmaxf(f + 1.f, e);
-    }
+    for (int i = 0; i < 8; ++i) y[i] = (bf16)elu1_f((float)x[i]);
     return y;
 }
 // phi'(x) from the mapped value: 1 above zero (where phi > 1), e^x = phi below.

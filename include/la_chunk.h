@@ -37,10 +37,10 @@
  *   - Preconditions NOT checked on the device: q_t . z_t > 0 for every token
  *     (true for positive features: q, k > 0 elementwise and z_in >= 0), and
  *     finite inputs.  No epsilon is added to the denominator.
- *   - Supported: D in {64, 128}, block == 64, G >= 1, 1 <= C, and one group's
- *     chunk plus 256 tokens below 2 GiB ((C + 256) * D * element size < 2^31:
- *     the kernels address a chunk with 32-bit byte offsets).  The backward
- *     additionally needs C <= LA_BWD_MAX_C and, for D == 128, bf16 elements.
+ *   - Supported: D in {64, 128}, block 64 (or 1 for the chunk calls), G >= 1,
+ *     1 <= C, and one group's chunk plus 256 tokens below 2 GiB
+ *     ((C + 256) * D * element size < 2^31: the kernels address a chunk with
+ *     32-bit byte offsets).  The backward additionally needs C <= LA_BWD_MAX_C.
  *     Anything else returns LA_ERR_UNSUPPORTED.
  */
 #ifndef LA_CHUNK_H
@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 5
+#define LA_ABI_VERSION 6
 #define LA_BWD_MAX_C 2048
 /* Longest sequences (tokens per group) of the sequence entry points, D = 64 and D = 128:
  * the lengths at which their results are verified to the parity tolerance against an fp64
@@ -80,21 +80,33 @@ typedef enum {
 
 /*
  * Forward over one chunk.
- *   q, k, v  : [G][C][D] dt, inputs.  q and k are positive features.
+ *   q, k, v  : [G][C][D] dt, inputs.  q and k are positive features (or, with
+ *              feature = LA_FEATURE_ELU1, the raw inputs x of the map phi).
  *   S_in     : [G][D][D] fp32 carried state, or NULL (zero state).
  *   z_in     : [G][D]    fp32 carried normaliser, or NULL.  S_in and z_in are
  *              both NULL or both non-NULL.
  *   o        : [G][C][D] dt, output o_t.
  *   S_out    : [G][D][D] fp32, output state after the chunk (S_C).
  *   z_out    : [G][D]    fp32, output normaliser after the chunk (z_C).
- *   block    : tokens per block of the blocked form (must be 64).
+ *   block    : 64: the blocked ("chunked") form of section 2, Opt 2 (64-token
+ *              blocks, the ragged tail token by token);
+ *              1: the cumsum form of the same section (Opt 1 names it among the
+ *              selectable forms): the exact per-token recurrence over the whole
+ *              chunk, in fp32 arithmetic, no blocking.  Both compute the same
+ *              function; they differ only in summation order.
+ *   feature  : LA_FEATURE_NONE, or LA_FEATURE_ELU1: q and k hold raw inputs x and
+ *              the op runs on phi(x) = elu(x) + 1 computed in fp32 and rounded to
+ *              the element type as the inputs are loaded (as in la_seq_fwd).  With
+ *              the map, the 128-token bf16 chunk at D = 64 runs its blocked kernel;
+ *              every other shape runs the per-token form.
  * S_out may not alias S_in: the call is pure (the carry goes in, a new carry
- * comes out), so chaining chunks ping-pongs two state buffers.
+ * comes out), so chaining chunks ping-pongs two state buffers.  A feature
+ * outside la_feature is LA_ERR_INVALID.
  */
 la_status la_chunk_fwd(const void *q, const void *k, const void *v,
                        const float *S_in, const float *z_in,
                        void *o, float *S_out, float *z_out,
-                       int G, int C, int D, int block, la_dtype dt, void *stream);
+                       int G, int C, int D, int block, la_feature feature, la_dtype dt, void *stream);
 
 /*
  * Backward over one chunk, for the loss
@@ -109,14 +121,19 @@ la_status la_chunk_fwd(const void *q, const void *k, const void *v,
  *   dS_in    : [G][D][D] fp32 output, gradient of S_in (pass it as the previous
  *              chunk's dS_out when chaining).
  *   dz_in    : [G][D]    fp32 output, gradient of z_in.
+ *   block, feature : as in the forward call.  With LA_FEATURE_ELU1, dq and dk are
+ *              the gradients with respect to the raw inputs: dq phi'(x_q), dk phi'(x_k),
+ *              phi'(x) = 1 for x > 0 and e^x otherwise (taken as min(1, phi)).
  * With a NULL carry, dS_in/dz_in still receive the gradient with respect to a
- * zero carry.
+ * zero carry.  fp32 elements at D == 128 run the per-token form whatever the
+ * block (the blocked form's fp32 tiles of that size exceed the local memory);
+ * its results agree with the blocked form's to fp32 rounding.
  */
 la_status la_chunk_bwd(const void *q, const void *k, const void *v,
                        const float *S_in, const float *z_in,
                        const void *dO, const float *dS_out, const float *dz_out,
                        void *dq, void *dk, void *dv, float *dS_in, float *dz_in,
-                       int G, int C, int D, int block, la_dtype dt, void *stream);
+                       int G, int C, int D, int block, la_feature feature, la_dtype dt, void *stream);
 
 /*
  * Forward over a whole sequence: n = T / chunk consecutive chunks per group, in order,
@@ -280,12 +297,12 @@ la_status la_time_next_launch(void *start_event, void *stop_event);
 
 /*
  * Measurement aid: the name of the kernel that la_chunk_fwd (backward = 0) or
- * la_chunk_bwd (backward = 1) launches for element type dt, chunk length C and
- * head dimension D, as it appears (demangled, template arguments aside) in
- * profiler output.  A static string; NULL when the configuration is not
- * supported.  Does not touch the device.
+ * la_chunk_bwd (backward = 1) launches for element type dt, chunk length C, head
+ * dimension D, block and feature map, as it appears (demangled, template
+ * arguments aside) in profiler output.  A static string; NULL when the
+ * configuration is not supported.  Does not touch the device.
  */
-const char *la_kernel_name(int backward, la_dtype dt, int C, int D);
+const char *la_kernel_name(int backward, la_dtype dt, int C, int D, int block, la_feature feature);
 
 /* The same for la_seq_fwd (backward = 0) and la_seq_bwd (backward = 1) at this chunk length. */
 const char *la_seq_kernel_name(int backward, la_dtype dt, int chunk, int D, la_feature feature);

@@ -11,7 +11,7 @@
 extern int g_last_launch;
 enum {
     L_NONE = 0, L_FWD, L_BWD, L_FWD_C128, L_BWD_C128, L_SEQ_FWD_C128, L_SEQ_BWD_C128, L_SEQ_FWD_D128,
-    L_SEQ_BWD_D128, L_CE_FWD, L_CE_BWD, L_CE_FWD_NOALLOC, L_FLOOR
+    L_SEQ_BWD_D128, L_CE_FWD, L_CE_BWD, L_CE_FWD_NOALLOC, L_FLOOR, L_CUMSUM_FWD, L_CUMSUM_BWD
 };
 
 static int failures = 0;
@@ -31,48 +31,74 @@ static void expect(const char *what, la_status got, la_status want, int launch_w
 
 int main() {
     // ---- la_chunk_fwd
-    expect("fwd headline", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 160, 128, 64, 64, LA_BF16, 0),
+    expect("fwd headline", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 160, 128, 64, 64, LA_FEATURE_NONE, LA_BF16, 0),
            LA_OK, L_FWD_C128);
-    expect("fwd ragged", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 4, 100, 64, 64, LA_BF16, 0),
+    expect("fwd ragged", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 4, 100, 64, 64, LA_FEATURE_NONE, LA_BF16, 0),
            LA_OK, L_FWD);
     expect("fwd fp32 d128 no carry",
-           la_chunk_fwd(A(0), A(1), A(2), nullptr, nullptr, A(5), F(6), F(7), 1, 37, 128, 64, LA_F32, 0), LA_OK, L_FWD);
-    expect("fwd G=0", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 0, 128, 64, 64, LA_BF16, 0),
+           la_chunk_fwd(A(0), A(1), A(2), nullptr, nullptr, A(5), F(6), F(7), 1, 37, 128, 64, LA_FEATURE_NONE, LA_F32, 0), LA_OK, L_FWD);
+    expect("fwd G=0", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 0, 128, 64, 64, LA_FEATURE_NONE, LA_BF16, 0),
            LA_ERR_INVALID, 0);
-    expect("fwd D=96", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 4, 128, 96, 64, LA_BF16, 0),
+    expect("fwd D=96", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 4, 128, 96, 64, LA_FEATURE_NONE, LA_BF16, 0),
            LA_ERR_UNSUPPORTED, 0);
-    expect("fwd half carry", la_chunk_fwd(A(0), A(1), A(2), nullptr, F(4), A(5), F(6), F(7), 4, 128, 64, 64, LA_BF16, 0),
+    expect("fwd half carry", la_chunk_fwd(A(0), A(1), A(2), nullptr, F(4), A(5), F(6), F(7), 4, 128, 64, 64, LA_FEATURE_NONE, LA_BF16, 0),
            LA_ERR_INVALID, 0);
     expect("fwd misaligned",
-           la_chunk_fwd((char *)A(0) + 8, A(1), A(2), F(3), F(4), A(5), F(6), F(7), 4, 128, 64, 64, LA_BF16, 0),
+           la_chunk_fwd((char *)A(0) + 8, A(1), A(2), F(3), F(4), A(5), F(6), F(7), 4, 128, 64, 64, LA_FEATURE_NONE, LA_BF16, 0),
            LA_ERR_ALIGN, 0);
-    expect("fwd S_out == S_in", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(3), F(7), 4, 128, 64, 64, LA_BF16, 0),
+    expect("fwd S_out == S_in", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(3), F(7), 4, 128, 64, 64, LA_FEATURE_NONE, LA_BF16, 0),
            LA_ERR_ALIAS, 0);
     expect("fwd overflow",
-           la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 0x7fffffff, 0x7fffffff, 128, 64, LA_BF16, 0),
+           la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 0x7fffffff, 0x7fffffff, 128, 64, LA_FEATURE_NONE, LA_BF16, 0),
            LA_ERR_INVALID, 0);
 
     // ---- la_chunk_bwd
     expect("bwd headline",
            la_chunk_bwd(A(0), A(1), A(2), F(3), F(4), A(5), nullptr, nullptr, A(8), A(9), A(10), F(11), F(12), 160, 128,
-                        64, 64, LA_BF16, 0),
+                        64, 64, LA_FEATURE_NONE, LA_BF16, 0),
            LA_OK, L_BWD_C128);
     expect("bwd d128 upstream",
            la_chunk_bwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), A(8), A(9), A(10), F(11), F(12), 160, 100, 128,
-                        64, LA_BF16, 0),
+                        64, LA_FEATURE_NONE, LA_BF16, 0),
            LA_OK, L_BWD);
     expect("bwd C > max",
            la_chunk_bwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), A(8), A(9), A(10), F(11), F(12), 4,
-                        LA_BWD_MAX_C + 1, 64, 64, LA_BF16, 0),
+                        LA_BWD_MAX_C + 1, 64, 64, LA_FEATURE_NONE, LA_BF16, 0),
            LA_ERR_UNSUPPORTED, 0);
     expect("bwd dq == dO",
            la_chunk_bwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), A(5), A(9), A(10), F(11), F(12), 4, 128, 64, 64,
-                        LA_BF16, 0),
+                        LA_FEATURE_NONE, LA_BF16, 0),
            LA_ERR_ALIAS, 0);
     expect("bwd half upstream",
            la_chunk_bwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), nullptr, A(8), A(9), A(10), F(11), F(12), 4, 128, 64,
-                        64, LA_BF16, 0),
+                        64, LA_FEATURE_NONE, LA_BF16, 0),
            LA_ERR_INVALID, 0);
+
+    // ---- block 1 (the cumsum form), the fused feature map, the fp32 backward at D = 128
+    expect("fwd cumsum", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 160, 128, 64, 1,
+                                      LA_FEATURE_NONE, LA_BF16, 0),
+           LA_OK, L_CUMSUM_FWD);
+    expect("fwd elu1 headline", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 160, 128, 64, 64,
+                                             LA_FEATURE_ELU1, LA_BF16, 0),
+           LA_OK, L_FWD_C128);
+    expect("fwd elu1 ragged", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 160, 100, 64, 64,
+                                           LA_FEATURE_ELU1, LA_BF16, 0),
+           LA_OK, L_CUMSUM_FWD);
+    expect("fwd bad feature", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 160, 100, 64, 64,
+                                           (la_feature)9, LA_BF16, 0),
+           LA_ERR_INVALID, 0);
+    expect("bwd fp32 d128", la_chunk_bwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), A(8), A(9), A(10), F(11),
+                                         F(12), 160, 128, 128, 64, LA_FEATURE_NONE, LA_F32, 0),
+           LA_OK, L_CUMSUM_BWD);
+    expect("bwd cumsum ragged", la_chunk_bwd(A(0), A(1), A(2), nullptr, nullptr, A(5), nullptr, nullptr, A(8), A(9),
+                                             A(10), F(11), F(12), 3, 37, 64, 1, LA_FEATURE_ELU1, LA_BF16, 0),
+           LA_OK, L_CUMSUM_BWD);
+    expect("bwd elu1 headline", la_chunk_bwd(A(0), A(1), A(2), F(3), F(4), A(5), nullptr, nullptr, A(8), A(9), A(10),
+                                             F(11), F(12), 160, 128, 64, 64, LA_FEATURE_ELU1, LA_BF16, 0),
+           LA_OK, L_BWD_C128);
+    expect("seq block 1", la_seq_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), F(8), F(9), 4, 512, 64, 128, 1,
+                                     LA_FEATURE_NONE, LA_BF16, 0),
+           LA_ERR_UNSUPPORTED, 0);
 
     // ---- sequence calls
     expect("seq fwd d64",
@@ -154,7 +180,7 @@ int main() {
         printf("FAIL la_time_next_launch\n");
         ++failures;
     }
-    if (!la_kernel_name(1, LA_BF16, 128, 64) || la_kernel_name(1, LA_F32, 128, 96) ||
+    if (!la_kernel_name(1, LA_BF16, 128, 64, 64, LA_FEATURE_NONE) || la_kernel_name(1, LA_F32, 128, 96, 64, LA_FEATURE_NONE) ||
         !la_seq_kernel_name(0, LA_BF16, 128, 128, LA_FEATURE_ELU1))
         ++failures;
 

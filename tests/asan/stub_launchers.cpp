@@ -12,7 +12,7 @@ namespace lachunk {
 
 enum : int {
     L_FWD = 1, L_BWD, L_FWD_C128, L_BWD_C128, L_SEQ_FWD_C128, L_SEQ_BWD_C128, L_SEQ_FWD_D128, L_SEQ_BWD_D128,
-    L_CE_FWD, L_CE_BWD, L_CE_FWD_NOALLOC, L_FLOOR
+    L_CE_FWD, L_CE_BWD, L_CE_FWD_NOALLOC, L_FLOOR, L_CUMSUM_FWD, L_CUMSUM_BWD
 };
 
 static hipError_t hit(int id) {
@@ -53,14 +53,37 @@ template hipError_t launch_bwd<__bf16, 128>(const void *, const void *, const vo
                                             float *, float *, int, int, hipStream_t, const hipEvent_t *);
 
 hipError_t launch_fwd_c128(const void *, const void *, const void *, const float *, const float *, void *, float *,
-                           float *, int, hipStream_t, const hipEvent_t *) {
+                           float *, int, bool, hipStream_t, const hipEvent_t *) {
     return hit(L_FWD_C128);
 }
 hipError_t launch_bwd_c128(const void *, const void *, const void *, const float *, const float *, const void *,
-                           const float *, const float *, void *, void *, void *, float *, float *, int, hipStream_t,
-                           const hipEvent_t *) {
+                           const float *, const float *, void *, void *, void *, float *, float *, int, bool,
+                           hipStream_t, const hipEvent_t *) {
     return hit(L_BWD_C128);
 }
+template <typename T, int D>
+hipError_t launch_cumsum_fwd(const void *, const void *, const void *, const float *, const float *, void *, float *,
+                             float *, int, int, bool, hipStream_t, const hipEvent_t *) {
+    return hit(L_CUMSUM_FWD);
+}
+template <typename T, int D>
+hipError_t launch_cumsum_bwd(const void *, const void *, const void *, const float *, const float *, const void *,
+                             const float *, const float *, void *, void *, void *, float *, float *, int, int, bool,
+                             hipStream_t, const hipEvent_t *) {
+    return hit(L_CUMSUM_BWD);
+}
+#define STUB_CUMSUM(T, D)                                                                                          \
+    template hipError_t launch_cumsum_fwd<T, D>(const void *, const void *, const void *, const float *,          \
+                                                const float *, void *, float *, float *, int, int, bool,          \
+                                                hipStream_t, const hipEvent_t *);                                  \
+    template hipError_t launch_cumsum_bwd<T, D>(const void *, const void *, const void *, const float *,          \
+                                                const float *, const void *, const float *, const float *, void *, \
+                                                void *, void *, float *, float *, int, int, bool, hipStream_t,     \
+                                                const hipEvent_t *);
+STUB_CUMSUM(float, 64)
+STUB_CUMSUM(float, 128)
+STUB_CUMSUM(__bf16, 64)
+STUB_CUMSUM(__bf16, 128)
 hipError_t launch_seq_fwd_c128(const void *, const void *, const void *, const float *, const float *, void *,
                                float *, float *, float *, float *, int, int, bool, hipStream_t, const hipEvent_t *) {
     return hit(L_SEQ_FWD_C128);

@@ -53,8 +53,19 @@ def test_kernel_names(lib):
     assert lac.kernel_name(True, "bf16", 128, 64) == "la_bwd_c128w16_kernel"
     assert lac.kernel_name(False, "bf16", 100, 128) == "la_fwd_kernel"
     assert lac.kernel_name(True, "float32", 128, 64) == "la_bwd_kernel"
-    assert lac.kernel_name(True, "float32", 128, 128) is None
+    # the fp32 backward at D = 128 runs the per-token form
+    assert lac.kernel_name(True, "float32", 128, 128) == "la_cumsum_bwd_kernel"
+    assert lac.kernel_name(False, "float32", 128, 128) == "la_fwd_kernel"
     assert lac.kernel_name(False, "bf16", 128, 96) is None
+    # block 1: the cumsum form on every shape; the fused map: the 128-token kernels at their
+    # shape, the per-token form elsewhere
+    assert lac.kernel_name(False, "bf16", 128, 64, block=1) == "la_cumsum_fwd_kernel"
+    assert lac.kernel_name(True, "float32", 37, 128, block=1) == "la_cumsum_bwd_kernel"
+    assert lac.kernel_name(False, "bf16", 128, 64, feature="elu1") == "la_fwd_c128_elu1_kernel"
+    assert lac.kernel_name(True, "bf16", 128, 64, feature="elu1") == "la_bwd_c128w16_elu1_kernel"
+    assert lac.kernel_name(True, "bf16", 100, 64, feature="elu1") == "la_cumsum_bwd_kernel"
+    assert lac.kernel_name(True, "bf16", lac.BWD_MAX_C + 1, 64, block=1) is None
+    assert lac.kernel_name(False, "bf16", 128, 64, block=16) is None
 
 
 def test_sequence_limits_match_the_header():
@@ -64,7 +75,7 @@ def test_sequence_limits_match_the_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lac.abi_version() == 5
+    assert lac.abi_version() == 6
     for s in range(6):
         assert len(lac.status_str(s)) > 0
     assert lac.status_str(99) == "unknown status"
@@ -79,24 +90,25 @@ def addr(i):
     return ctypes.c_void_p(BASE + i * STEP)
 
 
-def fwd_call(lib, G=4, C=128, D=64, block=64, dt=1, **over):
+def fwd_call(lib, G=4, C=128, D=64, block=64, dt=1, feature=0, **over):
     args = {n: addr(i) for i, n in enumerate(["q", "k", "v", "S_in", "z_in", "o", "S_out", "z_out"])}
     args.update(over)
     return lib.la_chunk_fwd(args["q"], args["k"], args["v"], args["S_in"], args["z_in"], args["o"],
-                            args["S_out"], args["z_out"], G, C, D, block, dt, None)
+                            args["S_out"], args["z_out"], G, C, D, block, feature, dt, None)
 
 
-def bwd_call(lib, G=4, C=128, D=64, block=64, dt=1, **over):
+def bwd_call(lib, G=4, C=128, D=64, block=64, dt=1, feature=0, **over):
     names = ["q", "k", "v", "S_in", "z_in", "dO", "dS_out", "dz_out", "dq", "dk", "dv", "dS_in", "dz_in"]
     args = {n: addr(i) for i, n in enumerate(names)}
     args.update(over)
-    return lib.la_chunk_bwd(*[args[n] for n in names], G, C, D, block, dt, None)
+    return lib.la_chunk_bwd(*[args[n] for n in names], G, C, D, block, feature, dt, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(G=0), INVALID), (dict(C=0), INVALID), (dict(G=-3), INVALID),
     (dict(D=32), UNSUPPORTED), (dict(D=96), UNSUPPORTED), (dict(block=32), UNSUPPORTED),
-    (dict(dt=7), UNSUPPORTED),
+    (dict(block=2), UNSUPPORTED), (dict(block=0), UNSUPPORTED), (dict(dt=7), UNSUPPORTED),
+    (dict(feature=2), INVALID), (dict(feature=-1, block=1), INVALID),
     (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(S_out=None), INVALID),
     (dict(S_in=None), INVALID),                          # z_in given without S_in
     (dict(q=ctypes.c_void_p(BASE + 8)), ALIGN),
@@ -114,8 +126,8 @@ def test_fwd_size_overflow(lib):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(G=0), INVALID), (dict(D=48), UNSUPPORTED), (dict(block=16), UNSUPPORTED),
-    (dict(C=lac.BWD_MAX_C + 1), UNSUPPORTED),
-    (dict(dt=0, D=128), UNSUPPORTED),                    # fp32 backward at D=128
+    (dict(C=lac.BWD_MAX_C + 1), UNSUPPORTED), (dict(C=lac.BWD_MAX_C + 1, block=1), UNSUPPORTED),
+    (dict(feature=3), INVALID),
     (dict(dO=None), INVALID), (dict(dS_in=None), INVALID),
     (dict(dS_out=None), INVALID),                        # dz_out without dS_out
     (dict(z_in=None), INVALID),

@@ -16,19 +16,19 @@ from tol import RTOL, check
 pytestmark = pytest.mark.gpu
 
 
-def _case(dtype, carry, upstream, G=3, T=300, D=64, chunk=128, seed=11, feature_map=None):
+def _case(dtype, carry, upstream, G=3, T=300, D=64, chunk=128, seed=11, feature_map=None, impl=None):
     I = inp.make_inputs(G=G, T=T, D=D, dtype=dtype, carry=carry, backward=True, seed=seed,
                         features="raw" if feature_map else "mapped")
     rng = np.random.default_rng(seed + 1)
     dS = torch.from_numpy(rng.standard_normal((G, D, D)).astype(np.float32)) if upstream else None
     dz = torch.from_numpy(rng.standard_normal((G, D)).astype(np.float32)) if upstream else None
-    print(f"[case] autograd dtype={dtype} carry={carry} upstream={upstream} G={G} T={T} D={D} chunk={chunk}",
-          flush=True)
+    print(f"[case] autograd dtype={dtype} carry={carry} upstream={upstream} G={G} T={T} D={D} chunk={chunk} "
+          f"feature_map={feature_map} impl={impl}", flush=True)
     dev = "cuda:0"
     leaf = lambda x: None if x is None else x.to(dev).clone().requires_grad_(True)
     q, k, v = leaf(I["q"]), leaf(I["k"]), leaf(I["v"])
     S_in, z_in = leaf(I["S_in"]), leaf(I["z_in"])
-    o, (S_out, z_out) = lac.linear_attention(q, k, v, S_in, z_in, chunk=chunk, feature_map=feature_map)
+    o, (S_out, z_out) = lac.linear_attention(q, k, v, S_in, z_in, chunk=chunk, feature_map=feature_map, impl=impl)
     loss = (o.float() * I["dO"].to(dev).float()).sum()
     if upstream:
         loss = loss + (S_out * dS.to(dev)).sum() + (z_out * dz.to(dev)).sum()
@@ -89,6 +89,22 @@ def test_autograd_fused_feature_map_wide_heads(gpu):
     _case("bf16", "zero", True, G=2, T=230, D=128, feature_map="elu1")
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f32", 64), ("f32", 128)])
+def test_autograd_cumsum_impl(gpu, dtype, D):
+    # the per-token form chunk by chunk (block 1 in the chunk calls), ragged last chunk
+    _case(dtype, "prior", True, G=2, T=200, D=D, chunk=128, impl="cumsum")
+
+
+def test_autograd_fused_map_chunk_impl(gpu):
+    # the map on the chunk path: a ragged D = 64 sequence (the sequence calls take whole chunks only)
+    _case("bf16", "prior", True, G=3, T=300, feature_map="elu1", impl="chunk")
+    _case("bf16", "zero", False, G=2, T=256, feature_map="elu1", impl="chunk")
+
+
+def test_autograd_fused_map_cumsum_impl(gpu):
+    _case("f32", "prior", True, G=2, T=150, D=128, chunk=64, feature_map="elu1", impl="cumsum")
+
+
 def _grads(I, dO, impl, D):
     dev = "cuda:0"
     leaf = lambda x: x.to(dev).clone().requires_grad_(True)
@@ -109,12 +125,12 @@ def test_autograd_impls_agree(gpu, T, D):
     print(f"[case] autograd impls seq vs chunk G={G} T={T} D={D}", flush=True)
     I = inp.make_inputs(G=G, T=T, D=D, dtype="bf16", carry="prior", backward=True, seed=90 + D)
     dO = I["dO"].to("cuda:0").float()
-    a, b = _grads(I, dO, "seq", D), _grads(I, dO, "chunk", D)
+    a, b, c = _grads(I, dO, "seq", D), _grads(I, dO, "chunk", D), _grads(I, dO, "cumsum", D)
     for name in a:
-        x, y = a[name].double(), b[name].double()
-        rel = float((x - y).norm() / y.norm())
-        print(f"  {name}: seq vs chunk normwise {rel:.2e}", flush=True)
-        assert rel < 2e-3, (name, rel)
+        x, y, u = a[name].double(), b[name].double(), c[name].double()
+        rel, relc = float((x - y).norm() / y.norm()), float((u - y).norm() / y.norm())
+        print(f"  {name}: seq vs chunk normwise {rel:.2e}, cumsum vs chunk {relc:.2e}", flush=True)
+        assert rel < 2e-3 and relc < 2e-3, (name, rel, relc)
     lac.set_attention_impl("chunk")
     try:
         c = _grads(I, dO, None, D)  # the default from the setter
@@ -129,5 +145,5 @@ def test_autograd_impl_seq_rejects_unsupported(gpu):
     with pytest.raises(ValueError, match="impl='seq'"):
         lac.linear_attention(q, q, q, impl="seq")
     x = torch.ones(2, 256, 64, dtype=torch.bfloat16, device="cuda:0")
-    with pytest.raises(ValueError, match="impl='chunk'"):
-        lac.linear_attention(x, x, x, feature_map="elu1", impl="chunk")
+    with pytest.raises(ValueError, match="unknown feature map"):
+        lac.linear_attention(x, x, x, feature_map="relu", impl="chunk")

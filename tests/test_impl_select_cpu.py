@@ -1,6 +1,6 @@
 """The selectable attention implementation of the autograd layer (host logic only): the
 explicit argument, set_attention_impl and the LACHUNK_ATTN_IMPL environment variable, in that
-order of precedence, and the errors for unknown names and for the fused map on the chunk path."""
+order of precedence, and the errors for unknown names."""
 import pytest
 import torch
 
@@ -18,7 +18,7 @@ def reset(monkeypatch):
 
 def test_default_is_auto():
     assert lac.get_attention_impl() == "auto"
-    assert set(lac.IMPLS) == {"auto", "seq", "chunk"}
+    assert set(lac.IMPLS) == {"auto", "seq", "chunk", "cumsum"}
 
 
 def test_environment_then_setter(monkeypatch):
@@ -33,7 +33,7 @@ def test_environment_then_setter(monkeypatch):
 def test_unknown_names_raise(monkeypatch):
     with pytest.raises(ValueError, match="unknown attention implementation"):
         lac.set_attention_impl("einsum")
-    monkeypatch.setenv(ag.IMPL_ENV, "cumsum")
+    monkeypatch.setenv(ag.IMPL_ENV, "einsum")
     with pytest.raises(ValueError, match=ag.IMPL_ENV):
         lac.get_attention_impl()
 
