@@ -252,35 +252,37 @@ __device__ __forceinline__ void bwd_c128_body(
         } else {
             state_step(0);
         }
-        // pass-1 operands: this wave's queries (row t = r, k = feature) and its two key tiles
-        bf16x8 qf[2], df[2], kfr[2][2], vfr[2][2];
+        // pass-1 operands: this wave's queries (row t = r, k = feature)
+        bf16x8 qf[2], df[2];
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
             qf[kc] = tfrag(tile(L::QT, blk), TL, tq, kc);
             df[kc] = tfrag(tile(L::GT, blk), TL, tq, kc);
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                kfr[jj][kc] = tfrag(tile(L::KT, blk), TL, 2 * h + jj, kc);
-                vfr[jj][kc] = tfrag(tile(L::VT, blk), TL, 2 * h + jj, kc);
-            }
         }
-        // A^T, G^T (lane: query t = r, key j = 16 (2h + jj) + 4g + i), masked to j <= t
+        // A^T, G^T (lane: query t = r, key j = 16 (2h + jj) + 4g + i), masked to j <= t.  Key tile
+        // j4 = 2h + jj lies below the query tile's diagonal (j4 < tq: no mask), on it (j4 == tq:
+        // masked per element) or above it (j4 > tq: zero).  A one-chunk launch skips the products
+        // of the tiles above the diagonal (uniform per wave); the sequence loop, short of
+        // registers, computes every tile and masks them all.
         floatx4 aT[2], gT[2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             aT[jj] = zero4();
             gT[jj] = zero4();
+            const int j4 = 2 * h + jj;
+            if (!SEQ && j4 > tq) continue;
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
-                mma(aT[jj], kfr[jj][kc], qf[kc]);
-                mma(gT[jj], vfr[jj][kc], df[kc]);
+                mma(aT[jj], tfrag(tile(L::KT, blk), TL, j4, kc), qf[kc]);
+                mma(gT[jj], tfrag(tile(L::VT, blk), TL, j4, kc), df[kc]);
             }
-            const int j4 = 2 * h + jj;
+            if (SEQ || j4 == tq) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool keep = j4 < tq || (j4 == tq && 4 * g + e <= r);
-                aT[jj][e] = keep ? aT[jj][e] : 0.f;
-                gT[jj][e] = keep ? gT[jj][e] : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    const bool keep = j4 < tq || (j4 == tq && 4 * g + e <= r);
+                    aT[jj][e] = keep ? aT[jj][e] : 0.f;
+                    gT[jj][e] = keep ? gT[jj][e] : 0.f;
+                }
             }
         }
         if (SEQ) {
@@ -329,12 +331,14 @@ __device__ __forceinline__ void bwd_c128_body(
                 }
             }
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
+            for (int jj = 0; jj < 2; ++jj) {
+                if (!SEQ && 2 * h + jj > tq) continue;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     dpart += aT[jj][e];
                     rpart += aT[jj][e] * gT[jj][e];
                 }
+            }
             const float dsum = gsum(dpart), rsum = gsum(rpart);
             if (g == 0) psum[(u * 2 + h) * 16 + r] = floatx2{dsum, rsum};
         }
@@ -350,18 +354,22 @@ __device__ __forceinline__ void bwd_c128_body(
             inv = __builtin_amdgcn_rcpf(den);
             const float rho = (mine[1] + other[1]) * inv;
             dden = -rho * inv;
-            // dP^T[j][t] = inv (G - rho), masked; split; stored [t][j] for dq and pass 2
-            floatx4 d[2];
+            // dP^T[j][t] = inv (G - rho), masked; split; stored [t][j] for dq and pass 2 (the tiles
+            // above the diagonal as zeros: pass 2 reads them within its 32-query slabs)
+            Split8 dps{};
+            if (SEQ || 2 * h <= tq) {
+                floatx4 d[2];
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int j4 = 2 * h + jj;
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int j4 = 2 * h + jj;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool keep = j4 < tq || (j4 == tq && 4 * g + e <= r);
-                    d[jj][e] = keep ? (gT[jj][e] - rho) * inv : 0.f;
+                    for (int e = 0; e < 4; ++e) {
+                        const bool keep = j4 < tq || (j4 == tq && 4 * g + e <= r);
+                        d[jj][e] = keep ? (gT[jj][e] - rho) * inv : 0.f;
+                    }
                 }
+                dps = split_acc(d[0], d[1]);
             }
-            const Split8 dps = split_acc(d[0], d[1]);
             tstore_frag_at(tile1(L::DP, 2 * blk), TL1, tq, h, dps.hi);
             tstore_frag_at(tile1(L::DP, 2 * blk + 1), TL1, tq, h, dps.lo);
             if (h == 0 && g == 0) {
@@ -378,9 +386,12 @@ __device__ __forceinline__ void bwd_c128_body(
 
         // ---- phase 4.  dq^T[p][t] = sum_j K^T[p][j] dP[t][j] + inv H^T[p][t] + dden z_b[p]
         {
+            // key chunk jc (keys 32 jc .. 32 jc + 31) holds keys at or before the query tile iff
+            // 2 jc <= tq (uniform); the other's dP is zero
             bf16x8 dph[2], dpl[2], ktr[2][2];
 #pragma unroll
             for (int jc = 0; jc < 2; ++jc) {
+                if (!SEQ && 2 * jc > tq) continue;
                 dph[jc] = tfrag(tile1(L::DP, 2 * blk), TL1, tq, jc);
                 dpl[jc] = tfrag(tile1(L::DP, 2 * blk + 1), TL1, tq, jc);
 #pragma unroll
@@ -392,12 +403,19 @@ __device__ __forceinline__ void bwd_c128_body(
                 floatx4 acc = hT[pp] * inv + dden * zv[pp];
 #pragma unroll
                 for (int jc = 0; jc < 2; ++jc) {
+                    if (!SEQ && 2 * jc > tq) continue;
                     mma(acc, ktr[pp][jc], dph[jc]);
                     mma(acc, ktr[pp][jc], dpl[jc]);
                 }
                 // fused feature map: the gradient of the raw query is dq phi'(x), phi' = min(1, phi)
                 if constexpr (FM) acc *= elu1_grad4(lds_b64(tile(L::QT, blk) + tq * 16 * TROW + TL.nat_at(2 * h + pp)));
-                store_bf16x4<!SEQ>(dqrow + 16 * (2 * h + pp), pack4(acc));
+                if constexpr (SEQ) {
+                    store_bf16x4<false>(dqrow + 16 * (2 * h + pp), pack4(acc));
+                } else {
+                    // staged into the S_1 copy's tile of this block (no longer read): the two
+                    // halves of each row meet there, and whole rows go out in phase 5
+                    tstore_acc(smem + L::SS + (2 + blk) * TBYTES, TL.nat_at(2 * h + pp), tq, pack4(acc));
+                }
             }
         }
         // reverse state: Sh += Q_b^T dN_b as C[c][p] = sum_t dN[t][c] Q[t][p], zh += Q_b^T dden_b;
@@ -492,7 +510,7 @@ __device__ __forceinline__ void bwd_c128_body(
             };
             if (inter_phase) {  // phase 5, block 0: against Sh_0
                 inter(tile1(L::SS, 0), tile1(L::SS, 1), TL1);
-                store();
+                if constexpr (SEQ) store();
                 return;
             }
 #pragma unroll
@@ -537,7 +555,7 @@ __device__ __forceinline__ void bwd_c128_body(
             }
             if (B == 1) {  // block 1 completes here, against Sh_1 = dS_out
                 if (has_up) inter(tile2(L::SH1, 0), tile2(L::SH1, 1), TL2);
-                store();
+                if constexpr (SEQ) store();
             }
         };
         using T1 = std::integral_constant<bool, true>;
@@ -557,17 +575,56 @@ __device__ __forceinline__ void bwd_c128_body(
         lds_barrier();  // Sh_0, zh_0 visible
 
         // ---- phase 5
+        const int tl = tid_c & 511;  // a thread's 16-byte piece of a staged tile: row tl / 8
+        if constexpr (!SEQ) {
+            // dq: whole 128-byte rows (8 threads per row), block sb of the staged tiles
+            const bf16x8 x = *reinterpret_cast<const bf16x8 *>(smem + L::SS + (2 + sb) * TBYTES + stage_off(tl));
+            __builtin_nontemporal_store(x, reinterpret_cast<bf16x8 *>(dq + (tok0 + 64 * sb + (tl >> 3)) * D + 8 * (tl & 7)));
+        }
         if (p2b == 0) {
             if (p2dk) pass2(T1{}, B0{}, true, acc, kv);
             else pass2(F1{}, B0{}, true, acc, kv);
         }
         reverse(0);
+        if constexpr (!SEQ) {
+            // every output staged in LDS regions no longer read (phase 5 reads none of them) and
+            // stored in whole lines after one more barrier: dv_b, dk_b as bf16 tiles in the dP
+            // region (tiles dv_0, dv_1, dk_0, dk_1), dS_in as fp32 rows of 256 bytes in the
+            // upstream state's region, 16-byte units XOR-swizzled by row (conflict-free writes)
+            {
+                const int B = p2b, jt = p2dk ? 3 - (w & 3) : (w & 3);
+                char *dst = smem + L::DP + ((p2dk ? 2 : 0) + B) * TBYTES;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    floatx4 y = acc[x];
+                    if (p2dk) {
+                        y += f4(L::ZH + 4 * (64 * B + 16 * x));
+                        if constexpr (FM) y *= elu1_grad4(lds_b64(tile(L::KT, B) + jt * 16 * TROW + TL.nat[x]));
+                    }
+                    tstore_acc(dst, TL.nat[x], jt, pack4(y));
+                }
+                const int p = 16 * pt + r;
+                *reinterpret_cast<floatx4 *>(smem + L::SH1 + p * 256 + 16 * ((4 * ct + g) ^ (p & 15))) = Sh;
+            }
+            lds_barrier();
+            const uint32_t so = stage_off(tl);
+            const size_t row = tok0 + 64 * sb + (tl >> 3);
+            const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(smem + L::DP + sb * TBYTES + so);
+            const bf16x8 xk = *reinterpret_cast<const bf16x8 *>(smem + L::DP + (2 + sb) * TBYTES + so);
+            __builtin_nontemporal_store(xv, reinterpret_cast<bf16x8 *>(dv + row * D + 8 * (tl & 7)));
+            __builtin_nontemporal_store(xk, reinterpret_cast<bf16x8 *>(dk + row * D + 8 * (tl & 7)));
+            const int p = tid_c >> 4, un = tid_c & 15;  // dS_in: 16 threads per 256-byte row
+            const floatx4 xs = *reinterpret_cast<const floatx4 *>(smem + L::SH1 + p * 256 + 16 * (un ^ (p & 15)));
+            __builtin_nontemporal_store(xs, reinterpret_cast<floatx4 *>(dS_in + ((size_t)grp * D + p) * D + 4 * un));
+        }
         // the tiles the next chunk's phase 0 writes are read up to here
         if (SEQ && c > 0) lds_barrier();
     }  // chunk loop
     {
         const int p = 16 * pt + r;
-        __builtin_nontemporal_store(Sh, reinterpret_cast<floatx4 *>(dS_in + ((size_t)grp * D + p) * D + 16 * ct + 4 * g));
+        if (SEQ)
+            __builtin_nontemporal_store(Sh,
+                                        reinterpret_cast<floatx4 *>(dS_in + ((size_t)grp * D + p) * D + 16 * ct + 4 * g));
         if (ct == 0 && g == 0) __builtin_nontemporal_store(zhr[0], dz_in + (size_t)grp * D + p);
     }
 }

@@ -15,10 +15,13 @@
 // ct).  Block 0 and the state are loaded first and block 1's keys and values last, so
 // that block 0's outputs are computed while the rest arrives.  Three phases separated by
 // two barriers:
-//   A  stage block 0's K, V; write the bf16 copy of S_0 and the split row of z_0
+//   A  stage block 0's K, V (and, in a one-chunk launch, block 1's); write the bf16 copy of S_0
+//      and the split row of z_0
 //   B  S_1 (copy + split z_1); block 0's outputs (scores, fp32 row sums, intra-block and
-//      inter-block numerator, o stored); stage block 1's K, V
-//   C  block 1's outputs against S_1; S_out = S_1 + K_1^T V_1 stored.
+//      inter-block numerator, o stored); block 1's waves: the intra-block part of their outputs
+//      (one-chunk launch) or the staging of block 1's K, V (sequence mode)
+//   C  block 1's outputs against S_1 (the inter-block part, one-chunk launch);
+//      S_out = S_1 + K_1^T V_1 stored.
 // The row sums of P come straight from the fp32 accumulators (lanes hold one query
 // each); P enters the numerator MFMA as a split hi + lo operand; the state copy is
 // a plain bf16 operand (its term has no cancellation against the others); z_b is a
@@ -255,7 +258,8 @@ __device__ __forceinline__ void fwd_c128_body(
                 nq[kc] = ldfrag_g<bf16>(qr, (uint32_t)(c + 1) * C * D + (64 * blk + 16 * tq) * D + 32 * kc, D, lane);
         }
 
-        // ---- phase A: block 0's keys and values, the S_0 copy and z_0 row
+        // ---- phase A: block 0's keys and values, the S_0 copy and z_0 row; in a one-chunk launch
+        // block 1's keys and values too (they arrive while block 0's are staged)
         *reinterpret_cast<bf16x8 *>(Kt + so) = FM ? elu1_8(kst0) : kst0;
         *reinterpret_cast<bf16x8 *>(Vt + so) = vst0;
         if (SEQ) {
@@ -263,23 +267,34 @@ __device__ __forceinline__ void fwd_c128_body(
             vst0 = gload<bf16x8>(vr, nb + tid * 16);
         }
         write_state(0);
+        if constexpr (!SEQ) {
+            *reinterpret_cast<bf16x8 *>(Kt + TBYTES + so) = FM ? elu1_8(kst1) : kst1;
+            *reinterpret_cast<bf16x8 *>(Vt + TBYTES + so) = vst1;
+        }
         lds_barrier();
 
-        // ---- phase B: S_1 (copy, z_1 row); block 0's outputs (their state S_0 is ready);
-        // then block 1's keys and values, by now arrived
+        // ---- phase B: S_1 (copy, z_1 row); block 0's outputs (their state S_0 is ready).  In a
+        // one-chunk launch block 1's waves compute the intra-block part of their outputs meanwhile
+        // (it needs no state); in sequence mode they stage block 1's keys and values, by now arrived.
         advance(0);
         write_state(1);
+        Part pa1;
         if (blk == 0) outputs(Blk0{});
-        *reinterpret_cast<bf16x8 *>(Kt + TBYTES + so) = FM ? elu1_8(kst1) : kst1;
-        *reinterpret_cast<bf16x8 *>(Vt + TBYTES + so) = vst1;
-        if (SEQ) {
+        else if (!SEQ) intra(Blk1{}, pa1);
+        if constexpr (SEQ) {
+            *reinterpret_cast<bf16x8 *>(Kt + TBYTES + so) = FM ? elu1_8(kst1) : kst1;
+            *reinterpret_cast<bf16x8 *>(Vt + TBYTES + so) = vst1;
             kst1 = gload<bf16x8>(kr, nb + TBYTES + tid * 16);
             vst1 = gload<bf16x8>(vr, nb + TBYTES + tid * 16);
         }
         lds_barrier();
 
-        // ---- phase C: block 1's outputs; the state after the chunk, S_1 + K_1^T V_1
-        if (blk == 1) outputs(Blk1{});
+        // ---- phase C: block 1's outputs (the inter-block part against S_1 only, in a one-chunk
+        // launch); the state after the chunk, S_1 + K_1^T V_1
+        if (blk == 1) {
+            if constexpr (SEQ) outputs(Blk1{});
+            else finish(Blk1{}, pa1);
+        }
         advance(1);
         if (SEQ) {
             qf[0] = nq[0];
