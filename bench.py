@@ -413,22 +413,27 @@ def bench_floors(args, torch, lac, nwg=160):
     `nwg` workgroups, on buffers rotated over the same footprint as the benchmark.  Each is timed
     as the attention kernels are: back to back from Python, replayed from HIP graphs, and one
     launch at a time between dispatch-bound events; and the two streaming kernels back to back
-    as a step, the floor of a step of the two attention launches."""
+    as a step, the floor of a step of the two attention launches.  The same bytes again over four
+    times the workgroups (128 threads each instead of 512): whether more workgroups lower it."""
     ib, ob = 81920 * nwg, 65536 * nwg  # the larger (backward) shape's bytes; the forward uses less
     nsets = max(2, math.ceil(args.footprint_mb * 1e6 / (ib + ob)))
     dev = "cuda:0"
     sets = [(torch.empty(ib, dtype=torch.uint8, device=dev).fill_(1), torch.empty(ob, dtype=torch.uint8, device=dev))
             for _ in range(nsets)]
     algo = {"empty": 0, "fwd": (65536 + 32768) * nwg, "bwd": (81920 + 65536) * nwg}
+    algo.update(fwd_small=algo["fwd"], bwd_small=algo["bwd"])
+    wgs = {"empty": nwg, "fwd": nwg, "bwd": nwg, "fwd_small": 4 * nwg, "bwd_small": 4 * nwg}  # same bytes
     K = args.steps
     out = {"floors": {}, "nwg": nwg, "threads": 512, "buffer_sets": nsets,
            "footprint_mb": round(nsets * (ib + ob) / 1e6, 1), "steps": K,
            "kernels": {k: lac.FLOOR_NAMES[lac.FLOOR_KINDS[k]] for k in lac.FLOOR_KINDS}}
-    cases = [("empty", ["empty"]), ("fwd", ["fwd"]), ("bwd", ["bwd"]), ("fwd+bwd step", ["fwd", "bwd"])]
+    cases = [("empty", ["empty"]), ("fwd", ["fwd"]), ("bwd", ["bwd"]), ("fwd+bwd step", ["fwd", "bwd"]),
+             ("fwd, 4x workgroups", ["fwd_small"]), ("bwd, 4x workgroups", ["bwd_small"]),
+             ("fwd+bwd step, 4x workgroups", ["fwd_small", "bwd_small"])]
     for label, kinds in cases:
         def step_on(j, kinds=kinds):
             for kd in kinds:
-                lac.floor_launch(kd, nwg, sets[j][0], sets[j][1])
+                lac.floor_launch(kd, wgs[kd], sets[j][0], sets[j][1])
         for i in range(args.warmup):
             step_on(i % nsets)
         plain, _, _ = timed_block_runs(torch, lambda i0, n: [step_on(i % nsets) for i in range(i0, i0 + n)], K)
@@ -449,7 +454,8 @@ def bench_floors(args, torch, lac, nwg=160):
             r.update({"dispatch_events_avg_us": sum(d) / K, "dispatch_events_median_us": d[K // 2],
                       "bytes": algo[kinds[0]]})
         else:
-            r["bytes"] = algo["fwd"] + algo["bwd"]
+            r["bytes"] = sum(algo[kd] for kd in kinds)
+        r["workgroups"] = [wgs[kd] for kd in kinds]
         if r["bytes"]:
             r["graph_frac_of_8TBs"] = r["bytes"] / (r["graph_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS
         out["floors"][label] = r
@@ -494,6 +500,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seq", action="store_true",
                     help="run the workload through the sequence entry points (one launch per direction)")
+    ap.add_argument("--block", type=int, choices=[1, 64], default=None,
+                    help="chunk entry points: 64, the blocked (chunked) form; 1, the cumsum form "
+                         "(the per-token recurrence); default the workload's")
     ap.add_argument("--feature", choices=["elu1"], default=None,
                     help="with --seq: raw q, k in, the feature map elu(x)+1 fused into the kernels")
     ap.add_argument("--footprint-mb", type=float, default=640.0)
@@ -516,11 +525,13 @@ def main():
         import causal_linear_attention_chunked_amd as lac
         from causal_linear_attention_chunked_amd import inputs as inp
         w = inp.workload(args.workload)
-        names = {lac.kernel_name(b, w.dtype, C, w.D) for b in (False, True) for C in set(w.chunks)}
+        names = {lac.kernel_name(b, w.dtype, C, w.D, blk, f) for b in (False, True) for C in set(w.chunks)
+                 for blk in (1, 64) for f in (None, "elu1")} - {None}
         names |= {lac.seq_kernel_name(b, w.dtype, max(w.chunks), w.D, f) for b in (False, True)
                   for f in (None, "elu1")} - {None}
         counters_summary(args.counters_summary, w.name + ("_seq" if args.seq else "")
-                         + (f"_{args.feature}" if args.feature else ""), sorted(names))
+                         + (f"_{args.feature}" if args.feature else "")
+                         + ("_block1" if args.block == 1 else ""), sorted(names))
         return
     import torch
     if args.copy_calibration:
@@ -537,8 +548,9 @@ def main():
     w = inp.workload(args.workload)
     if not w.backward:
         raise SystemExit("bench.py times forward+backward workloads")
-    if args.feature and not args.seq:
-        raise SystemExit("--feature runs through the sequence entry points: add --seq")
+    block = w.block if args.block is None else args.block
+    if args.seq and block != 64:
+        raise SystemExit("--seq runs the blocked form (block 64) only")
     I = inp.make_inputs(G=w.G, T=w.T, D=w.D, dtype=w.dtype, carry=w.carry, backward=w.backward, seed=w.seed,
                         prior_len=w.prior_len, features="raw" if args.feature else "mapped")
     dev = torch.device("cuda:0")
@@ -548,7 +560,8 @@ def main():
     n = len(bounds)
     carry = I["S_in"] is not None
 
-    tname = w.name + ("_seq" if args.seq else "") + (f"_{args.feature}" if args.feature else "")  # and the traffic file
+    tname = (w.name + ("_seq" if args.seq else "") + (f"_{args.feature}" if args.feature else "")
+             + ("_block1" if block == 1 else ""))  # and the traffic file
     if args.seq:
         # equal chunks but for a shorter last one
         regular = len(set(w.chunks[:-1])) <= 1 and w.chunks[-1] <= w.chunks[0]
@@ -607,11 +620,11 @@ def main():
         c = s["chunks"][i]
         S, z = carry_in(s, i)
         if kind == "fwd":
-            lac.fwd(c["q"], c["k"], c["v"], S, z, out=c["fout"])
+            lac.fwd(c["q"], c["k"], c["v"], S, z, block=block, out=c["fout"], feature=args.feature)
         else:
             up = s["chunks"][i + 1]["bout"] if i + 1 < n else None
             lac.bwd(c["q"], c["k"], c["v"], S, z, c["dO"], None if up is None else up[3],
-                    None if up is None else up[4], out=c["bout"])
+                    None if up is None else up[4], block=block, out=c["bout"], feature=args.feature)
 
     def step(s):
         for kind, _, _, i in launches:
@@ -680,7 +693,7 @@ def main():
         for (kind, C, b, _), e in zip(launches, ev[i]):
             name = (lac.seq_kernel_name(kind == "seqbwd", w.dtype, max(w.chunks), D, args.feature)
                     if kind.startswith("seq")
-                    else lac.kernel_name(kind == "bwd", w.dtype, C, D))
+                    else lac.kernel_name(kind == "bwd", w.dtype, C, D, block, args.feature))
             p = per.setdefault(name, {"launches": 0, "bytes": 0, "ms": 0.0})
             p["launches"] += 1
             p["bytes"] += b
@@ -695,13 +708,13 @@ def main():
     top = max(per, key=lambda k: per[k]["ms"])
     kt = kernels[top]
     out = {
-        "metric": (METRIC if w.name == HEADLINE and not args.seq
+        "metric": (METRIC if tname == HEADLINE
                    else f"tokens·groups/s for linear-attn fwd+bwd, {tname}"),
         "value": value, "unit": "tokens·groups/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "G": G, "T": w.T, "chunks": n, "C": max(w.chunks), "D": D,
-                   "block": w.block, "carry": w.carry, "launches_per_step": len(launches),
+                   "block": block, "carry": w.carry, "launches_per_step": len(launches),
                    "buffer_sets": nsets, "footprint_mb": round(nsets * set_bytes / 1e6, 1),
                    "entry_points": "la_seq_fwd/la_seq_bwd" if args.seq else "la_chunk_fwd/la_chunk_bwd",
                    "timed_runs": len(per_run), "ms_per_step_runs": per_run, "ms_per_step_mean": ms_per_step_mean,
@@ -721,7 +734,7 @@ def main():
         "kernels": kernels,
         "step_roofline_frac": set_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
     }
-    if w.name == HEADLINE and not args.seq:
+    if tname == HEADLINE:
         # the pages' own figure for this shape (context, another machine, not the target): their
         # CPU micro-benchmark of the chunked form, fp32, forward+backward 72.4 ms at G=160, C=128, D=64
         out["context"] = {"pages_cpu_fwdbwd_tokens_groups_per_s": 160 * 128 / 72.4e-3,

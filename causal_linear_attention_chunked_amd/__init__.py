@@ -481,14 +481,16 @@ def ce_bwd(h, W, targets, lse, dloss=None, ce_chunk: int = 0, workspace=None, ou
     return dh, dW
 
 
-FLOOR_KINDS = {"empty": 0, "fwd": 1, "bwd": 2}
-FLOOR_NAMES = {0: "la_floor_empty_kernel", 1: "la_floor_stream_kernel<8, 4>", 2: "la_floor_stream_kernel<10, 8>"}
+FLOOR_KINDS = {"empty": 0, "fwd": 1, "bwd": 2, "fwd_small": 3, "bwd_small": 4}
+FLOOR_NAMES = {0: "la_floor_empty_kernel", 1: "la_floor_stream_kernel<8, 4, 512>", 2: "la_floor_stream_kernel<10, 8, 512>",
+               3: "la_floor_stream_kernel<8, 4, 128>", 4: "la_floor_stream_kernel<10, 8, 128>"}
 
 
 def floor_launch(kind: str, nwg: int, inp, out):
     """Measurement aid: one launch-floor kernel (no arithmetic) of ``nwg`` workgroups on the
     current stream.  kind "empty", or "fwd" / "bwd": every workgroup reads 65536 / 81920 bytes of
-    ``inp`` and writes 32768 / 65536 bytes of ``out`` (contiguous CUDA tensors, any dtype)."""
+    ``inp`` and writes 32768 / 65536 bytes of ``out`` (contiguous CUDA tensors, any dtype);
+    "fwd_small" / "bwd_small": a quarter of that per workgroup (128 threads instead of 512)."""
     lib = _lib or load_library()
     if kind not in FLOOR_KINDS:
         raise ValueError(f"unknown floor kind {kind!r}; use one of {sorted(FLOOR_KINDS)}")

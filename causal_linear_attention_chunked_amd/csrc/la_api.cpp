@@ -393,10 +393,10 @@ const char *la_seq_kernel_name(int backward, la_dtype dt, int chunk, int D, la_f
 la_status la_floor_launch(int kind, int nwg, const void *in, size_t in_bytes, void *out, size_t out_bytes,
                           void *stream) {
     const TakenEvents te;
-    if (kind < 0 || kind > 2 || nwg < 1) return LA_ERR_INVALID;
-    int nin, nout;
-    lachunk::floor_shape(kind, &nin, &nout);
-    const size_t per_in = (size_t)nin * lachunk::FLOOR_THREADS * 16, per_out = (size_t)nout * lachunk::FLOOR_THREADS * 16;
+    if (kind < 0 || kind >= lachunk::FLOOR_KINDS || nwg < 1) return LA_ERR_INVALID;
+    int nin, nout, nt;
+    lachunk::floor_shape(kind, &nin, &nout, &nt);
+    const size_t per_in = (size_t)nin * nt * 16, per_out = (size_t)nout * nt * 16;
     // the empty kernel's only pointer is never written, but must be a device buffer of 4 bytes per thread
     const size_t need_out = kind == 0 ? (size_t)lachunk::FLOOR_THREADS * 4 : (size_t)nwg * per_out;
     if (!out || out_bytes < need_out || (kind != 0 && (!in || in_bytes < (size_t)nwg * per_in))) return LA_ERR_INVALID;

@@ -105,14 +105,19 @@ hipError_t launch_ce_bwd(const void *h, const void *W, const int *targets, const
                          void *dh, float *dW, void *ws, int N, int d, int V, int ce_chunk, hipStream_t stream,
                          const hipEvent_t ev[2]);
 
-// Launch floors (measurement aid): kind 0 an empty kernel; kind 1 and 2 streaming kernels whose
+// Launch floors (measurement aid): kind 0 an empty kernel; kinds 1 and 2 streaming kernels whose
 // workgroups of FLOOR_THREADS threads each issue nin 16-byte loads per thread up front and then
-// nout stores: the forward's and the backward's bytes per group at the headline shape.
-constexpr int FLOOR_THREADS = 512;
+// nout stores: the forward's and the backward's bytes per group at the headline shape; kinds 3
+// and 4 the same per thread in workgroups of FLOOR_SMALL_THREADS threads (the same bytes over
+// four times the workgroups).
+constexpr int FLOOR_THREADS = 512, FLOOR_SMALL_THREADS = 128;
 constexpr int FLOOR_FWD_NIN = 8, FLOOR_FWD_NOUT = 4, FLOOR_BWD_NIN = 10, FLOOR_BWD_NOUT = 8;
-inline void floor_shape(int kind, int *nin, int *nout) {
-    *nin = kind == 1 ? FLOOR_FWD_NIN : kind == 2 ? FLOOR_BWD_NIN : 0;
-    *nout = kind == 1 ? FLOOR_FWD_NOUT : kind == 2 ? FLOOR_BWD_NOUT : 0;
+constexpr int FLOOR_KINDS = 5;
+inline void floor_shape(int kind, int *nin, int *nout, int *nthreads) {
+    const bool fwd = kind == 1 || kind == 3, bwd = kind == 2 || kind == 4;
+    *nin = fwd ? FLOOR_FWD_NIN : bwd ? FLOOR_BWD_NIN : 0;
+    *nout = fwd ? FLOOR_FWD_NOUT : bwd ? FLOOR_BWD_NOUT : 0;
+    *nthreads = kind >= 3 ? FLOOR_SMALL_THREADS : FLOOR_THREADS;
 }
 hipError_t launch_floor(int kind, int nwg, const void *in, void *out, hipStream_t stream, const hipEvent_t ev[2]);
 

@@ -317,7 +317,9 @@ const char *la_seq_kernel_name(int backward, la_dtype dt, int chunk, int D, la_f
  *           (non-temporal stores): at nwg = 160 the forward's bytes at the headline shape
  *           (160 groups, one 128-token chunk, D = 64, bf16: 10.5 MB read, 5.3 MB written);
  *   kind 2: the same with 81920 bytes read and 65536 written per workgroup: the backward's
- *           (13.2 MB read, 10.5 MB written at nwg = 160).
+ *           (13.2 MB read, 10.5 MB written at nwg = 160);
+ *   kind 3, 4: kinds 1 and 2 in workgroups of 128 threads (a quarter of the bytes per
+ *           workgroup): at nwg = 640 the same bytes as kinds 1 and 2 at nwg = 160.
  * in_bytes, out_bytes: the sizes of the device buffers, which must hold those counts times nwg
  * (LA_ERR_INVALID otherwise); 16-byte aligned; not overlapping.  la_time_next_launch applies.
  */

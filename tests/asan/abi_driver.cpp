@@ -162,7 +162,11 @@ int main() {
     expect("floor fwd", la_floor_launch(1, 160, A(0), 160 * 65536, A(1), 160 * 32768, 0), LA_OK, L_FLOOR);
     expect("floor bwd small out", la_floor_launch(2, 160, A(0), 160 * 81920, A(1), 160 * 65536 - 1, 0),
            LA_ERR_INVALID, 0);
-    expect("floor bad kind", la_floor_launch(3, 160, A(0), 1 << 30, A(1), 1 << 30, 0), LA_ERR_INVALID, 0);
+    expect("floor bwd, 128-thread workgroups", la_floor_launch(4, 640, A(0), 640 * 20480, A(1), 640 * 16384, 0),
+           LA_OK, L_FLOOR);
+    expect("floor fwd, 128-thread workgroups, small in",
+           la_floor_launch(3, 640, A(0), 640 * 16384 - 1, A(1), 640 * 8192, 0), LA_ERR_INVALID, 0);
+    expect("floor bad kind", la_floor_launch(5, 160, A(0), 1 << 30, A(1), 1 << 30, 0), LA_ERR_INVALID, 0);
     expect("floor overlap", la_floor_launch(1, 160, A(0), 160 * 65536, (char *)A(0) + 4096, 160 * 32768, 0),
            LA_ERR_ALIAS, 0);
 

@@ -304,6 +304,23 @@ def test_ce_fwd_noalloc_limits(lib):
     assert call(0) == INVALID and call(16, d=100) == UNSUPPORTED
 
 
+def test_floor_launch_rejects(lib):
+    # the measurement aid's host checks: kinds 0-4, buffer sizes per kind (512-thread and 128-thread
+    # workgroups), alignment and overlap; nothing here reaches a launch
+    call = lambda kind, nwg, ib, ob, i=addr(0), o=addr(1): lib.la_floor_launch(kind, nwg, i, ib, o, ob, None)
+    per = {1: (65536, 32768), 2: (81920, 65536), 3: (16384, 8192), 4: (20480, 16384)}
+    for kind, (pi, po) in per.items():
+        assert call(kind, 160, pi * 160 - 1, po * 160) == INVALID   # input one byte short
+        assert call(kind, 160, pi * 160, po * 160 - 1) == INVALID   # output one byte short
+        assert call(kind, 160, pi * 160, po * 160, i=None) == INVALID
+        assert call(kind, 160, pi * 160, po * 160, i=ctypes.c_void_p(BASE + 8)) == ALIGN
+        assert call(kind, 160, pi * 160, po * 160, o=ctypes.c_void_p(BASE + 4096)) == ALIAS
+    assert call(5, 160, 1 << 30, 1 << 30) == INVALID and call(-1, 160, 1 << 30, 1 << 30) == INVALID
+    assert call(1, 0, 1 << 30, 1 << 30) == INVALID
+    assert call(0, 160, 0, 512 * 4 - 1, i=None) == INVALID       # the empty kernel's never-written buffer
+    assert lac.FLOOR_KINDS == {"empty": 0, "fwd": 1, "bwd": 2, "fwd_small": 3, "bwd_small": 4}
+
+
 def test_time_next_launch_pairs(lib):
     assert lib.la_time_next_launch(addr(0), None) == INVALID
     assert lib.la_time_next_launch(None, addr(1)) == INVALID
