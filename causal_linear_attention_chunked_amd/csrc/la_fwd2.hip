@@ -47,7 +47,9 @@ struct Fwd2Lds {
     static constexpr int ST = VT + 2 * TBYTES;    // S_b^T copies (bf16), b = 0, 1
     static constexpr int ZR = ST + 2 * TBYTES;    // [b][hi, lo][64] bf16 rows of z_b
     static constexpr int BYTES = ZR + 4 * 128;
-    static_assert(BYTES <= 160 * 1024, "LDS budget");
+    static constexpr int OS = BYTES;              // one-chunk launch: each wave's 16 x 64 tile of o
+    static constexpr int BYTES_OS = OS + 8 * 2048;
+    static_assert(BYTES_OS <= 160 * 1024, "LDS budget");
 };
 }  // namespace
 
@@ -60,7 +62,7 @@ __device__ __forceinline__ void fwd_c128_body(
     using L = Fwd2Lds;
     constexpr int D = 64, C = 128;
     constexpr uint32_t CHUNK = C * D * 2;
-    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char smem[SEQ ? L::BYTES : L::BYTES_OS];
     char *const Kt = smem + L::KT, *const Vt = smem + L::VT, *const STt = smem + L::ST, *const zrow = smem + L::ZR;
 
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
@@ -230,9 +232,27 @@ __device__ __forceinline__ void fwd_c128_body(
                 mma(dn, zf[kc][1], qf[kc]);
             }
             const float inv = __builtin_amdgcn_rcpf(gsum(pa.dsum) + dn[0]);
-            bf16 *orow = o + (tok0 + 64 * B + 16 * tq + r) * D + 4 * g;
+            if constexpr (SEQ) {
+                bf16 *orow = o + (tok0 + 64 * B + 16 * tq + r) * D + 4 * g;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) store_bf16x4<!SEQ>(orow + 16 * c, pack4(pa.nm[c] * inv));
+                for (int c = 0; c < 4; ++c) store_bf16x4<false>(orow + 16 * c, pack4(pa.nm[c] * inv));
+            } else {
+                // the wave's 16 x 64 tile through its own LDS slab (8-byte units XOR-swizzled by row:
+                // conflict-free both ways), then out as whole 128-byte rows, 16 bytes per lane
+                char *slab = smem + L::OS + w * 2048;
+                const int f = 2 * (r >> 1);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    *reinterpret_cast<bf16x4 *>(slab + r * 128 + 8 * ((4 * c + g) ^ f)) = pack4(pa.nm[c] * inv);
+                wave_lds_sync();
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int row = 8 * i + (lane >> 3), u = lane & 7;  // 16-byte unit u of the row
+                    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(slab + row * 128 + 8 * ((2 * u) ^ (2 * (row >> 1))));
+                    __builtin_nontemporal_store(
+                        x, reinterpret_cast<bf16x8 *>(o + (tok0 + 64 * B + 16 * tq + row) * D + 8 * u));
+                }
+            }
         };
         auto outputs = [&](auto b_tag) {
             Part pa;

@@ -132,6 +132,15 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Orders a wave's LDS writes before its later LDS reads of what other lanes of the same wave
+// wrote.  A wave's LDS operations complete in issue order, so no workgroup barrier is needed; the
+// fences keep the compiler from moving the reads above the writes.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 // Store of four bf16 outputs (8 bytes per lane; the four lanes of an accumulator row write
 // 32 contiguous bytes per instruction).  Non-temporal (NT) or write-back.  A one-chunk
 // launch is faster with non-temporal stores, at the price of partial-sector writes (more
