@@ -587,35 +587,33 @@ __device__ __forceinline__ void bwd_c128_body(
         }
         reverse(0);
         if constexpr (!SEQ) {
-            // every output staged in LDS regions no longer read (phase 5 reads none of them) and
-            // stored in whole lines after one more barrier: dv_b, dk_b as bf16 tiles in the dP
-            // region (tiles dv_0, dv_1, dk_0, dk_1), dS_in as fp32 rows of 256 bytes in the
-            // upstream state's region, 16-byte units XOR-swizzled by row (conflict-free writes)
-            {
-                const int B = p2b, jt = p2dk ? 3 - (w & 3) : (w & 3);
-                char *dst = smem + L::DP + ((p2dk ? 2 : 0) + B) * TBYTES;
+            // dv_b or dk_b: the wave's 16 x 64 tile through its own 2 KB slab of the dP region (no
+            // longer read in this phase; 8-byte units XOR-swizzled by row, conflict-free both
+            // ways), then out as whole 128-byte rows, 16 bytes per lane; no barrier, since only the
+            // wave reads its slab.  dS_in straight from the accumulators, 64-byte row pieces.
+            const int B = p2b, jt = p2dk ? 3 - (w & 3) : (w & 3);
+            char *slab = smem + L::DP + w * 2048;
+            const int f = 2 * (r >> 1);
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    floatx4 y = acc[x];
-                    if (p2dk) {
-                        y += f4(L::ZH + 4 * (64 * B + 16 * x));
-                        if constexpr (FM) y *= elu1_grad4(lds_b64(tile(L::KT, B) + jt * 16 * TROW + TL.nat[x]));
-                    }
-                    tstore_acc(dst, TL.nat[x], jt, pack4(y));
+            for (int x = 0; x < 4; ++x) {
+                floatx4 y = acc[x];
+                if (p2dk) {
+                    y += f4(L::ZH + 4 * (64 * B + 16 * x));
+                    if constexpr (FM) y *= elu1_grad4(lds_b64(tile(L::KT, B) + jt * 16 * TROW + TL.nat[x]));
                 }
-                const int p = 16 * pt + r;
-                *reinterpret_cast<floatx4 *>(smem + L::SH1 + p * 256 + 16 * ((4 * ct + g) ^ (p & 15))) = Sh;
+                *reinterpret_cast<bf16x4 *>(slab + r * 128 + 8 * ((4 * x + g) ^ f)) = pack4(y);
             }
-            lds_barrier();
-            const uint32_t so = stage_off(tl);
-            const size_t row = tok0 + 64 * sb + (tl >> 3);
-            const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(smem + L::DP + sb * TBYTES + so);
-            const bf16x8 xk = *reinterpret_cast<const bf16x8 *>(smem + L::DP + (2 + sb) * TBYTES + so);
-            __builtin_nontemporal_store(xv, reinterpret_cast<bf16x8 *>(dv + row * D + 8 * (tl & 7)));
-            __builtin_nontemporal_store(xk, reinterpret_cast<bf16x8 *>(dk + row * D + 8 * (tl & 7)));
-            const int p = tid_c >> 4, un = tid_c & 15;  // dS_in: 16 threads per 256-byte row
-            const floatx4 xs = *reinterpret_cast<const floatx4 *>(smem + L::SH1 + p * 256 + 16 * (un ^ (p & 15)));
-            __builtin_nontemporal_store(xs, reinterpret_cast<floatx4 *>(dS_in + ((size_t)grp * D + p) * D + 4 * un));
+            wave_lds_sync();
+            bf16 *const out = p2dk ? dk : dv;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = 8 * i + (lane >> 3), un = lane & 7;  // 16-byte unit un of the row
+                const bf16x8 x = *reinterpret_cast<const bf16x8 *>(slab + row * 128 + 8 * ((2 * un) ^ (2 * (row >> 1))));
+                __builtin_nontemporal_store(
+                    x, reinterpret_cast<bf16x8 *>(out + (tok0 + 64 * B + 16 * jt + row) * D + 8 * un));
+            }
+            const int p = 16 * pt + r;
+            __builtin_nontemporal_store(Sh, reinterpret_cast<floatx4 *>(dS_in + ((size_t)grp * D + p) * D + 16 * ct + 4 * g));
         }
         // the tiles the next chunk's phase 0 writes are read up to here
         if (SEQ && c > 0) lds_barrier();
