@@ -82,13 +82,17 @@ la_status seq_checks(int G, int T, int D, int chunk, int block, la_dtype dt, la_
     return LA_OK;
 }
 
-// Which kernel family a chunk call runs: the 128-token kernels (bf16, D = 64, C = 128, block 64),
-// the per-token cumsum kernels (block 1; the fused feature map on any other shape; the fp32
-// backward at D = 128, whose blocked fp32 tiles exceed the LDS), or the general blocked kernels.
-enum class Path { C128, CUMSUM, GENERAL };
+// Which kernel family a chunk call runs: the 128-token kernels (bf16, D = 64, C = 128, block 64);
+// the D = 128 kernels (bf16, block 64: the sequence forward over a one-chunk sequence, and the
+// backward that builds the carry after the chunk from the carry before it; forward chunks up to
+// LA_SEQ_D128_MAX_T tokens); the per-token cumsum kernels (block 1; the fused feature map on any
+// other shape; the fp32 backward at D = 128, whose blocked fp32 tiles exceed the LDS); or the
+// general blocked kernels.
+enum class Path { C128, D128, CUMSUM, GENERAL };
 Path chunk_path(bool backward, la_dtype dt, int C, int D, int block, la_feature feature) {
     const bool c128 = dt == LA_BF16 && D == 64 && C == 128 && block == BK_TOKENS;
     if (c128) return Path::C128;
+    if (dt == LA_BF16 && D == 128 && block == BK_TOKENS && (backward || C <= LA_SEQ_D128_MAX_T)) return Path::D128;
     if (block == 1 || feature == LA_FEATURE_ELU1 || (backward && dt == LA_F32 && D == 128)) return Path::CUMSUM;
     return Path::GENERAL;
 }
@@ -132,6 +136,8 @@ la_status la_chunk_fwd(const void *q, const void *k, const void *v, const float 
     const Path path = chunk_path(false, dt, C, D, block, feature);
     if (path == Path::C128)
         e = lachunk::launch_fwd_c128(q, k, v, S_in, z_in, o, S_out, z_out, G, fm, s, te.ev);
+    else if (path == Path::D128)
+        e = lachunk::launch_seq_fwd_d128(q, k, v, S_in, z_in, o, S_out, z_out, nullptr, nullptr, G, C, fm, s, te.ev);
     else if (path == Path::CUMSUM)
         e = dt == LA_BF16
                 ? (D == 64 ? lachunk::launch_cumsum_fwd<__bf16, 64>(q, k, v, S_in, z_in, o, S_out, z_out, G, C, fm, s, te.ev)
@@ -178,6 +184,9 @@ la_status la_chunk_bwd(const void *q, const void *k, const void *v, const float 
     const Path path = chunk_path(true, dt, C, D, block, feature);
     if (path == Path::C128)
         e = lachunk::launch_bwd_c128(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, G, fm, s,
+                                     te.ev);
+    else if (path == Path::D128)
+        e = lachunk::launch_bwd_d128(q, k, v, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, G, C, fm, s,
                                      te.ev);
     else if (path == Path::CUMSUM)
         e = dt == LA_BF16
@@ -372,6 +381,9 @@ const char *la_kernel_name(int backward, la_dtype dt, int C, int D, int block, l
         case Path::C128:
             if (backward) return fm ? "la_bwd_c128w16_elu1_kernel" : "la_bwd_c128w16_kernel";
             return fm ? "la_fwd_c128_elu1_kernel" : "la_fwd_c128_kernel";
+        case Path::D128:
+            if (backward) return fm ? "la_bwd_d128_elu1_kernel" : "la_bwd_d128_kernel";
+            return fm ? "la_seq_fwd_d128_elu1_kernel" : "la_seq_fwd_d128_kernel";
         case Path::CUMSUM: return backward ? "la_cumsum_bwd_kernel" : "la_cumsum_fwd_kernel";
         case Path::GENERAL: break;
     }

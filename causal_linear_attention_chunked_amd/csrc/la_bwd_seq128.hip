@@ -33,6 +33,10 @@
 //   3  den, rho, inv, dden; dP (split, stored [t][j]); Sh_b split copy, zh_b
 //   4  dq; dv or dk of the wave's (key tile, column half); Sh_{b-1}, zh_{b-1}
 // Rows past the end of the sequence read as zero, get inv = 0 and are not stored.
+// FROM_IN (the one-chunk entry point, whose caller holds the carry before the chunk, not after
+// it): the carry after the last token is first built from the carry before the first, S_in +
+// sum_b K_b^T V_b over the blocks in order (z with a two-sum), the next block's keys and values
+// loaded while one block's are added; the reverse walk then recovers the states from it as above.
 // FM: q and k are raw inputs, mapped by elu(x) + 1 as they are staged; dq and dk are the
 // gradients of the raw inputs, scaled at their stores by phi'(x) = min(1, phi) read back from the
 // mapped tiles.  Mapped rows past the end of the sequence are zero, as raw ones are (phi(0) = 1
@@ -75,7 +79,7 @@ constexpr uint32_t key_table() {
 }
 }  // namespace
 
-template <bool FM>
+template <bool FM, bool FROM_IN>
 __device__ __forceinline__ void bwd_seq128_body(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ S_last, const float *__restrict__ z_last, const float *__restrict__ S_res,
@@ -116,7 +120,10 @@ __device__ __forceinline__ void bwd_seq128_body(
     const GRes qr(q + gtok0 * D, seq_bytes), kr(k + gtok0 * D, seq_bytes), vr(v + gtok0 * D, seq_bytes),
         gr(dO + gtok0 * D, seq_bytes);
     const float *const dummy = dS_in;  // a valid base for an empty range
-    const GRes sres(S_last + (size_t)grp * D * D, D * D * 4), zres(z_last + (size_t)grp * D, D * 4);
+    // S_last, z_last: the carry after the last token, or with FROM_IN the carry before the first (NULL
+    // together: a zero carry)
+    const GRes sres(S_last ? (const void *)(S_last + (size_t)grp * D * D) : dummy, S_last ? D * D * 4 : 0);
+    const GRes zres(z_last ? (const void *)(z_last + (size_t)grp * D) : dummy, z_last ? D * 4 : 0);
     const GRes shres(dS_out ? (const void *)(dS_out + (size_t)grp * D * D) : dummy, dS_out ? D * D * 4 : 0);
     const GRes zhres(dz_out ? (const void *)(dz_out + (size_t)grp * D) : dummy, dz_out ? D * 4 : 0);
     const GRes srres(S_res ? (const void *)(S_res + (size_t)grp * D * D) : dummy, S_res ? D * D * 4 : 0);
@@ -162,6 +169,51 @@ __device__ __forceinline__ void bwd_seq128_body(
     }
     issue_fence();
     const bf16x8 ones = ones_frag<bf16>();
+
+    if constexpr (FROM_IN) {
+        // the carry after the last token: S += K_b^T V_b as C[c][p] = sum_j V[j][c] K[j][p] and z
+        // += K_b^T 1 (two-sum), block by block in order; rows past the end read (and map) as zero
+        const int row = tid >> 4, f = (tid >> 3) & 1;
+        const uint32_t so = f * TBYTES + stage_off(row * 8 + (tid & 7));
+        bf16x8 kx = gload<bf16x8>(kr, tid * 16), vx = gload<bf16x8>(vr, tid * 16);
+        for (int b = 0; b < nblk; ++b) {
+            const bool live = row < T - b * BK;
+            *reinterpret_cast<bf16x8 *>(smem + L::KT + so) = FM ? (live ? elu1_8(kx) : bf16x8{}) : kx;
+            *reinterpret_cast<bf16x8 *>(smem + L::VT + so) = vx;
+            // the next block's, in flight during this one (past the range after the last: zeros)
+            kx = gload<bf16x8>(kr, (uint32_t)(b + 1) * BLOCK + tid * 16);
+            vx = gload<bf16x8>(vr, (uint32_t)(b + 1) * BLOCK + tid * 16);
+            lds_barrier();
+            const int lane = tid & 63, r = lane & 15, g = lane >> 4;
+            const TileLanes TL(lane);
+            const uint32_t tr_c = TL.tr_at(cl);
+            bf16x8 vt[2];
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) vt[kc] = tfrag_tr(tq_(L::VT, cf), tr_c, kc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int pf = i >> 1, pl = pt0 + 2 * (i & 1);
+                bf16x8 kt[2];
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) kt[kc] = tfrag_tr(tq_(L::KT, pf), TL.tr_at(pl), kc);
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) mma(Sacc[i], vt[kc], kt[kc]);
+                if (ct == 0) {
+                    floatx4 Pz = zero4();
+#pragma unroll
+                    for (int kc = 0; kc < 2; ++kc) mma(Pz, ones, kt[kc]);
+                    if (g == 0) {
+                        const int p = 16 * (pt0 + 2 * i) + r;
+                        float zr = zrun[p], zc = zcmp[p];
+                        two_sum(zr, zc, Pz[0]);
+                        zrun[p] = zr;
+                        zcmp[p] = zc;
+                    }
+                }
+            }
+            lds_barrier();  // the tiles are rewritten by the next block (or the first reverse step)
+        }
+    }
 
     for (int b = nblk - 1; b >= 0; --b) {
         // lane-dependent offsets derived afresh each block from an opaque copy of the thread index
@@ -470,7 +522,8 @@ __global__ __launch_bounds__(S128_THREADS, 1) void la_seq_bwd_d128_kernel(
     const float *__restrict__ dS_out, const float *__restrict__ dz_out,
     bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
     float *__restrict__ dS_in, float *__restrict__ dz_in, int T) {
-    bwd_seq128_body<false>(q, k, v, S_last, z_last, S_res, z_res, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, T);
+    bwd_seq128_body<false, false>(q, k, v, S_last, z_last, S_res, z_res, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in,
+                                  T);
 }
 
 // the same with the feature map fused: dq and dk are the gradients of the raw inputs
@@ -481,7 +534,40 @@ __global__ __launch_bounds__(S128_THREADS, 1) void la_seq_bwd_d128_elu1_kernel(
     const float *__restrict__ dS_out, const float *__restrict__ dz_out,
     bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
     float *__restrict__ dS_in, float *__restrict__ dz_in, int T) {
-    bwd_seq128_body<true>(q, k, v, S_last, z_last, S_res, z_res, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in, T);
+    bwd_seq128_body<true, false>(q, k, v, S_last, z_last, S_res, z_res, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in,
+                                 T);
+}
+
+// One chunk of C tokens from the carry before it (the chunk entry point), with and without the map.
+__global__ __launch_bounds__(S128_THREADS, 1) void la_bwd_d128_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_in, const float *__restrict__ z_in, const bf16 *__restrict__ dO,
+    const float *__restrict__ dS_out, const float *__restrict__ dz_out,
+    bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
+    float *__restrict__ dS_in, float *__restrict__ dz_in, int C) {
+    bwd_seq128_body<false, true>(q, k, v, S_in, z_in, nullptr, nullptr, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in,
+                                 C);
+}
+
+__global__ __launch_bounds__(S128_THREADS, 1) void la_bwd_d128_elu1_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ S_in, const float *__restrict__ z_in, const bf16 *__restrict__ dO,
+    const float *__restrict__ dS_out, const float *__restrict__ dz_out,
+    bf16 *__restrict__ dq, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
+    float *__restrict__ dS_in, float *__restrict__ dz_in, int C) {
+    bwd_seq128_body<true, true>(q, k, v, S_in, z_in, nullptr, nullptr, dO, dS_out, dz_out, dq, dk, dv, dS_in, dz_in,
+                                C);
+}
+
+hipError_t launch_bwd_d128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
+                           const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
+                           float *dS_in, float *dz_in, int G, int C, bool elu1, hipStream_t stream,
+                           const hipEvent_t ev[2]) {
+    hipExtLaunchKernelGGL(elu1 ? la_bwd_d128_elu1_kernel : la_bwd_d128_kernel, dim3((unsigned)G),
+                          dim3(S128_THREADS), 0, stream, ev[0], ev[1], 0, (const bf16 *)q, (const bf16 *)k,
+                          (const bf16 *)v, S_in, z_in, (const bf16 *)dO, dS_out, dz_out, (bf16 *)dq, (bf16 *)dk,
+                          (bf16 *)dv, dS_in, dz_in, C);
+    return hipGetLastError();
 }
 
 hipError_t launch_seq_bwd_d128(const void *q, const void *k, const void *v, const float *S_last,

@@ -65,6 +65,14 @@ hipError_t launch_seq_bwd_d128(const void *q, const void *k, const void *v, cons
                                const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv, float *dS_in,
                                float *dz_in, int G, int T, bool elu1, hipStream_t stream, const hipEvent_t ev[2]);
 
+// bf16, D = 128: the backward over one chunk of C tokens (C >= 1, the last 64-token block possibly
+// ragged) from the carry before it: the carry after the chunk is built first, then the reverse walk
+// of launch_seq_bwd_d128.
+hipError_t launch_bwd_d128(const void *q, const void *k, const void *v, const float *S_in, const float *z_in,
+                           const void *dO, const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
+                           float *dS_in, float *dz_in, int G, int C, bool elu1, hipStream_t stream,
+                           const hipEvent_t ev[2]);
+
 // Cross-entropy over a tied head (bf16 h, W; fp32 loss, lse, dW; bf16 dh).  The GEMM tiles
 // (CE_MT class rows x CE_NT tokens, CE_CK k per stage) and the shape of the workspace: padded
 // sizes, the backward's chunking and the split of dh over the vocabulary.  Host arithmetic

@@ -97,8 +97,11 @@ typedef enum {
  *   feature  : LA_FEATURE_NONE, or LA_FEATURE_ELU1: q and k hold raw inputs x and
  *              the op runs on phi(x) = elu(x) + 1 computed in fp32 and rounded to
  *              the element type as the inputs are loaded (as in la_seq_fwd).  With
- *              the map, the 128-token bf16 chunk at D = 64 runs its blocked kernel;
- *              every other shape runs the per-token form.
+ *              the map, bf16 chunks of 128 tokens at D = 64 and bf16 chunks at D = 128
+ *              run their blocked kernels; every other shape runs the per-token form.
+ * bf16 at D = 128 (block 64, C up to LA_SEQ_D128_MAX_T) runs la_seq_fwd's kernel over
+ * a one-chunk sequence: a ragged end is a masked 64-token block there, not the
+ * token-by-token tail (the same function in another summation order).
  * S_out may not alias S_in: the call is pure (the carry goes in, a new carry
  * comes out), so chaining chunks ping-pongs two state buffers.  A feature
  * outside la_feature is LA_ERR_INVALID.
@@ -127,7 +130,9 @@ la_status la_chunk_fwd(const void *q, const void *k, const void *v,
  * With a NULL carry, dS_in/dz_in still receive the gradient with respect to a
  * zero carry.  fp32 elements at D == 128 run the per-token form whatever the
  * block (the blocked form's fp32 tiles of that size exceed the local memory);
- * its results agree with the blocked form's to fp32 rounding.
+ * its results agree with the blocked form's to fp32 rounding.  bf16 at D == 128
+ * (block 64) runs la_seq_bwd's walk over the chunk's 64-token blocks, last first,
+ * after building the carry after the chunk from S_in, z_in in the same launch.
  */
 la_status la_chunk_bwd(const void *q, const void *k, const void *v,
                        const float *S_in, const float *z_in,

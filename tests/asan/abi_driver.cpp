@@ -11,7 +11,7 @@
 extern int g_last_launch;
 enum {
     L_NONE = 0, L_FWD, L_BWD, L_FWD_C128, L_BWD_C128, L_SEQ_FWD_C128, L_SEQ_BWD_C128, L_SEQ_FWD_D128,
-    L_SEQ_BWD_D128, L_CE_FWD, L_CE_BWD, L_CE_FWD_NOALLOC, L_FLOOR, L_CUMSUM_FWD, L_CUMSUM_BWD
+    L_SEQ_BWD_D128, L_CE_FWD, L_CE_BWD, L_CE_FWD_NOALLOC, L_FLOOR, L_CUMSUM_FWD, L_CUMSUM_BWD, L_BWD_D128
 };
 
 static int failures = 0;
@@ -34,6 +34,13 @@ int main() {
     expect("fwd headline", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 160, 128, 64, 64, LA_FEATURE_NONE, LA_BF16, 0),
            LA_OK, L_FWD_C128);
     expect("fwd ragged", la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 4, 100, 64, 64, LA_FEATURE_NONE, LA_BF16, 0),
+           LA_OK, L_FWD);
+    expect("fwd bf16 d128 ragged: the D = 128 sequence forward",
+           la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 4, 100, 128, 64, LA_FEATURE_NONE, LA_BF16, 0),
+           LA_OK, L_SEQ_FWD_D128);
+    expect("fwd bf16 d128 beyond the sequence kernel's length",
+           la_chunk_fwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), 1, LA_SEQ_D128_MAX_T + 1, 128, 64, LA_FEATURE_NONE,
+                        LA_BF16, 0),
            LA_OK, L_FWD);
     expect("fwd fp32 d128 no carry",
            la_chunk_fwd(A(0), A(1), A(2), nullptr, nullptr, A(5), F(6), F(7), 1, 37, 128, 64, LA_FEATURE_NONE, LA_F32, 0), LA_OK, L_FWD);
@@ -60,6 +67,10 @@ int main() {
     expect("bwd d128 upstream",
            la_chunk_bwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), A(8), A(9), A(10), F(11), F(12), 160, 100, 128,
                         64, LA_FEATURE_NONE, LA_BF16, 0),
+           LA_OK, L_BWD_D128);
+    expect("bwd fp32 d64",
+           la_chunk_bwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), A(8), A(9), A(10), F(11), F(12), 16, 100, 64,
+                        64, LA_FEATURE_NONE, LA_F32, 0),
            LA_OK, L_BWD);
     expect("bwd C > max",
            la_chunk_bwd(A(0), A(1), A(2), F(3), F(4), A(5), F(6), F(7), A(8), A(9), A(10), F(11), F(12), 4,

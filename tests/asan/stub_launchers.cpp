@@ -12,7 +12,7 @@ namespace lachunk {
 
 enum : int {
     L_FWD = 1, L_BWD, L_FWD_C128, L_BWD_C128, L_SEQ_FWD_C128, L_SEQ_BWD_C128, L_SEQ_FWD_D128, L_SEQ_BWD_D128,
-    L_CE_FWD, L_CE_BWD, L_CE_FWD_NOALLOC, L_FLOOR, L_CUMSUM_FWD, L_CUMSUM_BWD
+    L_CE_FWD, L_CE_BWD, L_CE_FWD_NOALLOC, L_FLOOR, L_CUMSUM_FWD, L_CUMSUM_BWD, L_BWD_D128
 };
 
 static hipError_t hit(int id) {
@@ -101,6 +101,11 @@ hipError_t launch_seq_bwd_d128(const void *, const void *, const void *, const f
                                const float *, const float *, const void *, const float *, const float *, void *,
                                void *, void *, float *, float *, int, int, bool, hipStream_t, const hipEvent_t *) {
     return hit(L_SEQ_BWD_D128);
+}
+hipError_t launch_bwd_d128(const void *, const void *, const void *, const float *, const float *, const void *,
+                           const float *, const float *, void *, void *, void *, float *, float *, int, int, bool,
+                           hipStream_t, const hipEvent_t *) {
+    return hit(L_BWD_D128);
 }
 hipError_t launch_ce_fwd(const void *, const void *, const int *, float *, float *, void *, int, int, int,
                          hipStream_t, const hipEvent_t *) {

@@ -51,7 +51,11 @@ def test_library_exports_every_declared_symbol(lib):
 def test_kernel_names(lib):
     assert lac.kernel_name(False, "bf16", 128, 64) == "la_fwd_c128_kernel"
     assert lac.kernel_name(True, "bf16", 128, 64) == "la_bwd_c128w16_kernel"
-    assert lac.kernel_name(False, "bf16", 100, 128) == "la_fwd_kernel"
+    assert lac.kernel_name(False, "bf16", 100, 128) == "la_seq_fwd_d128_kernel"
+    assert lac.kernel_name(True, "bf16", 100, 128) == "la_bwd_d128_kernel"
+    assert lac.kernel_name(True, "bf16", 128, 128, feature="elu1") == "la_bwd_d128_elu1_kernel"
+    assert lac.kernel_name(False, "bf16", 16385, 128) == "la_fwd_kernel"
+    assert lac.kernel_name(False, "bf16", 16384, 128) == "la_seq_fwd_d128_kernel"
     assert lac.kernel_name(True, "float32", 128, 64) == "la_bwd_kernel"
     # the fp32 backward at D = 128 runs the per-token form
     assert lac.kernel_name(True, "float32", 128, 128) == "la_cumsum_bwd_kernel"

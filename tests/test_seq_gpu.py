@@ -317,6 +317,44 @@ def test_seq_d128_matches_chained_calls(gpu):
         assert rel < 2e-3, (name, rel)
 
 
+@pytest.mark.parametrize("C,feature", [(1, None), (100, None), (128, "elu1"), (640, None), (2048, None)])
+def test_chunk_d128_backward_from_the_carry_before(gpu, C, feature):
+    # la_chunk_bwd at bf16, D = 128 builds the carry after the chunk from the carry before it, then
+    # walks back like la_seq_bwd: against the oracle, and against la_seq_bwd given the forward's
+    # final carry with its remainders (the same walk: to fp32 rounding)
+    G = 3
+    say(f"[case] chunk bwd D=128 from S_in, C={C}, feature={feature}")
+    I = inp.make_inputs(G=G, T=C, D=128, dtype="bf16", carry="prior", backward=True, seed=70 + C,
+                        features="raw" if feature else "mapped")
+    dS, dz = upstream(G, 128, 71)
+    q, k, v, dO = (dev(I[n]) for n in ("q", "k", "v", "dO"))
+    S_in, z_in = dev(I["S_in"]), dev(I["z_in"])
+    assert lac.kernel_name(True, "bf16", C, 128, feature=feature) == (
+        "la_bwd_d128_elu1_kernel" if feature else "la_bwd_d128_kernel")
+    o, S_out, z_out = lac.fwd(q, k, v, S_in, z_in, feature=feature)
+    dq, dk, dv, dS_in, dz_in = lac.bwd(q, k, v, S_in, z_in, dO, dev(dS), dev(dz), feature=feature)
+    _, S2, z2, Sr, zr = lac.seq_fwd(q, k, v, S_in, z_in, chunk=128 * ((C + 127) // 128), feature=feature,
+                                    residual=True)
+    ref = lac.seq_bwd(q, k, v, S2, z2, dO, dev(dS), dev(dz), chunk=128 * ((C + 127) // 128), feature=feature,
+                      S_res=Sr, z_res=zr)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv", "dS_in", "dz_in"), (dq, dk, dv, dS_in, dz_in), ref):
+        a, b = a.double(), b.double()
+        rel = float((a - b).norm() / b.norm())
+        say(f"  {name}: chunk call vs sequence call normwise {rel:.2e}")
+        assert rel < 1e-3, (name, rel)
+    res = {"o": o, "S_out": S_out, "z_out": z_out, "dq": dq, "dk": dk, "dv": dv, "dS_in": dS_in, "dz_in": dz_in}
+    if feature:
+        a = [I[n] for n in ("q", "k", "v", "S_in", "z_in")]
+        ro, rS, rz = oracle.features.fwd(*a, dtype="bf16")
+        rb = oracle.features.bwd(*a, I["dO"], dS, dz, dtype="bf16")
+    else:
+        ro, rS, rz = oracle.fwd(I["q"], I["k"], I["v"], I["S_in"], I["z_in"])
+        rb = oracle.bwd(I["q"], I["k"], I["v"], I["S_in"], I["z_in"], I["dO"], dS, dz)
+    for name, r in zip(("o", "S_out", "z_out", "dq", "dk", "dv", "dS_in", "dz_in"), (ro, rS, rz, *rb)):
+        check(name, res[name], r, RTOL["bf16"])
+
+
 def test_seq_rejects_unsupported(gpu):
     x = torch.ones(2, 200, 64, dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(lac.LachunkError, match="UNSUPPORTED"):
