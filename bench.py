@@ -89,14 +89,33 @@ def plan_launches(G, chunks, D, esz, carry):
     return out
 
 
-def kernel_source_hash():
-    """Hash of every source of the attention kernels (all of csrc/ but the cross-entropy's file):
-    counter-measured traffic is only reported for the build it was taken on."""
+# The sources each kernel is built from (beside the shared headers): counter-measured traffic is
+# reported only for the build it was taken on, and an edit elsewhere does not void it.
+KERNEL_SOURCES = {
+    "la_fwd_c128": "la_fwd2.hip", "la_seq_fwd_c128": "la_fwd2.hip",
+    "la_bwd_c128w16": "la_bwd4.hip", "la_seq_bwd_c128w16": "la_bwd4.hip",
+    "la_seq_fwd_d128": "la_fwd_seq128.hip",
+    "la_seq_bwd_d128": "la_bwd_seq128.hip", "la_bwd_d128": "la_bwd_seq128.hip",
+    "la_fwd": "la_fwd.hip", "la_bwd": "la_bwd.hip",
+    "la_cumsum_fwd": "la_cumsum.hip", "la_cumsum_bwd": "la_cumsum.hip",
+}
+SHARED_HEADERS = ("la_common.h", "la_tile.h")
+
+
+def kernel_source_hash(kernel):
+    """Hash of the sources `kernel` is built from: its own file and the shared headers (every
+    attention source when the kernel is not in KERNEL_SOURCES)."""
     import glob
+    csrc = os.path.join(ROOT, "causal_linear_attention_chunked_amd", "csrc")
+    base = kernel[:-len("_kernel")] if kernel.endswith("_kernel") else kernel
+    base = base[:-len("_elu1")] if base.endswith("_elu1") else base
+    if base in KERNEL_SOURCES:
+        files = [os.path.join(csrc, f) for f in (*SHARED_HEADERS, KERNEL_SOURCES[base])]
+    else:
+        files = [f for f in sorted(glob.glob(os.path.join(csrc, "*")))
+                 if os.path.basename(f) not in ("la_ce.hip", "la_floor.hip")]
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "causal_linear_attention_chunked_amd", "csrc", "*"))):
-        if os.path.basename(f) in ("la_ce.hip", "la_floor.hip"):
-            continue
+    for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
             h.update(fh.read())
@@ -114,10 +133,10 @@ def measured_traffic(workload, kernel):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
-        return None
     k = t.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
+    if k is None or k.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return k.get("bytes_per_launch")
 
 
 def counter_rows(d, counter):
@@ -141,7 +160,7 @@ def counters_summary(d, workload, kernels):
     fc = max(v for _, v in counter_rows(os.path.join(d, "fetch_copy"), "FETCH_SIZE"))
     wc = max(v for _, v in counter_rows(os.path.join(d, "write_copy"), "WRITE_SIZE"))
     scale_f, scale_w = cal / fc, cal / wc
-    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+    out = {"workload": workload,
            "calibration": {"copy_KiB": cal, "fetch_KiB_read": fc, "write_KiB_read": wc,
                            "fetch_scale": scale_f, "write_scale": scale_w},
            "kernels": {}}
@@ -155,7 +174,7 @@ def counters_summary(d, workload, kernels):
         fb = sum(fv) / len(fv) * scale_f * 1024
         wb = sum(wv) / len(wv) * scale_w * 1024
         out["kernels"][k] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb,
-                             "dispatches": [len(fv), len(wv)]}
+                             "dispatches": [len(fv), len(wv)], "source_hash": kernel_source_hash(k)}
     with open(traffic_file(workload), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out), flush=True)
