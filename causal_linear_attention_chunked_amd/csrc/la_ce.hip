@@ -65,6 +65,14 @@ __device__ __forceinline__ void lds_load16(const int4v &rs, const void *lds, uin
                  : "memory");
 }
 
+// The same for one dword per lane: lane l's 4 bytes at voff go to LDS byte lds + 4 x lane.
+__device__ __forceinline__ void lds_load4(const int4v &rs, const void *lds, uint32_t voff) {
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "{m0}"((uint32_t)(size_t)(lds_void *)lds)
+                 : "memory");
+}
+
 // s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt untouched), n < 16
 template <int n>
 __device__ __forceinline__ void wait_vm_lgkm() {
@@ -108,12 +116,20 @@ struct TileWalk {
 // (vmcnt(6): the six of the next step, always issued after them, may stay in flight; after an
 // epilogue its stores and loads are newer still, so the wait then also covers some of them) and
 // for its LDS reads, then a barrier: every wave's loads of the step have landed and every wave is
-// done reading the stage the step after next is loaded into, which is issued next; then the
-// products.  The loads past the end of the stream are issued at an offset past every buffer range
-// (no memory is read), so that every step has the same loads in flight.
-template <bool AKM, bool BKM, class TileF, class EpiF>
+// done reading the stage the step after next is loaded into; then the products, with the loads
+// of the step after next issued behind them, half after each k-chunk.  The loads past the end of
+// the stream are issued at an offset past every buffer range (no memory is read), so that every
+// step has the same loads in flight.
+// pre(L), when given, runs right after the barrier of tile L's next-to-last k-step (every tile has
+// at least two): loads it issues into LDS there (lds_load4) are complete and visible when the
+// tile's epilogue runs, behind the next step's wait and barrier, so the epilogue never waits on
+// memory (a load of its own would wait for every load in flight, the stages' too).
+struct NoPre {
+    __device__ __forceinline__ void operator()(uint32_t) const {}
+};
+template <bool AKM, bool BKM, class TileF, class EpiF, class PreF = NoPre>
 __device__ __forceinline__ void gemm_tiles(char *s0, char *s1, char *s2, const Operand &A, const Operand &B,
-                                           const TileWalk &walk, TileF tile_at, EpiF epi) {
+                                           const TileWalk &walk, TileF tile_at, EpiF epi, PreF pre = PreF{}) {
     if (walk.count == 0) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 3, wn = w >> 2;
@@ -143,14 +159,25 @@ __device__ __forceinline__ void gemm_tiles(char *s0, char *s1, char *s2, const O
     };
     set_offsets();
     constexpr uint32_t PAST = 0x80000000u;  // byte offset past every operand's range (< 2^31 bytes)
-    auto issue_next = [&](char *st, bool live) {
+    // Loads of one k-step in two halves (A tiles 0-2, then A tile 3 and both B tiles), then the
+    // cursor moves on.  The halves are issued after the products of each k-chunk: right after a
+    // barrier all eight waves' loads reach the memory pipeline at once and a wave's issue stalls
+    // until its loads are taken (hundreds of clocks for a step's 48 KB per CU); behind the
+    // products that stall overlaps them.
+    auto issue_half = [&](char *st, bool live, int half) {
         const uint32_t kk = itr.k0 + (uint32_t)is * CK;
         const uint32_t ka = AKM ? kk * A.ld : kk, kb = BKM ? kk * B.ld : kk;
+        if (half == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_load16(A.rs, st + i * TBYTES + 1024 * w, live ? (offa[i] + ka) * 2 : PAST);
+            for (int i = 0; i < 3; ++i) lds_load16(A.rs, st + i * TBYTES + 1024 * w, live ? (offa[i] + ka) * 2 : PAST);
+        } else {
+            lds_load16(A.rs, st + 3 * TBYTES + 1024 * w, live ? (offa[3] + ka) * 2 : PAST);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            lds_load16(B.rs, st + (4 + i) * TBYTES + 1024 * w, live ? (offb[i] + kb) * 2 : PAST);
+            for (int i = 0; i < 2; ++i)
+                lds_load16(B.rs, st + (4 + i) * TBYTES + 1024 * w, live ? (offb[i] + kb) * 2 : PAST);
+        }
+    };
+    auto advance_loads = [&](bool live) {
         if (live && ++is == itr.nk) {
             is = 0;
             if (++ij < walk.count) {
@@ -158,6 +185,11 @@ __device__ __forceinline__ void gemm_tiles(char *s0, char *s1, char *s2, const O
                 set_offsets();
             }
         }
+    };
+    auto issue_next = [&](char *st, bool live) {
+        issue_half(st, live, 0);
+        issue_half(st, live, 1);
+        advance_loads(live);
     };
 
     floatx4 acc[4][4];
@@ -167,7 +199,9 @@ __device__ __forceinline__ void gemm_tiles(char *s0, char *s1, char *s2, const O
         for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
     uint32_t cj = 0;  // product cursor: tile cj, k-step cs of its cnk
     int cs = 0, cnk = itr.nk;
-    auto compute = [&](const char *st) {
+    // the products of one k-step from stage st, each k-chunk's followed by half of the loads of
+    // the step after next into stage nxt (free: every wave is past its last read of it)
+    auto compute = [&](const char *st, char *nxt, bool live) {
         const char *At = st + wm * TBYTES, *Bt = st + (4 + wn) * TBYTES;
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
@@ -181,15 +215,17 @@ __device__ __forceinline__ void gemm_tiles(char *s0, char *s1, char *s2, const O
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) mma(acc[i][j], af[i], bfr[j]);
+            issue_half(nxt, live, kc);
         }
+        advance_loads(live);
     };
     auto step = [&](char *cur, char *nxt, int g) {
         wait_vm_lgkm<6>();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue_next(nxt, g + 2 < S);
-        compute(cur);
+        if (cs == cnk - 2) pre(walk[cj]);
+        compute(cur, nxt, g + 2 < S);
         if (++cs == cnk) {
             epi(walk[cj], acc);
 #pragma unroll
@@ -236,21 +272,25 @@ __global__ __launch_bounds__(CE_THREADS, 1) void la_ce_fwd_kernel(
     __shared__ __attribute__((aligned(16))) char s1[STAGE];
     __shared__ __attribute__((aligned(16))) char s2[STAGE];
     __shared__ floatx2 xch[4 * NT];  // [4 wm][128 tokens]
+    __shared__ int tg_lds[NT];       // the tile's targets, loaded before its epilogue
     // logical tile: the token tiles of one class tile consecutively (they share its rows of W)
     const uint32_t ntt = (uint32_t)Npad / NT, nvt = (uint32_t)(V + MT - 1) / MT;
     const Operand A{rsrc4(W, (uint32_t)V * d * 2), (uint32_t)d, false};
     const Operand B{rsrc4(h, (uint32_t)N * d * 2), (uint32_t)d, false};
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w & 3, wn = w >> 2;
-    const GRes tres(targets, (uint32_t)N * 4);
+    const int4v trs = rsrc4(targets, (uint32_t)N * 4);
     auto tile_at = [&](uint32_t L) { return TileRange{(L / ntt) * MT, (L % ntt) * NT, 0u, d / CK}; };
+    auto pre = [&](uint32_t L) {  // the two waves with wm = 0: 64 targets each
+        if (wm == 0) lds_load4(trs, tg_lds + 64 * wn, ((L % ntt) * NT + 64 * wn + lane) * 4);
+    };
     auto epi = [&](uint32_t L, floatx4 (&acc)[4][4]) {
         const uint32_t vt = L / ntt, v0 = vt * MT, t0 = (L % ntt) * NT;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int tloc = 64 * wn + 16 * j + r;
             const int t = (int)t0 + tloc;
-            const int tgt = gload<int>(tres, (uint32_t)t * 4);
+            const int tgt = tg_lds[tloc];
             float mx = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -290,7 +330,7 @@ __global__ __launch_bounds__(CE_THREADS, 1) void la_ce_fwd_kernel(
         }
         lds_barrier();  // xch is rewritten by the next tile's epilogue
     };
-    gemm_tiles<false, false>(s0, s1, s2, A, B, TileWalk(nvt * ntt), tile_at, epi);
+    gemm_tiles<false, false>(s0, s1, s2, A, B, TileWalk(nvt * ntt), tile_at, epi, pre);
 }
 
 // lse_t = max + log(sum over the class tiles' partials), nll_t = lse_t - tl_t: 16 tokens per
@@ -346,21 +386,30 @@ __global__ __launch_bounds__(CE_THREADS, 1) void la_ce_p_kernel(
     __shared__ __attribute__((aligned(16))) char s0[STAGE];
     __shared__ __attribute__((aligned(16))) char s1[STAGE];
     __shared__ __attribute__((aligned(16))) char s2[STAGE];
+    __shared__ int tg_lds[NT];      // the tile's targets and lse, loaded before its epilogue
+    __shared__ float lse_lds[NT];
     const uint32_t ntt = (uint32_t)(Nc + NT - 1) / NT, nvt = (uint32_t)Vpad / MT;
     const Operand A{rsrc4(W, (uint32_t)V * d * 2), (uint32_t)d, false};
     const Operand B{rsrc4(h + (size_t)c0 * d, (uint32_t)Nc * d * 2), (uint32_t)d, false};
     const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), wm = w & 3, wn = w >> 2;
     const float scale = (dloss ? *dloss : 1.f) / (float)N;
-    const GRes tres(targets + c0, (uint32_t)Nc * 4), lres(lse + c0, (uint32_t)Nc * 4);
+    const int4v trs = rsrc4(targets + c0, (uint32_t)Nc * 4), lrs = rsrc4(lse + c0, (uint32_t)Nc * 4);
     auto tile_at = [&](uint32_t L) { return TileRange{(L / ntt) * MT, (L % ntt) * NT, 0u, d / CK}; };
+    auto pre = [&](uint32_t L) {  // the two waves with wm = 0: 64 tokens each
+        if (wm == 0) {
+            const uint32_t off = ((L % ntt) * NT + 64 * wn + lane) * 4;
+            lds_load4(trs, tg_lds + 64 * wn, off);
+            lds_load4(lrs, lse_lds + 64 * wn, off);
+        }
+    };
     auto epi = [&](uint32_t L, floatx4 (&acc)[4][4]) {
         const uint32_t v0 = (L / ntt) * MT, t0 = (L % ntt) * NT;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int tloc = (int)t0 + 64 * wn + 16 * j + r;  // token within the chunk
-            const int tgt = gload<int>(tres, (uint32_t)tloc * 4);
-            const float l = gload<float>(lres, (uint32_t)tloc * 4);
+            const int tgt = tg_lds[64 * wn + 16 * j + r];
+            const float l = lse_lds[64 * wn + 16 * j + r];
             const bool live = tloc < Nc;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -376,7 +425,7 @@ __global__ __launch_bounds__(CE_THREADS, 1) void la_ce_p_kernel(
             }
         }
     };
-    gemm_tiles<false, false>(s0, s1, s2, A, B, TileWalk(nvt * ntt), tile_at, epi);
+    gemm_tiles<false, false>(s0, s1, s2, A, B, TileWalk(nvt * ntt), tile_at, epi, pre);
 }
 
 // dW tiles: C[m = feature][n = class] = sum_t h[t][m] P[t][n] over the chunk's (padded) tokens;
