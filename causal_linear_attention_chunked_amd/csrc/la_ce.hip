@@ -286,29 +286,47 @@ __global__ __launch_bounds__(CE_THREADS, 1) void la_ce_fwd_kernel(
     };
     auto epi = [&](uint32_t L, floatx4 (&acc)[4][4]) {
         const uint32_t vt = L / ntt, v0 = vt * MT, t0 = (L % ntt) * NT;
+        const int vbase = (int)v0 + 64 * wm + 4 * g;  // acc[i][j][e] is class vbase + 16 i + e
+        const bool full = (int)v0 + MT <= V;          // no class of the tile past V (uniform)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int tloc = 64 * wn + 16 * j + r;
             const int t = (int)t0 + tloc;
-            const int tgt = tg_lds[tloc];
-            float mx = -INFINITY;
+            // the target's offset from the lane's first class: the lane holds its logit when it
+            // is one of vbase + 16 i + e (rare: a branch, not a compare per element)
+            const int q = tg_lds[tloc] - vbase;
+            if ((unsigned)q < 64u && (q & 12) == 0 && t < N) {
+                float x = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int vv = (int)v0 + 64 * wm + 16 * i + 4 * g + e;
-                    if (vv < V) mx = fmaxf(mx, acc[i][j][e]);
-                    if (vv == tgt && t < N) tl[t] = acc[i][j][e];
-                }
-            mx = gmax(mx);
-            float sum = 0.f;
+                    for (int e = 0; e < 4; ++e) x = q == 16 * i + e ? acc[i][j][e] : x;
+                tl[t] = x;
+            }
+            float mx = -INFINITY, sum = 0.f;
+            if (full) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int vv = (int)v0 + 64 * wm + 16 * i + 4 * g + e;
-                    sum += vv < V ? exp_f(acc[i][j][e] - mx) : 0.f;
-                }
+                    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, acc[i][j][e]);
+                mx = gmax(mx);
+                const float ml = -mx * LOG2E;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sum += __builtin_amdgcn_exp2f(fmaf(acc[i][j][e], LOG2E, ml));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (vbase + 16 * i + e < V) mx = fmaxf(mx, acc[i][j][e]);
+                mx = gmax(mx);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sum += vbase + 16 * i + e < V ? exp_f(acc[i][j][e] - mx) : 0.f;
+            }
             sum = gsum(sum);
             if (g == 0) xch[wm * NT + tloc] = floatx2{mx, sum};
         }
@@ -405,21 +423,32 @@ __global__ __launch_bounds__(CE_THREADS, 1) void la_ce_p_kernel(
     };
     auto epi = [&](uint32_t L, floatx4 (&acc)[4][4]) {
         const uint32_t v0 = (L / ntt) * MT, t0 = (L % ntt) * NT;
+        // every class and token of the tile in range (uniform): no masks
+        const bool full = (int)v0 + MT <= V && (int)t0 + NT <= Nc;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int tloc = (int)t0 + 64 * wn + 16 * j + r;  // token within the chunk
             const int tgt = tg_lds[64 * wn + 16 * j + r];
             const float l = lse_lds[64 * wn + 16 * j + r];
             const bool live = tloc < Nc;
+            const float ll = -l * LOG2E;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int vb = (int)v0 + 64 * wm + 16 * i + 4 * g;
                 floatx4 p;
+                if (full) {
+                    const int q = tgt - vb;  // the target is element q of these four when 0 <= q < 4
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int vv = vb + e;
-                    const float x = exp_f(acc[i][j][e] - l) - (vv == tgt ? 1.f : 0.f);
-                    p[e] = (live && vv < V) ? x * scale : 0.f;
+                    for (int e = 0; e < 4; ++e)
+                        p[e] = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[i][j][e], LOG2E, ll)), scale,
+                                    q == e ? -scale : 0.f);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int vv = vb + e;
+                        const float x = exp_f(acc[i][j][e] - l) - (vv == tgt ? 1.f : 0.f);
+                        p[e] = (live && vv < V) ? x * scale : 0.f;
+                    }
                 }
                 *reinterpret_cast<bf16x4 *>(P + (size_t)tloc * Vpad + vb) = pack4(p);
             }
