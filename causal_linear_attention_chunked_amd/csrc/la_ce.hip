@@ -39,6 +39,8 @@ constexpr int CK = CE_CK;        // k per stage
 constexpr int STAGE = (MT + NT) / 64 * TBYTES;  // one stage: A tiles 0-3, then B tiles 0-1 (48 KB)
 
 typedef int int4v __attribute__((ext_vector_type(4)));
+typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
+typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Buffer descriptor of `bytes` bytes at `base` as four dwords (the layout and flags of GRes):
@@ -432,6 +434,7 @@ __global__ __launch_bounds__(CE_THREADS, 1) void la_ce_p_kernel(
             const float l = lse_lds[64 * wn + 16 * j + r];
             const bool live = tloc < Nc;
             const float ll = -l * LOG2E;
+            uint32_t pk[4][2];  // P of classes vb(i) .. vb(i) + 3 in bf16, two per dword
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int vb = (int)v0 + 64 * wm + 16 * i + 4 * g;
@@ -450,7 +453,25 @@ __global__ __launch_bounds__(CE_THREADS, 1) void la_ce_p_kernel(
                         p[e] = (live && vv < V) ? x * scale : 0.f;
                     }
                 }
-                *reinterpret_cast<bf16x4 *>(P + (size_t)tloc * Vpad + vb) = pack4(p);
+                const bf16x4 b4 = pack4(p);
+                pk[i][0] = __builtin_bit_cast(uint2v, b4)[0];
+                pk[i][1] = __builtin_bit_cast(uint2v, b4)[1];
+            }
+            // 16-byte stores: lanes of lane groups g and g ^ 1 trade pieces (the odd group's piece
+            // of tile i for the even group's piece of tile i + 1), after which lane group g holds
+            // eight consecutive classes, 16 (g & 1) + 8 (g >> 1) past the pair's first: each store
+            // writes 64 contiguous bytes of 16 token rows
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+                uint32_t lo[2], hi[2];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const auto sw = __builtin_amdgcn_permlane16_swap(pk[i][c], pk[i + 1][c], false, false);
+                    lo[c] = sw[0];
+                    hi[c] = sw[1];
+                }
+                const int vb = (int)v0 + 64 * wm + 16 * i + 16 * (g & 1) + 8 * (g >> 1);
+                *reinterpret_cast<uint4v *>(P + (size_t)tloc * Vpad + vb) = uint4v{lo[0], lo[1], hi[0], hi[1]};
             }
         }
     };
