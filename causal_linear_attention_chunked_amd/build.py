@@ -4,6 +4,7 @@
 """
 from __future__ import annotations
 
+import importlib.util
 import os
 import subprocess
 import sys
@@ -32,6 +33,13 @@ def build(verbose: bool = False) -> str:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
         objs.append(obj)
+    # the inline-assembly check on the device assembly (the device flags; -fPIC is for the host)
+    spec = importlib.util.spec_from_file_location("lachunk_asm_check", os.path.join(HERE, "asm_check.py"))
+    asm_check = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(asm_check)
+    found = asm_check.check(HIPCC, [f for f in DEVICE_FLAGS if f != "-fPIC"], CSRC)
+    if found:
+        raise RuntimeError("inline assembly too close to a VALU write of its SGPRs:\n" + "\n".join(found))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

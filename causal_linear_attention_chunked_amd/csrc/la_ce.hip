@@ -60,6 +60,10 @@ struct Operand {
 // uniform (M0).  Issued as assembly, so the compiler neither counts them nor orders LDS reads
 // after them: the main loop waits for them itself (vmcnt) and a barrier publishes them.  Loads
 // the compiler does not know of can only make its own waits for its own loads stricter.
+// Nor does the compiler look inside assembly for hazards: a VALU write of an SGPR (a v_readlane
+// restoring a spilled descriptor, say) needs five wait states before a vector memory instruction
+// reads that SGPR.  The build compiles this file to assembly and refuses a library in which such
+// a write comes closer than that to one of these loads (asm_check.py).
 __device__ __forceinline__ void lds_load16(const int4v &rs, const void *lds, uint32_t voff) {
     asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
