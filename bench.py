@@ -433,9 +433,55 @@ def bench_ce(args, w, torch, lac, inp):
         "kernels": entry,
         "step_roofline_frac": 4 * gemm / (ms_per_step / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
     }
+    if args.library_gemms:
+        out["library_gemms"] = library_gemms(torch, N, d, V)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_ce(I, w)
     print(json.dumps(out), flush=True)
+
+
+def library_gemms(torch, N, d, V, reps=20, runs=5):
+    """The cross-entropy's four products as plain library GEMMs (torch.mm, hipBLASLt on ROCm) on
+    the same shapes, bf16 in and out, each replayed `reps` times from a HIP graph: the vendor
+    library's time for the bare products, beside which the fused kernels' times are read."""
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(0)
+    h = torch.randn(N, d, device=dev, dtype=torch.bfloat16, generator=g)
+    W = torch.randn(V, d, device=dev, dtype=torch.bfloat16, generator=g)
+    P = torch.randn(N, V, device=dev, dtype=torch.bfloat16, generator=g)
+    cases = {
+        "logits W h^T (V x N)": lambda: torch.mm(W, h.t()),
+        "logits h W^T (N x V)": lambda: torch.mm(h, W.t()),
+        "dW = P^T h (V x d, k = N)": lambda: torch.mm(P.t(), h),
+        "dh = P W (N x d, k = V)": lambda: torch.mm(P, W),
+    }
+    out = {}
+    for name, f in cases.items():
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                f()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(reps):
+                f()
+        gr.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(runs):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            gr.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+        us = sorted(ts)[len(ts) // 2]
+        tf = 2.0 * N * V * d / (us * 1e-6) / 1e12
+        out[name] = {"us": us, "TFLOP/s": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS}
+    return out
 
 
 def bench_floors(args, torch, lac, nwg=160):
@@ -542,6 +588,8 @@ def main():
                     help="time the launch-floor kernels (no arithmetic) of the headline launches' sizes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only plain 256 MiB device-to-device copies (HBM counter calibration)")
+    ap.add_argument("--library-gemms", action="store_true",
+                    help="cross-entropy workloads: also time the four products as plain torch.mm GEMMs")
     ap.add_argument("--counters-summary", metavar="DIR",
                     help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE passes under DIR into per-launch HBM bytes")
     args = ap.parse_args()
