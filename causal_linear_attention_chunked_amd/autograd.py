@@ -10,7 +10,10 @@ q, k, v are (G, T, D) CUDA tensors (bf16 or fp32; q and k already positive, e.g.
 elu(x) + 1); S_in (G, D, D) and z_in (G, D) are fp32 or None for a zero carry.
 Where the library's sequence entry points take the shape (bf16; D = 64 in whole
 128-token chunks, or D = 128 in chunks of a multiple of 64 tokens) the sequence is
-one forward and one backward launch with the carry kept on chip; otherwise every chunk is one forward launch and its backward
+one forward and one backward launch with the carry kept on chip; a sequence longer than
+those calls take (SEQ_D64_MAX_T, SEQ_D128_MAX_T tokens) runs as consecutive segments of
+whole chunks, each one such pair of launches, the carry passed from one to the next;
+otherwise every chunk is one forward launch and its backward
 one backward launch that recomputes the chunk from its saved inputs (q, k, v and
 the carry that fed it).  Either way nothing of size (G, C, D, D) or (G, C, C) is
 kept between the passes, the memory-flat principle of the page's section 1.  Gradients flow to q, k, v and,
@@ -40,6 +43,7 @@ from . import fwd as _fwd
 from . import seq_bwd as _seq_bwd
 from . import seq_fwd as _seq_fwd
 from . import seq_supported as _seq_supported
+from . import SEQ_D64_MAX_T, SEQ_D128_MAX_T
 
 
 class ChunkFunction(torch.autograd.Function):
@@ -115,6 +119,25 @@ def chunk_attention(q, k, v, S_in=None, z_in=None, block: int = 64, feature_map=
     return ChunkFunction.apply(q, k, v, S_in, z_in, block, _fm(feature_map))
 
 
+def seq_segments(dtype, T: int, D: int, chunk: int, feature=None):
+    """Token counts of the consecutive segments a (G, T, D) sequence runs as through the sequence
+    entry points: [T] where they take all T tokens; for a longer sequence of a shape they take,
+    segments of the most whole chunks one call takes, then the rest; None where they take no
+    segment of the shape."""
+    if _seq_supported(dtype, T, D, chunk, feature):
+        return [T]
+    tmax = SEQ_D128_MAX_T if D == 128 else SEQ_D64_MAX_T
+    L = tmax - tmax % chunk if chunk >= 1 else 0
+    if T <= tmax or L < 1 or not _seq_supported(dtype, L, D, chunk, feature):
+        return None
+    segs = [L] * (T // L)
+    if T % L:
+        if not _seq_supported(dtype, T % L, D, chunk, feature):
+            return None
+        segs.append(T % L)
+    return segs
+
+
 IMPLS = ("auto", "seq", "chunk", "cumsum")
 IMPL_ENV = "LACHUNK_ATTN_IMPL"
 _impl = None  # set by set_attention_impl; None: the environment variable, else "auto"
@@ -159,12 +182,19 @@ def linear_attention(q, k, v, S_in=None, z_in=None, chunk: int = 128, block: int
     if T == 0:
         return q.new_empty(q.shape), (S_in, z_in)
     fm = _fm(feature_map)
-    seq_ok = _seq_supported(q.dtype, T, q.shape[2], chunk, fm) and block == 64
-    if name == "seq" and not seq_ok:
+    segs = seq_segments(q.dtype, T, q.shape[2], chunk, fm) if block == 64 else None
+    if name == "seq" and segs is None:
         raise ValueError("impl='seq': the sequence entry points take bf16, block 64, and D = 64 in whole "
                          "128-token chunks or D = 128 in chunks of a multiple of 64 tokens")
-    if seq_ok and name in ("seq", "auto"):
-        o, S, z = SeqFunction.apply(q, k, v, S_in, z_in, chunk, block, fm)
+    if segs is not None and name in ("seq", "auto"):
+        outs = []
+        S, z = S_in, z_in
+        t0 = 0
+        for L in segs:
+            o, S, z = SeqFunction.apply(q[:, t0:t0 + L], k[:, t0:t0 + L], v[:, t0:t0 + L], S, z, chunk, block, fm)
+            outs.append(o)
+            t0 += L
+        o = outs[0] if len(outs) == 1 else torch.cat(outs, dim=1)
         return o, (S, z)
     blk = 1 if name == "cumsum" else block
     outs = []

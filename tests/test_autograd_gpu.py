@@ -80,6 +80,15 @@ def test_autograd_sequence_entry_points_wide_heads(gpu):
     _case("bf16", "prior", True, G=2, T=300, D=128)
 
 
+def test_autograd_sequence_longer_than_one_call(gpu):
+    # D = 128 past the sequence calls' length: two segments (the longest one call takes, then 300
+    # tokens with a ragged end), the carry passed from the first to the second, the gradients back
+    from causal_linear_attention_chunked_amd import autograd as ag
+    T = lac.SEQ_D128_MAX_T + 300
+    assert ag.seq_segments(torch.bfloat16, T, 128, 128) == [lac.SEQ_D128_MAX_T, 300]
+    _case("bf16", "prior", True, G=1, T=T, D=128, seed=23)
+
+
 def test_autograd_fused_feature_map(gpu):
     _case("bf16", "prior", True, G=3, T=384, feature_map="elu1")
 

@@ -45,3 +45,25 @@ def test_impl_checked_before_the_device():
         lac.linear_attention(q, q, q, impl="fast")
     with pytest.raises(ValueError):
         lac.linear_attention(q, q, q, impl="chunk")
+
+
+def test_sequence_segments():
+    # the segments a sequence runs as through the sequence entry points (host logic)
+    bf, seg = torch.bfloat16, ag.seq_segments
+    T128, T64 = lac.SEQ_D128_MAX_T, lac.SEQ_D64_MAX_T
+    assert seg(bf, 300, 128, 128) == [300]                       # one call, a ragged last chunk
+    assert seg(bf, T128, 128, 128) == [T128]
+    # longer: whole-chunk segments of the longest length one call takes, then the rest
+    assert seg(bf, T128 + 100, 128, 128) == [T128, 100]
+    assert seg(bf, 2 * T128 + 64, 128, 192) == [T128 - T128 % 192] * 2 + [2 * T128 + 64 - 2 * (T128 - T128 % 192)]
+    assert seg(bf, 3 * T128, 128, 64) == [T128] * 3
+    assert seg(bf, T64 + 256, 64, 128) == [T64, 256]
+    # shapes the sequence calls never take stay None, whatever the length
+    assert seg(bf, T64 + 100, 64, 128) is None                   # D = 64 takes whole 128-token chunks only
+    assert seg(bf, 300, 64, 64) is None
+    assert seg(torch.float32, 2 * T128, 128, 128) is None        # bf16 only
+    assert seg(bf, T128 + 1, 128, 100) is None                   # chunks a multiple of 64 at D = 128
+    # every segment but the last is whole chunks, and they add up
+    for T, D, C in ((5 * T128 + 7, 128, 128), (T128 + 64, 128, 640)):
+        s = seg(bf, T, D, C)
+        assert sum(s) == T and all(x % C == 0 for x in s[:-1]) and all(x <= T128 for x in s)
