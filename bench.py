@@ -365,8 +365,9 @@ def bench_ce(args, w, torch, lac, inp):
     and la_ce_bwd over the N tokens, inputs resident on the device.  Bound by MFMA: four products
     of 2 N V d flops each (the forward's logits; the backward's recomputed logits, dh and dW)."""
     N, d, V = w.N, w.d, w.V
+    ce_chunk = args.ce_chunk or N  # tokens per backward chunk (0: all N at once)
     I = inp.ce_workload_inputs(w)
-    ws_bytes = lac.ce_workspace_bytes(N, d, V)
+    ws_bytes = lac.ce_workspace_bytes(N, d, V, ce_chunk)
     set_bytes = V * d * 2 + V * d * 4 + 2 * N * d * 2 + ws_bytes  # W, dW, h, dh, workspace
     nsets = max(1, math.ceil(args.footprint_mb * 1e6 / set_bytes))
     dev = "cuda:0"
@@ -382,7 +383,7 @@ def bench_ce(args, w, torch, lac, inp):
         lac.ce_fwd(s["h"], s["W"], s["targets"], workspace=s["ws"], out=s["fout"])
 
     def bwd(s):
-        lac.ce_bwd(s["h"], s["W"], s["targets"], s["fout"][1], workspace=s["ws"], out=s["bout"])
+        lac.ce_bwd(s["h"], s["W"], s["targets"], s["fout"][1], ce_chunk=ce_chunk, workspace=s["ws"], out=s["bout"])
 
     def step(i):
         fwd(sets[i % nsets])
@@ -417,11 +418,12 @@ def bench_ce(args, w, torch, lac, inp):
     top = "la_ce_bwd"
     kt = entry[top]
     out = {
-        "metric": f"tokens/s for the tied-head cross-entropy fwd+bwd, {w.name}",
+        "metric": f"tokens/s for the tied-head cross-entropy fwd+bwd, {w.name}"
+                  + (f", backward in chunks of {ce_chunk}" if ce_chunk != N else ""),
         "value": N / (ms_per_step / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "N": N, "d": d, "V": V, "ce_chunk": N, "buffer_sets": nsets,
+        "config": {"workload": w.name, "N": N, "d": d, "V": V, "ce_chunk": ce_chunk, "buffer_sets": nsets,
                    "footprint_mb": round(nsets * set_bytes / 1e6, 1), "workspace_bytes": ws_bytes,
                    "timed_runs": len(per_run), "ms_per_step_runs": per_run, "graph_captured": False,
                    "host_enqueue_us_per_step": host_s * 1e6 / K,
@@ -588,6 +590,8 @@ def main():
                     help="time the launch-floor kernels (no arithmetic) of the headline launches' sizes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only plain 256 MiB device-to-device copies (HBM counter calibration)")
+    ap.add_argument("--ce-chunk", type=int, default=0,
+                    help="cross-entropy workloads: tokens per backward chunk (default: all N at once)")
     ap.add_argument("--library-gemms", action="store_true",
                     help="cross-entropy workloads: also time the four products as plain torch.mm GEMMs")
     ap.add_argument("--counters-summary", metavar="DIR",
